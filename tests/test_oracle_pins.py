@@ -1,0 +1,439 @@
+"""Pins for the CPU oracle, against facts that do not come from the oracle itself.
+
+Source page: "PR #34602: feat(unified-memory): dense KV views for uniform-row
+MHA/SWA models" (sglang report).  What pins what:
+
+* ``walk()`` below enumerates a page envelope in memory order straight from its
+  description ``[L0_K*ps | L0_V*ps | L1_K*ps | ...]`` (implementation step 1):
+  it never uses a kernel id, a block index or a view offset.  Addressing,
+  view bases, translate, the tail pad and the row bound are checked against it
+  by brute force on tiny pools.
+* ``oracle/strided.py`` (the nested strided reference, the page's own test
+  oracle) checks the oracle's store / gather / move byte for byte.
+* Gates are checked at boundary values that the walk determines.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import MHA, MLA, Spec
+from oracle.strided import StridedPool, layer_view_4d
+import ukv_workloads as W
+
+
+def walk(num_pages, layer_num, kind, page_size, row_bytes, anchor=0):
+    """Byte address of every (page, layer, kv, offset) row, walking the envelope in order."""
+    addr = anchor
+    out = {}
+    kvs = (0, 1) if kind == MHA else (0,)
+    for p in range(num_pages):
+        for l in range(layer_num):
+            for kv in kvs:
+                for o in range(page_size):
+                    out[(p, l, kv, o)] = addr
+                    addr += row_bytes
+    return out, addr
+
+
+SHAPES = [
+    (kind, L, ps, P, H, D, es)
+    for kind in (MHA, MLA)
+    for L in (1, 2, 3)
+    for ps in (1, 2, 4)
+    for P in (1, 2, 5)
+    for (H, D, es) in ((1, 4, 2), (2, 8, 2), (3, 2, 1))
+]
+
+
+def make_spec(kind, L, P, H, D, es):
+    return Spec(kind, L, H, D, D if kind == MHA else 0, es, P)
+
+
+@pytest.mark.parametrize("kind,L,ps,P,H,D,es", SHAPES)
+def test_addressing_matches_envelope_walk(kind, L, ps, P, H, D, es):
+    pool = oracle.OraclePool([make_spec(kind, L, P, H, D, es)], ps)
+    sp = pool.plan.subs[0]
+    rb = H * D * es
+    addrs, end = walk(P, L, kind, ps, rb)
+    assert sp.row_bytes == rb
+    assert sp.envelope_bytes == end
+    assert sp.page_bytes == end // P
+    for (p, l, kv, o), a in addrs.items():
+        base = pool.view_base(0, l, kv)
+        kid = oracle.kernel_id(p * ps + o, ps, sp.blocks_per_page)
+        assert base + kid * rb == a, (p, l, kv, o)
+        assert 0 <= kid < sp.n_rows
+
+
+@pytest.mark.parametrize("kind,L,ps,P,H,D,es", SHAPES[::5])
+def test_spec_offsets_equal_block_origins(kind, L, ps, P, H, D, es):
+    pool = oracle.OraclePool([make_spec(kind, L, P, H, D, es)], ps)
+    addrs, _ = walk(P, L, kind, ps, H * D * es)
+    for l in range(L):
+        for kv in ((0, 1) if kind == MHA else (0,)):
+            assert pool.view_base(0, l, kv) == addrs[(0, l, kv, 0)]
+
+
+@pytest.mark.parametrize("L,ps,P", [(1, 1, 1), (2, 4, 3), (3, 2, 5)])
+def test_k_and_v_share_an_id_without_aliasing(L, ps, P):
+    spec = make_spec(MHA, L, P, 2, 8, 2)
+    pool = oracle.OraclePool([spec], ps)
+    sp = pool.plan.subs[0]
+    rb = sp.row_bytes
+    seen = set()
+    for t in range(P * ps):
+        kid = oracle.kernel_id(t, ps, sp.blocks_per_page)
+        for l in range(L):
+            k = pool.view_base(0, l, 0) + kid * rb
+            v = pool.view_base(0, l, 1) + kid * rb
+            assert v - k == ps * rb
+            seen.update((k, v))
+    # a bijection onto the envelope, one row per rb bytes
+    assert sorted(seen) == list(range(0, sp.envelope_bytes, rb))
+
+
+@pytest.mark.parametrize("kind,L,ps,P", [(MHA, 2, 4, 16), (MHA, 3, 1, 2), (MLA, 3, 4, 5), (MLA, 1, 2, 3)])
+def test_tail_pad_covers_view_overrun_and_is_one_envelope(kind, L, ps, P):
+    spec = make_spec(kind, L, P, 2, 8, 2)
+    pool = oracle.OraclePool([spec], ps)
+    sp = pool.plan.subs[0]
+    addrs, end = walk(P, L, kind, ps, sp.row_bytes)
+    # furthest byte any dense view reaches, from the view bases the walk pinned
+    reach = max(pool.view_base(0, l, kv) + sp.n_rows * sp.row_bytes
+                for l in range(L) for kv in ((0, 1) if kind == MHA else (0,)))
+    assert reach - end <= sp.tail_pad_bytes
+    # "a whole page envelope" of pad: the bytes of one page in the walk
+    assert sp.tail_pad_bytes == end // P
+    assert pool.plan.required_bytes == end + sp.tail_pad_bytes
+    # valid kernel ids never reach the pad: the last row the walk knows ends the envelope
+    assert max(addrs.values()) + sp.row_bytes == end
+
+
+def test_builder_check_boundaries_tiny_pool():
+    """Two layers, two heads of dim 8, bf16, page size 4, 16 pages."""
+    spec = make_spec(MHA, 2, 16, 2, 8, 2)
+    pool = oracle.OraclePool([spec], 4)
+    sp = pool.plan.subs[0]
+    _, end = walk(16, 2, MHA, 4, 32)
+    overrun = max(pool.view_base(0, l, kv) + sp.n_rows * 32 for l in range(2) for kv in (0, 1)) - end
+    assert overrun == 3 * 4 * 32  # three blocks of four 32-byte rows past the last envelope
+    assert pool.builder_check(0, end)[0] == "tail_pad"
+    assert pool.builder_check(0, end + overrun - 1)[0] == "tail_pad"
+    assert pool.builder_check(0, end + overrun) == ("ok", end + overrun)
+    assert pool.plan.required_bytes == end + sp.page_bytes == 8192 + 512
+
+
+def test_pool_tail_pad_is_max_over_specs_and_subpools_back_to_back():
+    a = make_spec(MHA, 2, 3, 2, 8, 2)
+    b = make_spec(MLA, 5, 4, 1, 16, 2)
+    pool = oracle.OraclePool([a, b], 4)
+    sa, sb = pool.plan.subs
+    wa, ea = walk(3, 2, MHA, 4, 32)
+    wb, eb = walk(4, 5, MLA, 4, 32, anchor=ea)
+    assert sb.anchor_bytes == ea
+    assert pool.plan.tail_pad_bytes == max(sa.tail_pad_bytes, sb.tail_pad_bytes) == max(ea // 3, (eb - ea) // 4)
+    assert pool.plan.required_bytes == eb + pool.plan.tail_pad_bytes
+    for (p, l, kv, o), addr in wb.items():
+        kid = oracle.kernel_id(p * 4 + o, 4, sb.blocks_per_page)
+        assert pool.view_base(1, l, kv) + kid * 32 == addr
+
+
+def test_multiplier_one_collapse_aliases_k_over_v():
+    """With a page multiplier of 1 (the override the pages keep only for tests), a K write
+    for a slot on page 1 lands in page 0's V rows: physical ids written into dense rows."""
+    ps, L, P = 4, 2, 3
+    pool = oracle.OraclePool([make_spec(MHA, L, P, 2, 8, 2)], ps)
+    rb = 32
+    addrs, _ = walk(P, L, MHA, ps, rb)
+    for o in range(ps):
+        wrong = pool.view_base(0, 0, 0) + oracle.kernel_id(1 * ps + o, ps, 1) * rb
+        assert wrong == addrs[(0, 0, 1, o)]  # page 0, layer 0, V
+        assert wrong != addrs[(1, 0, 0, o)]
+        right = pool.view_base(0, 0, 0) + oracle.kernel_id(1 * ps + o, ps, 2 * L) * rb
+        assert right == addrs[(1, 0, 0, o)]
+
+
+def test_asymmetric_kv_rejected_mla_exempt():
+    assert oracle.plan([Spec(MHA, 2, 8, 192, 128, 2, 4)], 16).code == "asymmetric_kv"
+    assert oracle.plan([Spec(MHA, 2, 8, 128, 128, 2, 4)], 16).code == "ok"
+    assert oracle.plan([Spec(MLA, 2, 1, 576, 512, 2, 4)], 16).code == "ok"
+    # a later asymmetric spec rejects the whole pool
+    assert oracle.plan([Spec(MLA, 2, 1, 576, 0, 2, 4), Spec(MHA, 2, 8, 64, 128, 2, 4)], 16).code == "asymmetric_kv"
+
+
+def _rows_per_page(L, kind, ps):
+    addrs, _ = walk(1, L, kind, ps, 1)
+    return len(addrs)
+
+
+@pytest.mark.parametrize("L,ps", [(80, 16), (32, 16), (3, 4)])
+def test_int32_row_bound_boundary(L, ps):
+    per_page = _rows_per_page(L, MHA, ps)  # rows one page adds to every dense view
+    limit = 1 << 31
+    p_max = (limit - 1) // per_page  # the largest page count whose rows stay below 2^31
+    ok = oracle.plan([Spec(MHA, L, 8, 128, 128, 2, p_max)], ps)
+    bad = oracle.plan([Spec(MHA, L, 8, 128, 128, 2, p_max + 1)], ps)
+    assert ok.code == "ok" and ok.subs[0].n_rows == p_max * per_page < limit
+    assert bad.code == "kernel_id_bound"
+    if (L, ps) == (80, 16):
+        assert (p_max, p_max * per_page) == (838860, 2147481600)
+    if (L, ps) == (32, 16):
+        # 2^21 pages give exactly 2^31 rows: rejected, "must be less than 2^31"
+        assert oracle.plan([Spec(MHA, L, 8, 128, 128, 2, 1 << 21)], ps).code == "kernel_id_bound"
+        assert p_max == (1 << 21) - 1
+
+
+def test_invalid_and_overflow_specs():
+    good = Spec(MHA, 2, 2, 8, 8, 2, 4)
+    assert oracle.plan([], 4).code == "invalid_arg"
+    assert oracle.plan([good], 0).code == "invalid_arg"
+    for bad in (Spec(MHA, 0, 2, 8, 8, 2, 4), Spec(MHA, 2, 0, 8, 8, 2, 4), Spec(MHA, 2, 2, 0, 0, 2, 4),
+                Spec(MHA, 2, 2, 8, 8, 3, 4), Spec(MHA, 2, 2, 8, 8, 2, 0), Spec(7, 2, 2, 8, 8, 2, 4)):
+        assert oracle.plan([bad], 4).code == "invalid_arg", bad
+    assert oracle.plan([good] * 9, 4).code == "invalid_arg"
+    huge = Spec(MHA, 1, 1 << 30, 1 << 30, 1 << 30, 8, 1)
+    assert oracle.plan([huge], 1).code == "overflow"
+    # anchors must be multiples of the itemsize: a 1-byte sub-pool of odd size, then a 2-byte one
+    odd = Spec(MLA, 1, 1, 3, 0, 1, 1)
+    assert oracle.plan([odd, Spec(MLA, 1, 1, 4, 0, 2, 1)], 1).code == "alignment"
+
+
+# ---------------------------------------------------------------------------
+# translate
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind,L,ps,P", [(MHA, 2, 4, 5), (MHA, 1, 1, 3), (MLA, 3, 2, 4), (MHA, 3, 16, 2)])
+def test_translate_brute_force_against_walk(kind, L, ps, P):
+    spec = make_spec(kind, L, P, 1, 4, 2)
+    pool = oracle.OraclePool([spec], ps)
+    rb = pool.plan.subs[0].row_bytes
+    addrs, _ = walk(P, L, kind, ps, rb)
+    slots = np.arange(P * ps, dtype=np.int64)
+    ids, flags = pool.translate(0, slots)
+    assert flags == frozenset()
+    base = pool.view_base(0, 0, 0)
+    for t, kid in zip(slots, ids):
+        p, o = divmod(int(t), ps)
+        assert base + int(kid) * rb == addrs[(p, 0, 0, o)]
+
+
+def test_translate_tombstones_unmapped_and_range():
+    ps, L, P = 4, 2, 6
+    bpp = 2 * L
+    pool = oracle.OraclePool([make_spec(MHA, L, P, 2, 8, 2)], ps)
+    ids, flags = pool.translate(0, [-1, -5, -4, 0, 3])
+    assert ids.tolist() == [0, 0, 0, 0, 3] and flags == frozenset()
+    ids, flags = pool.translate(0, [P * ps])
+    assert ids.tolist() == [0] and flags == {"slot_range"}
+    # with a virtual-to-physical table: page 0 -> 2, page 1 unmapped, page 2 -> 5, page 3 -> 9 (past the pool)
+    v2p = np.array([2, -1, 5, 9], dtype=np.int32)
+    slots = np.array([1, 5, 10, -1, 14, 17], dtype=np.int64)
+    ids, flags = pool.translate(0, slots, v2p)
+    exp = [2 * ps * bpp + 1, 0, 5 * ps * bpp + 2, 0, 0, 0]
+    assert ids.tolist() == exp
+    assert flags == {"slot_range"}
+    # ps == 1: phys * blocks_per_page
+    pool1 = oracle.OraclePool([make_spec(MHA, L, P, 2, 8, 2)], 1)
+    ids, _ = pool1.translate(0, np.arange(P))
+    assert ids.tolist() == [p * bpp for p in range(P)]
+    # one block per page: the kernel-facing id is the physical slot
+    ids = [oracle.kernel_id(t, ps, 1) for t in range(P * ps)]
+    assert ids == list(range(P * ps))
+
+
+def test_translate_pages_matches_first_slot_rows():
+    ps, L, P = 4, 3, 7
+    pool = oracle.OraclePool([make_spec(MHA, L, P, 2, 8, 2)], ps)
+    rb = 32
+    addrs, _ = walk(P, L, MHA, ps, rb)
+    pages = np.array([0, 3, 6, -1, 2], dtype=np.int32)
+    kp, flags = pool.translate_pages(0, pages)
+    assert flags == frozenset()
+    base = pool.view_base(0, 0, 0)
+    for q, e in zip(pages, kp):
+        if q < 0:
+            assert e == 0
+            continue
+        for o in range(ps):
+            assert base + (int(e) * ps + o) * rb == addrs[(int(q), 0, 0, o)]
+    kp, flags = pool.translate_pages(0, np.array([7], dtype=np.int32))
+    assert kp.tolist() == [0] and flags == {"slot_range"}
+    kp, flags = pool.translate_pages(0, np.array([1, 0, 2], dtype=np.int32), v2p=np.array([4, -3], dtype=np.int32))
+    assert kp.tolist() == [0, 4 * 2 * L, 0] and flags == {"slot_range"}
+
+
+# ---------------------------------------------------------------------------
+# store / gather / move against the strided reference
+# ---------------------------------------------------------------------------
+
+def _filled_pool(shapes, ps, seed=7):
+    specs = [Spec(s.kind, s.layer_num, s.head_num, s.head_dim, s.v_head_dim, s.elem_bytes, s.num_pages) for s in shapes]
+    req = oracle.plan(specs, ps).required_bytes
+    n = (req + 7) // 8 * 8
+    raw = W.fill_pattern_host(seed, 0, n).copy()
+    return oracle.OraclePool(specs, ps, raw), raw
+
+
+def _strided(pool, sub):
+    s, sp = pool.specs[sub], pool.plan.subs[sub]
+    return StridedPool(pool.raw, sp.anchor_bytes, s.num_pages, s.layer_num, s.kind == MLA, pool.page_size, sp.row_bytes)
+
+
+def _rows(seed, n, rb):
+    return W.normal_bf16_host(seed, n * rb // 2).view(np.uint8).reshape(n, rb)
+
+
+def test_store_matches_strided_reference_tiny():
+    w = W.tiny_mha()
+    pool, raw = _filled_pool(w.shapes, w.page_size)
+    ref_raw = raw.copy()
+    ref = StridedPool(ref_raw, 0, 16, 2, False, 4, 32)
+    slots = w.store_slots[0]
+    ids, flags = pool.translate(0, slots)
+    assert flags == frozenset()
+    for layer in range(2):
+        k = _rows(10 + layer, slots.size, 32)
+        v = _rows(20 + layer, slots.size, 32)
+        assert pool.store(0, layer, ids, k, v) == frozenset()
+        # reference: live slots at (page, offset); tombstones at the page-0 sink row, in order
+        ref.store_slots(layer, slots, k, v)
+        for i in np.nonzero(slots < 0)[0]:
+            ref.env[0, layer, 0, 0] = k[i]
+            ref.env[0, layer, 1, 0] = v[i]
+    assert np.array_equal(raw, ref_raw)
+
+
+def test_store_skips_and_flags_ids_off_the_kernel_space():
+    pool, raw = _filled_pool([W.mha(2, 2, 8, 4)], 4)
+    before = raw.copy()
+    bad = [4, 15, 4 * 16, -2]  # block 1 of page 0, block 3 of page 0, page 4 (past the pool), negative
+    for i in bad:
+        assert pool.store(0, 0, [i], _rows(1, 1, 32), _rows(2, 1, 32)) == {"bad_id"}
+    assert np.array_equal(raw, before)
+
+
+@pytest.mark.parametrize("window", [0, 3, 8, 100])
+def test_gather_matches_strided_reference(window):
+    w = W.tiny_mha()
+    pool, raw = _filled_pool(w.shapes, w.page_size)
+    ref = _strided(pool, 0)
+    pages, lens = w.req_pages[0], w.req_lens[0]
+    table = W.padded_table(pages)
+    bt, flags = pool.translate_pages(0, table)
+    assert flags == frozenset()
+    cu = W.out_offsets(lens, window)
+    for layer in range(2):
+        k_out = np.zeros((cu[-1], 32), dtype=np.uint8)
+        v_out = np.zeros((cu[-1], 32), dtype=np.uint8)
+        assert pool.gather(0, layer, bt, lens, cu, window, k_out, v_out) == frozenset()
+        rk, rv = ref.gather_pages(layer, pages, lens, window)
+        assert np.array_equal(k_out, rk) and np.array_equal(v_out, rv)
+
+
+def test_store_then_gather_round_trip_and_mla():
+    w = W.hybrid(num_reqs=3, len_lo=5, len_hi=150, layer_num=2, window=7)
+    pool, raw = _filled_pool(w.shapes, w.page_size)
+    for sub in (0, 1):
+        rb = pool.row_bytes(sub)
+        slots = w.store_slots[sub]
+        ids, _ = pool.translate(sub, slots)
+        bt, _ = pool.translate_pages(sub, W.padded_table(w.req_pages[sub]))
+        lens = w.req_lens[sub]
+        for layer in range(2):
+            k = _rows(30 + layer + 10 * sub, slots.size, rb)
+            v = _rows(40 + layer, slots.size, rb) if sub == 0 else None
+            assert pool.store(sub, layer, ids, k, v) == frozenset()
+            win = w.windows[sub][layer]
+            cu = W.out_offsets(lens, win)
+            ko = np.zeros((cu[-1], rb), dtype=np.uint8)
+            vo = np.zeros((cu[-1], rb), dtype=np.uint8) if sub == 0 else None
+            assert pool.gather(sub, layer, bt, lens, cu, win, ko, vo) == frozenset()
+            # expected: request r keeps its last `win` positions (all when win == 0)
+            starts = np.concatenate([[0], np.cumsum(lens)])
+            keep = np.concatenate([np.arange(starts[r] + (lens[r] - win if 0 < win < lens[r] else 0), starts[r + 1])
+                                   for r in range(len(lens))])
+            assert np.array_equal(ko, k[keep])
+            if sub == 0:
+                assert np.array_equal(vo, v[keep])
+    # nothing outside the two sub-pools' envelopes moved: the tail pad is intact
+    end = pool.plan.subs[1].anchor_bytes + pool.plan.subs[1].envelope_bytes
+    fill = W.fill_pattern_host(7, 0, (pool.plan.required_bytes + 7) // 8 * 8)
+    assert np.array_equal(raw[end:], fill[end:])
+
+
+def test_gather_flags_bad_blocks_and_layout():
+    pool, raw = _filled_pool([W.mha(2, 2, 8, 4)], 4)
+    lens = np.array([3, 2], dtype=np.int32)
+    bt = np.array([[4, 0], [5, 0]], dtype=np.int32)  # 5 is not a multiple of the 4 blocks per page
+    cu = W.out_offsets(lens)
+    ko = np.zeros((5, 32), np.uint8)
+    vo = np.zeros((5, 32), np.uint8)
+    assert pool.gather(0, 0, bt, lens, cu, 0, ko, vo) == {"bad_block"}
+    assert not ko[3:].any()
+    cu_bad = np.array([0, 2, 5], dtype=np.int64)  # request 0 gets 2 rows for 3 positions, request 1 gets 3 for 2
+    assert "layout" in pool.gather(0, 0, np.array([[4, 0], [8, 0]], np.int32), lens, cu_bad, 0, ko, vo)
+    ko2 = np.zeros((6, 32), np.uint8)
+    assert pool.gather(0, 0, np.array([[4, 0], [8, 0]], np.int32), lens, cu, 0, ko2, ko2.copy()) == {"layout"}
+
+
+def test_move_matches_strided_reference_and_is_reversible():
+    w = W.tiny_mha()
+    pool, raw = _filled_pool(w.shapes, w.page_size)
+    orig = raw.copy()
+    ref_raw = raw.copy()
+    ref = StridedPool(ref_raw, 0, 16, 2, False, 4, 32)
+    src_ids, _ = pool.translate(0, w.move_src[0])
+    dst_ids, _ = pool.translate(0, w.move_dst[0])
+    assert pool.move(0, dst_ids, src_ids, 0, 2) == frozenset()
+    for layer in range(2):
+        for kv in (0, 1):
+            snap = [ref.row(layer, kv, *divmod(int(s), 4)).copy() for s in w.move_src[0]]
+            for d, row in zip(w.move_dst[0], snap):
+                ref.env[divmod(int(d), 4)[0], layer, kv, divmod(int(d), 4)[1]] = row
+    assert np.array_equal(raw, ref_raw)
+    # moving the original dst contents back needs them saved: a move is a gather(src) then a store(dst)
+    pool2, raw2 = _filled_pool(w.shapes, w.page_size)
+    for layer in range(2):
+        rows_k = np.stack([orig[pool.view_base(0, layer, 0) + int(i) * 32:][:32] for i in src_ids])
+        rows_v = np.stack([orig[pool.view_base(0, layer, 1) + int(i) * 32:][:32] for i in src_ids])
+        pool2.store(0, layer, dst_ids, rows_k, rows_v)
+    assert np.array_equal(raw2, raw)
+    # src and dst swapped twice restores the pool
+    pool3, raw3 = _filled_pool(w.shapes, w.page_size)
+    both_a = np.concatenate([src_ids, dst_ids])
+    both_b = np.concatenate([dst_ids, src_ids])
+    pool3.move(0, both_b, both_a, 0, 2)
+    assert not np.array_equal(raw3, orig)
+    pool3.move(0, both_b, both_a, 0, 2)
+    assert np.array_equal(raw3, orig)
+
+
+def test_move_partial_layer_range_and_bad_ids():
+    w = W.tiny_mha()
+    pool, raw = _filled_pool(w.shapes, w.page_size)
+    orig = raw.copy()
+    src_ids, _ = pool.translate(0, w.move_src[0])
+    dst_ids, _ = pool.translate(0, w.move_dst[0])
+    pool.move(0, dst_ids, src_ids, 1, 2)
+    for kv in (0, 1):
+        b0 = pool.view_base(0, 0, kv)
+        for i in dst_ids:
+            assert np.array_equal(raw[b0 + int(i) * 32:][:32], orig[b0 + int(i) * 32:][:32])  # layer 0 untouched
+    raw[:] = orig
+    assert pool.move(0, np.array([5], np.int32), src_ids[:1], 0, 2) == {"bad_id"}
+    assert np.array_equal(raw, orig)
+
+
+def test_layer_view_4d_agrees_with_dense_rows():
+    """The old 4-D per-layer view (page, offset, head, dim) and the dense 3-D view read the same words."""
+    spec = make_spec(MHA, 3, 4, 2, 8, 2)
+    pool, raw = _filled_pool([W.mha(3, 2, 8, 4)], 2)
+    for l, kv in itertools.product(range(3), (0, 1)):
+        v4 = layer_view_4d(raw, 0, 4, 3, 2, 2, 2, 8, 2, l, kv)
+        base = pool.view_base(0, l, kv)
+        for p, o in itertools.product(range(4), range(2)):
+            kid = oracle.kernel_id(p * 2 + o, 2, 6)
+            dense = raw[base + kid * 32: base + kid * 32 + 32].view(np.uint16).reshape(2, 8)
+            assert np.array_equal(v4[p, o], dense)
