@@ -1,0 +1,261 @@
+/*
+ * ukv.h - unified page-major KV-cache pool on AMD Instinct MI355X (gfx950).
+ *
+ * One raw uint8 HBM buffer holds every sub-pool's KV cache.  A page of an MHA
+ * sub-pool is the envelope [L0_K*ps | L0_V*ps | L1_K*ps | ...]: 2L blocks of
+ * ps equally wide rows.  Every (layer, K/V) pair is a dense view
+ * (n_rows, head_num, head_dim) whose base is the start of block 2l (K) or
+ * 2l+1 (V), so all views share one kernel-facing id space
+ *
+ *     kernel_id(t) = (t / ps) * (ps * blocks_per_page) + t % ps,
+ *
+ * with blocks_per_page = 2L for MHA and L for MLA.  On that pool this library
+ * runs four HIP kernels: id translation, the per-layer K/V scatter-store, the
+ * block-table gather and the row move.
+ *
+ * Source for the method: the report page "PR #34602: feat(unified-memory):
+ * dense KV views for uniform-row MHA/SWA models" (sgl-project/sglang), cited
+ * below as DKV with its section headings: 执行摘要 (summary), 功能与动机
+ * (motivation), 实现拆解 (implementation) steps 1-5, 关键文件 (key files),
+ * 关键源码片段 (key excerpts: unified_memory_pool.py, multi_ended_allocator.py,
+ * layout/page_major.py), 评论区精华 (review), 风险与影响 (risks).
+ *
+ * Conventions for every entry point:
+ *  - Return UKV_OK (0) or a negative UKV_ERR_* code; on error
+ *    ukv_last_error() gives a readable message (thread-local).  Nothing is
+ *    launched when a call returns an error.
+ *  - Pointers named *_dev are device pointers on the pool's device; the
+ *    caller owns them (the library never frees caller memory).
+ *  - Data-path calls are asynchronous on `stream` (0 = the null stream),
+ *    never allocate and never synchronise.  They only check host-visible
+ *    arguments; conditions found on the device (an id off the kernel-facing
+ *    id space, a bad block-table entry, ...) skip the affected row and set a
+ *    sticky per-pool flag, read with ukv_pool_error_flags().
+ *  - The calling thread's current HIP device must be the pool's device.
+ */
+#ifndef UKV_H
+#define UKV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes --------------------------------------------------------- */
+#define UKV_OK 0
+#define UKV_ERR_INVALID_ARG -1
+#define UKV_ERR_ASYMMETRIC_KV -2   /* MHA spec with head_dim != v_head_dim */
+#define UKV_ERR_KERNEL_ID_BOUND -3 /* kernel-facing rows would reach 2^31 */
+#define UKV_ERR_OVERFLOW -4        /* byte sizes overflow 64 bits */
+#define UKV_ERR_ALIGNMENT -5       /* misaligned anchor or buffer */
+#define UKV_ERR_TAIL_PAD -6        /* raw buffer smaller than envelopes + tail pad */
+#define UKV_ERR_HIP -7             /* a HIP runtime call failed */
+
+/* ---- sticky device flags (ukv_pool_error_flags) --------------------------- */
+#define UKV_FLAG_SLOT_RANGE 1u /* translate: slot / page past the pool or the v2p table; wrote 0 */
+#define UKV_FLAG_BAD_ID 2u     /* store/move: id not a kernel-facing row id; row skipped */
+#define UKV_FLAG_BAD_BLOCK 4u  /* gather: block-table entry not a kernel-facing page; row skipped */
+#define UKV_FLAG_LAYOUT 8u     /* gather: cu_out / seq_lens / out_rows disagree; row skipped */
+
+/* ---- sub-pool kinds -------------------------------------------------------- */
+#define UKV_MHA 0 /* a K row and a V row per token per layer: blocks_per_page = 2L */
+#define UKV_MLA 1 /* one latent row per token per layer:   blocks_per_page = L  */
+
+#define UKV_MAX_SUB 8
+
+/*
+ * One sub-pool.  Row bytes = head_num * head_dim * elem_bytes.  MLA: the
+ * latent row is head_num = 1, head_dim = 576 for the usual 512 + 64 latent;
+ * v_head_dim is ignored.  elem_bytes is the stored dtype's itemsize
+ * (1, 2, 4 or 8); rows are moved as bytes, never converted.
+ */
+typedef struct ukv_subpool_spec {
+    int32_t kind;
+    int32_t layer_num;
+    int32_t head_num;
+    int32_t head_dim;
+    int32_t v_head_dim;
+    int32_t elem_bytes;
+    int64_t num_pages; /* pages of this sub-pool; page 0 serves as the tombstone sink */
+} ukv_subpool_spec;
+
+typedef struct ukv_subpool_plan {
+    uint64_t row_bytes;
+    int64_t blocks_per_page; /* 2L (MHA) or L (MLA) */
+    uint64_t page_bytes;     /* one page envelope = ps * blocks_per_page * row_bytes */
+    int64_t n_rows;          /* rows of each dense view = num_pages * blocks_per_page * ps */
+    uint64_t anchor_bytes;   /* byte offset of the sub-pool's first page in the raw buffer */
+    uint64_t envelope_bytes; /* num_pages * page_bytes */
+    uint64_t tail_pad_bytes; /* this spec's view tail pad: one page envelope */
+} ukv_subpool_plan;
+
+typedef struct ukv_plan {
+    int32_t n_sub;
+    int32_t reserved;
+    int64_t page_size;
+    uint64_t envelope_bytes; /* all sub-pools, back to back in spec order */
+    uint64_t tail_pad_bytes; /* max over the specs */
+    uint64_t required_bytes; /* envelope_bytes + tail_pad_bytes: the raw buffer size */
+    ukv_subpool_plan sub[UKV_MAX_SUB];
+} ukv_plan;
+
+/* A dense per-layer view: element (row, h, d) of type elem_bytes sits at byte
+ * byte_offset + row * row_bytes + (h * head_dim + d) * elem_bytes of the raw buffer. */
+typedef struct ukv_view {
+    uint64_t byte_offset;
+    int64_t n_rows;
+    int32_t head_num;
+    int32_t head_dim;
+    int32_t elem_bytes;
+    int32_t reserved;
+    uint64_t row_bytes;
+    int64_t stride_elems[3]; /* (head_num * head_dim, head_dim, 1) */
+} ukv_view;
+
+typedef struct ukv_pool ukv_pool;
+
+/*
+ * Pool plan: spec arithmetic and the start-up gates, pure host code (no
+ * device, no allocation).  DKV 实现拆解 step 2 and the unified_memory_pool.py
+ * excerpt: blocks_per_page from the spec (MHA 2L, MLA L); the view tail pad
+ * derived from the specs as their maximum (MHA: page_size * entry bytes, one
+ * page envelope; MLA read the same way); the asymmetric-KV gate (an MHA spec
+ * needs head_dim == v_head_dim, MLA is exempt); the kernel-facing row bound
+ * num_pages * blocks_per_page * ps < 2^31 (DKV 风险 item 5).  Sub-pools sit
+ * back to back in spec order from byte 0.
+ *
+ * specs: host array of n_specs (1..UKV_MAX_SUB) specs; page_size >= 1.
+ * out:   host struct, filled on success.
+ * Errors: INVALID_ARG, ASYMMETRIC_KV, KERNEL_ID_BOUND, OVERFLOW, ALIGNMENT
+ * (an anchor that is not a multiple of its sub-pool's itemsize).
+ */
+int ukv_pool_plan(const ukv_subpool_spec *specs, int32_t n_specs, int64_t page_size, ukv_plan *out);
+
+/*
+ * Pool over a caller-owned device buffer (DKV unified_memory_pool.py excerpt:
+ * one uint8 buffer of total bytes + the derived tail pad).  Plans the specs,
+ * then borrows raw_dev: it must be a device allocation on the current
+ * device, 16-byte aligned, of at least plan.required_bytes (else
+ * UKV_ERR_TAIL_PAD: no caller can under-allocate the pad).  The handle owns
+ * two 4-byte device words for the sticky flags (allocated here, freed by
+ * ukv_pool_destroy); it never frees raw_dev.  Does not touch the buffer's
+ * contents.  *out is set only on success.
+ */
+int ukv_pool_create(const ukv_subpool_spec *specs, int32_t n_specs, int64_t page_size, void *raw_dev,
+                    uint64_t raw_bytes, ukv_pool **out);
+
+/* Frees the handle and its flag words (not the raw buffer).  NULL is a no-op. */
+int ukv_pool_destroy(ukv_pool *pool);
+
+/* Copy of the pool's plan. */
+int ukv_pool_get_plan(const ukv_pool *pool, ukv_plan *out);
+
+/*
+ * Dense view of (sub, layer, kv) (DKV 实现拆解 step 1, layout/page_major.py
+ * excerpt build_mha_views): base = anchor + (2*layer + kv) * ps * row_bytes
+ * for MHA (kv 0 = K, 1 = V), anchor + layer * ps * row_bytes for MLA (kv
+ * must be 0); n_rows rows.  The last view reaches (blocks_per_page-1)*ps
+ * rows past the last envelope, into the tail pad.
+ */
+int ukv_pool_view(const ukv_pool *pool, int32_t sub, int32_t layer, int32_t kv, ukv_view *out);
+
+/* The same view from a plan and its specs, pure host code (no pool, no device). */
+int ukv_plan_view(const ukv_plan *plan, const ukv_subpool_spec *specs, int32_t sub, int32_t layer, int32_t kv,
+                  ukv_view *out);
+
+/*
+ * Token slots -> kernel-facing row ids (DKV 实现拆解 step 3 and the
+ * multi_ended_allocator.py excerpt, translate_kv_loc_for_kernel): for each
+ * slot t, page = t / ps, offset = t % ps, phys = v2p[page] (identity when
+ * v2p_dev is NULL), id = phys * ps * blocks_per_page + offset.
+ *   t < 0 (tombstone) -> 0, the page-0 sink; phys < 0 (unmapped) -> 0;
+ *   page >= v2p_len, or phys >= num_pages -> 0 and UKV_FLAG_SLOT_RANGE.
+ * slots_dev: int64[n]; v2p_dev: int32[v2p_len] or NULL; out_dev: int32[n].
+ * out_dev must not overlap slots_dev (UKV_ERR_INVALID_ARG): the narrower
+ * int32 outputs of later slots would land on int64 inputs other threads may
+ * not have read yet.  n in [0, 2^31).  Translate once per batch; every layer
+ * reuses the ids.
+ */
+int ukv_translate_loc_for_kernel(const ukv_pool *pool, int32_t sub, const int64_t *slots_dev, int64_t n,
+                                 const int32_t *v2p_dev, int64_t v2p_len, int32_t *out_dev, hipStream_t stream);
+
+/*
+ * Page ids -> block-table entries of the dense views (DKV 功能与动机: every
+ * layer is read through one contiguous tensor and one shared block table):
+ * out = kernel_id(phys * ps) / ps = phys * blocks_per_page, with the same
+ * tombstone / unmapped / range rules as ukv_translate_loc_for_kernel.
+ * pages_dev, out_dev: int32[n]; either the same buffer (each element is read
+ * and then written by one thread) or not overlapping (UKV_ERR_INVALID_ARG).
+ * v2p_dev as above.
+ */
+int ukv_translate_pages_for_kernel(const ukv_pool *pool, int32_t sub, const int32_t *pages_dev, int64_t n,
+                                   const int32_t *v2p_dev, int64_t v2p_len, int32_t *out_dev, hipStream_t stream);
+
+/*
+ * Per-layer scatter-store (DKV 关键文件, memory_pool.py: _store_kv_layer is a
+ * plain 3-D row assignment): K_view[layer][ids[i]] = k[i] and
+ * V_view[layer][ids[i]] = v[i], each a row_bytes byte copy.
+ * ids_dev: int32[n] KERNEL-FACING ids (from ukv_translate_loc_for_kernel):
+ *   virtual or physical slots here silently hit other layers' rows (the
+ *   hazard DKV's review names for an unguarded fused store), so an id that
+ *   is not on some page's block-0 rows is skipped and raises UKV_FLAG_BAD_ID.
+ * k_dev, v_dev: rows of row_bytes at k_dev + i * src_row_stride_bytes
+ *   (src_row_stride_bytes >= row_bytes).  MLA: k_dev is the latent, v_dev
+ *   must be NULL.
+ * Id 0 is the sink row: tombstoned entries all write it and race (any of
+ * them may win, per 4-byte word).  Repeated live ids race the same way.
+ */
+int ukv_store_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t *ids_dev, int64_t n,
+                 const void *k_dev, const void *v_dev, int64_t src_row_stride_bytes, hipStream_t stream);
+
+/*
+ * Block-table gather into contiguous ragged K / V (DKV 功能与动机: a backend
+ * reads a layer through one contiguous tensor plus one shared block table).
+ * Output row o belongs to request r with cu_out[r] <= o < cu_out[r+1] and holds
+ * position j = j0 + (o - cu_out[r]), j0 = seq_lens[r] - window when
+ * 0 < window < seq_lens[r] (a sliding-window layer keeps its last `window`
+ * positions) and 0 otherwise; the source row of position j is
+ * block_table[r * bt_stride + j / ps] * ps + j % ps of the dense view.
+ * block_table_dev: int32[num_reqs * bt_stride], entries from
+ *   ukv_translate_pages_for_kernel (phys * blocks_per_page).  A bad entry
+ *   skips the row and raises UKV_FLAG_BAD_BLOCK.
+ * seq_lens_dev: int32[num_reqs]; cu_out_dev: int64[num_reqs + 1], non-decreasing,
+ *   cu_out[0] = 0, cu_out[num_reqs] = out_rows, cu_out[r+1] - cu_out[r] = kept
+ *   positions of r; a mismatch raises UKV_FLAG_LAYOUT and skips the rows concerned.
+ * k_out_dev, v_out_dev: out_rows * row_bytes bytes each (MLA: v_out_dev NULL).
+ * out_rows in [0, 2^31).  The pool is only read.
+ */
+int ukv_gather_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t *block_table_dev,
+                  int64_t bt_stride, const int32_t *seq_lens_dev, const int64_t *cu_out_dev, int32_t num_reqs,
+                  int32_t window, void *k_out_dev, void *v_out_dev, int64_t out_rows, hipStream_t stream);
+
+/*
+ * Row move on every layer in [layer_begin, layer_end), K and V (DKV 关键文件,
+ * memory_pool.py: _move_kv_cache_impl is a 3-D row copy):
+ * view[l][dst[i]] = view[l][src[i]].  dst_dev, src_dev: int32[n]
+ * kernel-facing ids; the src and dst sets must be disjoint and dst ids
+ * distinct (otherwise rows race).  A pair with an id off the kernel-facing
+ * space is skipped and raises UKV_FLAG_BAD_ID.
+ */
+int ukv_move_kv(const ukv_pool *pool, int32_t sub, const int32_t *dst_dev, const int32_t *src_dev, int64_t n,
+                int32_t layer_begin, int32_t layer_end, hipStream_t stream);
+
+/*
+ * Reads and clears the pool's sticky flags (UKV_FLAG_*): enqueued on
+ * `stream` after the work already there, then synchronises that stream.
+ */
+int ukv_pool_error_flags(ukv_pool *pool, hipStream_t stream, uint32_t *out_and_clear);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char *ukv_last_error(void);
+
+/* Name of a status code, e.g. "UKV_ERR_TAIL_PAD". */
+const char *ukv_status_name(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UKV_H */

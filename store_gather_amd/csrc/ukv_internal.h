@@ -1,0 +1,28 @@
+// Internal declarations shared by the host and kernel translation units of
+// libukv (not installed; the public ABI is include/ukv.h).
+#pragma once
+
+#include "ukv.h"
+
+#include <cstdint>
+
+namespace ukv {
+
+// Records a thread-local message for ukv_last_error() and returns `code`.
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+const char *last_error();
+
+int plan_pool(const ukv_subpool_spec *specs, int32_t n_specs, int64_t page_size, ukv_plan *out);
+int view_of(const ukv_plan &p, const ukv_subpool_spec &s, int32_t sub, int32_t layer, int32_t kv, ukv_view *out);
+
+}  // namespace ukv
+
+struct ukv_pool {
+    ukv_subpool_spec spec[UKV_MAX_SUB];
+    ukv_plan plan;
+    uint8_t *raw;        // borrowed device buffer
+    uint64_t raw_bytes;
+    int device;
+    uint32_t *flags_dev;  // [0] sticky flags, [1] read-back slot; owned
+};

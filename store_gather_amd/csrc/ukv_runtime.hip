@@ -1,0 +1,737 @@
+// libukv: the C-ABI entry points and the HIP kernels of the unified
+// page-major KV pool for gfx950 (MI355X).
+//
+// Source for the method: report page "PR #34602: feat(unified-memory): dense
+// KV views for uniform-row MHA/SWA models" (DKV), 实现拆解 (implementation)
+// steps 1-3, 关键文件 (key files: memory_pool.py, cache_move.py), 功能与动机
+// (motivation) and the multi_ended_allocator.py excerpt.  The pages show
+// Python/torch code and a retired Triton store kernel; nothing here follows
+// either.  Every data-path kernel is a byte copy bounded by HBM bandwidth:
+//
+//  - rows are moved as 16-byte integer vectors (global_load/store_dwordx4)
+//    whenever the row size, the view bases and the caller's pointers allow,
+//    so bf16 NaN payloads and denormals pass bit-exact;
+//  - one 64-lane wavefront owns a row (or a run of rows): the lanes cover
+//    the row's 16-byte chunks, so every access is a fully coalesced,
+//    contiguous wave-wide transfer;
+//  - per-row bookkeeping (the id, the request, the block-table entry) is
+//    wave-uniform and lives in scalar registers: the wave index is made
+//    uniform with readfirstlane, so those lookups are scalar loads;
+//  - all K and V loads of a row are issued before its stores, to keep
+//    several 1 KiB wave transfers in flight per wave;
+//  - nothing allocates, nothing synchronises; ids are int32 (the pool plan
+//    guarantees every view has fewer than 2^31 rows) and byte addresses are
+//    64-bit (base + (uint64) id * row_bytes), since pools reach hundreds of GiB.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+#include <new>
+#include <type_traits>
+
+#include "ukv_internal.h"
+
+// ----------------------------------------------------------------------------
+// errors
+// ----------------------------------------------------------------------------
+namespace ukv {
+
+namespace {
+thread_local char g_last_error[1024] = "";
+}
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+const char *last_error() { return g_last_error; }
+
+}  // namespace ukv
+
+using ukv::fail;
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+// The wave's index inside the block, made uniform so that everything derived
+// from it is computed in scalar registers.
+__device__ __forceinline__ int wave_in_block() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)); }
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// A kernel-facing row id lies on block 0 of some page: id = page * (ps *
+// blocks_per_page) + offset with offset < ps and page < num_pages.  The view
+// row count n_rows = num_pages * page_stride is below 2^31.
+__device__ __forceinline__ bool kernel_facing(int32_t id, uint32_t n_rows, uint32_t page_stride, uint32_t ps) {
+    return id >= 0 && (uint32_t)id < n_rows && ((uint32_t)id % page_stride) < ps;
+}
+
+// Copies NKV rows of `vecs` V-sized chunks, lanes striding over the chunks;
+// all loads of one round are issued before its stores.
+template <typename V, int NKV, int U>
+__device__ __forceinline__ void copy_rows(V *const (&dst)[NKV], const V *const (&src)[NKV], int vecs, int lane) {
+    for (int c0 = lane; c0 < vecs; c0 += kWave * U) {
+        V buf[NKV][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * kWave;
+            if (c < vecs) {
+#pragma unroll
+                for (int h = 0; h < NKV; ++h) buf[h][u] = src[h][c];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * kWave;
+            if (c < vecs) {
+#pragma unroll
+                for (int h = 0; h < NKV; ++h) dst[h][c] = buf[h][u];
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// translate (DKV 实现拆解 step 3; multi_ended_allocator.py excerpt)
+// ----------------------------------------------------------------------------
+struct TranslateArgs {
+    const int64_t *slots;  // or int32 page ids (pages mode)
+    const int32_t *pages;
+    const int32_t *v2p;
+    int32_t *out;
+    uint32_t *flags;
+    int64_t n;
+    int64_t v2p_len;
+    int64_t ps;
+    int64_t page_stride;  // ps * blocks_per_page
+    int64_t bpp;
+    int64_t num_pages;
+};
+
+// slot t -> id: tombstone (t < 0) -> 0; page = t / ps, offset = t % ps;
+// phys = v2p[page] (identity without a table); unmapped (phys < 0) -> 0;
+// past the table or the pool -> 0 plus UKV_FLAG_SLOT_RANGE;
+// else phys * ps * blocks_per_page + offset.
+__global__ __launch_bounds__(kBlock) void translate_slots_kernel(TranslateArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= a.n) return;
+    const int64_t t = a.slots[i];
+    int32_t id = 0;
+    bool out_of_range = false;
+    if (t >= 0) {
+        const int64_t page = t / a.ps;
+        const int64_t offset = t - page * a.ps;
+        int64_t phys = page;
+        if (a.v2p != nullptr) {
+            if (page >= a.v2p_len) {
+                out_of_range = true;
+                phys = -1;
+            } else {
+                phys = a.v2p[page];
+            }
+        }
+        if (phys >= a.num_pages) {
+            out_of_range = true;
+        } else if (phys >= 0) {
+            id = (int32_t)(phys * a.page_stride + offset);
+        }
+    }
+    a.out[i] = id;
+    if (out_of_range) atomicOr(a.flags, UKV_FLAG_SLOT_RANGE);
+}
+
+// page q -> the dense views' page index of its first slot, phys * blocks_per_page.
+__global__ __launch_bounds__(kBlock) void translate_pages_kernel(TranslateArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= a.n) return;
+    const int64_t q = a.pages[i];
+    int32_t kp = 0;
+    bool out_of_range = false;
+    if (q >= 0) {
+        int64_t phys = q;
+        if (a.v2p != nullptr) {
+            if (q >= a.v2p_len) {
+                out_of_range = true;
+                phys = -1;
+            } else {
+                phys = a.v2p[q];
+            }
+        }
+        if (phys >= a.num_pages) {
+            out_of_range = true;
+        } else if (phys >= 0) {
+            kp = (int32_t)(phys * a.bpp);
+        }
+    }
+    a.out[i] = kp;
+    if (out_of_range) atomicOr(a.flags, UKV_FLAG_SLOT_RANGE);
+}
+
+// ----------------------------------------------------------------------------
+// store (DKV 关键文件: _store_kv_layer, a plain 3-D row assignment)
+// ----------------------------------------------------------------------------
+struct StoreArgs {
+    uint8_t *pool;
+    uint64_t base[2];  // byte offsets of the K and V views of the layer
+    const int32_t *ids;
+    const uint8_t *src[2];
+    int64_t src_stride;
+    int64_t n;
+    uint32_t n_rows;
+    uint32_t page_stride;
+    uint32_t ps;
+    uint32_t row_bytes;
+    int32_t vecs;  // row_bytes / sizeof(V)
+    uint32_t *flags;
+};
+
+// One wave per token: K_view[ids[i]] = k[i], V_view[ids[i]] = v[i].
+template <typename V, int NKV>
+__global__ __launch_bounds__(kBlock) void store_kernel(StoreArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
+    if (i >= a.n) return;
+    const int lane = lane_id();
+    const int32_t id = a.ids[i];
+    if (!kernel_facing(id, a.n_rows, a.page_stride, a.ps)) {
+        if (lane == 0) atomicOr(a.flags, UKV_FLAG_BAD_ID);
+        return;
+    }
+    V *dst[NKV];
+    const V *src[NKV];
+#pragma unroll
+    for (int h = 0; h < NKV; ++h) {
+        dst[h] = reinterpret_cast<V *>(a.pool + a.base[h] + (uint64_t)(uint32_t)id * a.row_bytes);
+        src[h] = reinterpret_cast<const V *>(a.src[h] + i * a.src_stride);
+    }
+    copy_rows<V, NKV, 2>(dst, src, a.vecs, lane);
+}
+
+// ----------------------------------------------------------------------------
+// gather (DKV 功能与动机: one contiguous tensor + one shared block table)
+// ----------------------------------------------------------------------------
+struct GatherArgs {
+    const uint8_t *pool;
+    uint64_t base[2];
+    const int32_t *bt;
+    int64_t bt_stride;
+    const int32_t *seq_lens;
+    const int64_t *cu_out;
+    uint8_t *out[2];
+    int64_t out_rows;
+    int32_t num_reqs;
+    int32_t window;
+    uint32_t ps;
+    uint32_t bpp;
+    uint32_t num_pages;
+    uint32_t row_bytes;
+    int32_t vecs;
+    int32_t rows_per_wave;
+    uint32_t *flags;
+};
+
+// One wave per run of `rows_per_wave` consecutive output rows.  The request
+// of the first row is found by binary search over cu_out; later rows advance
+// it.  Row o of request r holds position j = j0 + (o - cu_out[r]) and reads
+// dense row bt[r][j / ps] * ps + j % ps.
+template <typename V, int NKV>
+__global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
+    const int lane = lane_id();
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (a.cu_out[0] != 0 || a.cu_out[a.num_reqs] != a.out_rows) atomicOr(a.flags, UKV_FLAG_LAYOUT);
+    }
+    const int64_t o0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave_in_block()) * a.rows_per_wave;
+    if (o0 >= a.out_rows) return;
+    const int64_t o1 = o0 + a.rows_per_wave < a.out_rows ? o0 + a.rows_per_wave : a.out_rows;
+
+    // r = number of requests r' >= 1 with cu_out[r'] <= o0 (upper bound).
+    int32_t lo = 0, hi = a.num_reqs;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (a.cu_out[mid + 1] <= o0)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    int32_t r = lo;
+    uint32_t bad = 0;
+    for (int64_t o = o0; o < o1; ++o) {
+        while (r < a.num_reqs && a.cu_out[r + 1] <= o) ++r;
+        if (r >= a.num_reqs || o < a.cu_out[r]) {
+            bad |= UKV_FLAG_LAYOUT;
+            continue;
+        }
+        const int64_t len = a.seq_lens[r];
+        const int64_t j0 = (a.window > 0 && len > a.window) ? len - a.window : 0;
+        const int64_t q = o - a.cu_out[r];
+        if (q >= len - j0) {
+            bad |= UKV_FLAG_LAYOUT;
+            continue;
+        }
+        const uint32_t j = (uint32_t)(j0 + q);  // < seq_lens[r] <= INT32_MAX
+        const uint32_t page_idx = j / a.ps;
+        if ((int64_t)page_idx >= a.bt_stride) {
+            bad |= UKV_FLAG_BAD_BLOCK;
+            continue;
+        }
+        const int32_t kp = a.bt[(int64_t)r * a.bt_stride + page_idx];
+        if (kp < 0 || (uint32_t)kp % a.bpp != 0 || (uint32_t)kp / a.bpp >= a.num_pages) {
+            bad |= UKV_FLAG_BAD_BLOCK;
+            continue;
+        }
+        const uint64_t row = (uint64_t)(uint32_t)kp * a.ps + (j - page_idx * a.ps);
+        V *dst[NKV];
+        const V *src[NKV];
+#pragma unroll
+        for (int h = 0; h < NKV; ++h) {
+            src[h] = reinterpret_cast<const V *>(a.pool + a.base[h] + row * a.row_bytes);
+            dst[h] = reinterpret_cast<V *>(a.out[h] + (uint64_t)o * a.row_bytes);
+        }
+        copy_rows<V, NKV, 2>(dst, src, a.vecs, lane);
+    }
+    if (bad != 0 && lane == 0) atomicOr(a.flags, bad);
+}
+
+// ----------------------------------------------------------------------------
+// move (DKV 关键文件: _move_kv_cache_impl, a 3-D row copy per layer, K and V)
+// ----------------------------------------------------------------------------
+struct MoveArgs {
+    uint8_t *pool;
+    uint64_t base0;       // byte offset of view (layer_begin, kv 0)
+    uint64_t layer_step;  // bytes between consecutive layers' views
+    uint64_t kv_step;     // bytes between a layer's K and V views
+    const int32_t *dst;
+    const int32_t *src;
+    int64_t n;
+    int32_t nl;
+    uint32_t n_rows;
+    uint32_t page_stride;
+    uint32_t ps;
+    uint32_t row_bytes;
+    int32_t vecs;
+    uint32_t *flags;
+};
+
+// One wave per (row pair i, layer l), layers of one pair adjacent in the grid.
+template <typename V, int NKV>
+__global__ __launch_bounds__(kBlock) void move_kernel(MoveArgs a) {
+    const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
+    if (w >= a.n * a.nl) return;
+    const int lane = lane_id();
+    const int64_t i = w / a.nl;
+    const int32_t l = (int32_t)(w - i * a.nl);
+    const int32_t d = a.dst[i];
+    const int32_t s = a.src[i];
+    if (!kernel_facing(d, a.n_rows, a.page_stride, a.ps) || !kernel_facing(s, a.n_rows, a.page_stride, a.ps)) {
+        if (lane == 0 && l == 0) atomicOr(a.flags, UKV_FLAG_BAD_ID);
+        return;
+    }
+    uint8_t *layer_base = a.pool + a.base0 + (uint64_t)l * a.layer_step;
+    V *dst[NKV];
+    const V *src[NKV];
+#pragma unroll
+    for (int h = 0; h < NKV; ++h) {
+        src[h] = reinterpret_cast<const V *>(layer_base + h * a.kv_step + (uint64_t)(uint32_t)s * a.row_bytes);
+        dst[h] = reinterpret_cast<V *>(layer_base + h * a.kv_step + (uint64_t)(uint32_t)d * a.row_bytes);
+    }
+    copy_rows<V, NKV, 2>(dst, src, a.vecs, lane);
+}
+
+__global__ void flags_fetch_clear_kernel(uint32_t *f) {
+    if (threadIdx.x == 0) f[1] = atomicExch(&f[0], 0u);
+}
+
+// ----------------------------------------------------------------------------
+// host helpers
+// ----------------------------------------------------------------------------
+
+// Largest power of two <= 16 dividing every value: the widest integer vector
+// every row access of a call can use.
+int vec_bytes_for(std::initializer_list<uint64_t> values) {
+    uint64_t acc = 16;
+    for (uint64_t v : values) {
+        while (acc > 1 && (v % acc) != 0) acc >>= 1;
+    }
+    return (int)acc;
+}
+
+int check_pool_call(const ukv_pool *pool, int32_t sub, const char *who) {
+    if (pool == nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: null pool", who);
+    if (sub < 0 || sub >= pool->plan.n_sub)
+        return fail(UKV_ERR_INVALID_ARG, "%s: sub-pool %d outside [0, %d)", who, sub, pool->plan.n_sub);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != pool->device)
+        return fail(UKV_ERR_INVALID_ARG, "%s: current device %d is not the pool's device %d", who, dev, pool->device);
+    return UKV_OK;
+}
+
+int check_launch(const char *who) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(UKV_ERR_HIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
+    return UKV_OK;
+}
+
+bool ranges_overlap(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na != 0 && nb != 0 && x < y + nb && y < x + na;
+}
+
+template <int NKV, typename F>
+int dispatch_vec(int vb, F &&f) {
+    switch (vb) {
+        case 16: return f((uint4 *)nullptr);
+        case 8: return f((uint2 *)nullptr);
+        case 4: return f((uint32_t *)nullptr);
+        case 2: return f((uint16_t *)nullptr);
+        default: return f((uint8_t *)nullptr);
+    }
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// C ABI
+// ----------------------------------------------------------------------------
+extern "C" {
+
+int ukv_pool_plan(const ukv_subpool_spec *specs, int32_t n_specs, int64_t page_size, ukv_plan *out) {
+    return ukv::plan_pool(specs, n_specs, page_size, out);
+}
+
+int ukv_pool_create(const ukv_subpool_spec *specs, int32_t n_specs, int64_t page_size, void *raw_dev,
+                    uint64_t raw_bytes, ukv_pool **out) {
+    if (out == nullptr) return fail(UKV_ERR_INVALID_ARG, "ukv_pool_create: null out");
+    ukv_plan plan;
+    int rc = ukv::plan_pool(specs, n_specs, page_size, &plan);
+    if (rc != UKV_OK) return rc;
+    if (raw_dev == nullptr) return fail(UKV_ERR_INVALID_ARG, "ukv_pool_create: null raw buffer");
+    if (((uintptr_t)raw_dev & 15u) != 0)
+        return fail(UKV_ERR_ALIGNMENT, "ukv_pool_create: raw buffer %p is not 16-byte aligned", raw_dev);
+    if (raw_bytes < plan.required_bytes)
+        return fail(UKV_ERR_TAIL_PAD,
+                    "ukv_pool_create: raw buffer holds %llu bytes but the pool needs %llu: %llu of page envelopes "
+                    "plus a %llu-byte view tail pad (one page envelope, the max over the sub-pool specs)",
+                    (unsigned long long)raw_bytes, (unsigned long long)plan.required_bytes,
+                    (unsigned long long)plan.envelope_bytes, (unsigned long long)plan.tail_pad_bytes);
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof(attr));
+    if (hipPointerGetAttributes(&attr, raw_dev) != hipSuccess || attr.type != hipMemoryTypeDevice) {
+        (void)hipGetLastError();
+        return fail(UKV_ERR_INVALID_ARG, "ukv_pool_create: raw buffer %p is not device memory", raw_dev);
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != attr.device)
+        return fail(UKV_ERR_INVALID_ARG, "ukv_pool_create: buffer lives on device %d, current device is %d",
+                    attr.device, dev);
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)raw_dev) == hipSuccess && base != nullptr) {
+        if ((uintptr_t)raw_dev + raw_bytes > (uintptr_t)base + size)
+            return fail(UKV_ERR_INVALID_ARG,
+                        "ukv_pool_create: %llu bytes from %p run past the device allocation (%zu bytes at %p)",
+                        (unsigned long long)raw_bytes, raw_dev, size, (void *)base);
+    } else {
+        (void)hipGetLastError();
+    }
+    ukv_pool *p = new (std::nothrow) ukv_pool;
+    if (p == nullptr) return fail(UKV_ERR_INVALID_ARG, "ukv_pool_create: out of host memory");
+    std::memset(p, 0, sizeof(*p));
+    std::memcpy(p->spec, specs, sizeof(ukv_subpool_spec) * (size_t)n_specs);
+    p->plan = plan;
+    p->raw = (uint8_t *)raw_dev;
+    p->raw_bytes = raw_bytes;
+    p->device = dev;
+    hipError_t e = hipMalloc((void **)&p->flags_dev, 2 * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(p->flags_dev, 0, 2 * sizeof(uint32_t));
+    if (e != hipSuccess) {
+        if (p->flags_dev) (void)hipFree(p->flags_dev);
+        delete p;
+        return fail(UKV_ERR_HIP, "ukv_pool_create: flag words: %s", hipGetErrorString(e));
+    }
+    *out = p;
+    return UKV_OK;
+}
+
+int ukv_pool_destroy(ukv_pool *pool) {
+    if (pool == nullptr) return UKV_OK;
+    hipError_t e = hipFree(pool->flags_dev);
+    delete pool;
+    if (e != hipSuccess) return fail(UKV_ERR_HIP, "ukv_pool_destroy: %s", hipGetErrorString(e));
+    return UKV_OK;
+}
+
+int ukv_pool_get_plan(const ukv_pool *pool, ukv_plan *out) {
+    if (pool == nullptr || out == nullptr) return fail(UKV_ERR_INVALID_ARG, "ukv_pool_get_plan: null argument");
+    *out = pool->plan;
+    return UKV_OK;
+}
+
+int ukv_pool_view(const ukv_pool *pool, int32_t sub, int32_t layer, int32_t kv, ukv_view *out) {
+    if (pool == nullptr || out == nullptr) return fail(UKV_ERR_INVALID_ARG, "ukv_pool_view: null argument");
+    if (sub < 0 || sub >= pool->plan.n_sub)
+        return fail(UKV_ERR_INVALID_ARG, "ukv_pool_view: sub-pool %d outside [0, %d)", sub, pool->plan.n_sub);
+    return ukv::view_of(pool->plan, pool->spec[sub], sub, layer, kv, out);
+}
+
+int ukv_plan_view(const ukv_plan *plan, const ukv_subpool_spec *specs, int32_t sub, int32_t layer, int32_t kv,
+                  ukv_view *out) {
+    if (plan == nullptr || specs == nullptr || out == nullptr)
+        return fail(UKV_ERR_INVALID_ARG, "ukv_plan_view: null argument");
+    if (sub < 0 || sub >= plan->n_sub || plan->n_sub > UKV_MAX_SUB)
+        return fail(UKV_ERR_INVALID_ARG, "ukv_plan_view: sub-pool %d outside [0, %d)", sub, plan->n_sub);
+    return ukv::view_of(*plan, specs[sub], sub, layer, kv, out);
+}
+
+static int translate_common(const ukv_pool *pool, int32_t sub, const void *in, uint64_t in_elem, int64_t n,
+                            const int32_t *v2p, int64_t v2p_len, int32_t *out, hipStream_t stream, bool pages,
+                            const char *who) {
+    int rc = check_pool_call(pool, sub, who);
+    if (rc != UKV_OK) return rc;
+    if (n < 0 || n > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n=%lld outside [0, 2^31)", who, (long long)n);
+    if (n == 0) return UKV_OK;
+    if (in == nullptr || out == nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: null input or output", who);
+    if (v2p != nullptr && v2p_len < 0) return fail(UKV_ERR_INVALID_ARG, "%s: v2p_len < 0", who);
+    const bool same = (const void *)out == in && in_elem == sizeof(int32_t);
+    if (!same && ranges_overlap(in, (uint64_t)n * in_elem, out, (uint64_t)n * sizeof(int32_t)))
+        return fail(UKV_ERR_INVALID_ARG, "%s: output overlaps the input", who);
+    const ukv_subpool_spec &s = pool->spec[sub];
+    const ukv_subpool_plan &q = pool->plan.sub[sub];
+    TranslateArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.slots = (const int64_t *)in;
+    a.pages = (const int32_t *)in;
+    a.v2p = v2p;
+    a.out = out;
+    a.flags = pool->flags_dev;
+    a.n = n;
+    a.v2p_len = v2p == nullptr ? 0 : v2p_len;
+    a.ps = pool->plan.page_size;
+    a.bpp = q.blocks_per_page;
+    a.page_stride = pool->plan.page_size * q.blocks_per_page;
+    a.num_pages = s.num_pages;
+    const unsigned grid = (unsigned)((n + kBlock - 1) / kBlock);
+    if (pages)
+        hipLaunchKernelGGL(translate_pages_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
+    else
+        hipLaunchKernelGGL(translate_slots_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
+    return check_launch(who);
+}
+
+int ukv_translate_loc_for_kernel(const ukv_pool *pool, int32_t sub, const int64_t *slots_dev, int64_t n,
+                                 const int32_t *v2p_dev, int64_t v2p_len, int32_t *out_dev, hipStream_t stream) {
+    return translate_common(pool, sub, slots_dev, sizeof(int64_t), n, v2p_dev, v2p_len, out_dev, stream, false,
+                            "ukv_translate_loc_for_kernel");
+}
+
+int ukv_translate_pages_for_kernel(const ukv_pool *pool, int32_t sub, const int32_t *pages_dev, int64_t n,
+                                   const int32_t *v2p_dev, int64_t v2p_len, int32_t *out_dev, hipStream_t stream) {
+    return translate_common(pool, sub, pages_dev, sizeof(int32_t), n, v2p_dev, v2p_len, out_dev, stream, true,
+                            "ukv_translate_pages_for_kernel");
+}
+
+int ukv_store_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t *ids_dev, int64_t n,
+                 const void *k_dev, const void *v_dev, int64_t src_row_stride_bytes, hipStream_t stream) {
+    const char *who = "ukv_store_kv";
+    int rc = check_pool_call(pool, sub, who);
+    if (rc != UKV_OK) return rc;
+    const ukv_subpool_spec &s = pool->spec[sub];
+    const ukv_subpool_plan &q = pool->plan.sub[sub];
+    if (layer < 0 || layer >= s.layer_num)
+        return fail(UKV_ERR_INVALID_ARG, "%s: layer %d outside [0, %d)", who, layer, s.layer_num);
+    if (n < 0 || n > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n=%lld outside [0, 2^31)", who, (long long)n);
+    const int nkv = s.kind == UKV_MHA ? 2 : 1;
+    if (nkv == 1 && v_dev != nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: MLA sub-pool takes no V rows", who);
+    if (n == 0) return UKV_OK;
+    if (ids_dev == nullptr || k_dev == nullptr || (nkv == 2 && v_dev == nullptr))
+        return fail(UKV_ERR_INVALID_ARG, "%s: null ids, K or V", who);
+    if (src_row_stride_bytes < (int64_t)q.row_bytes)
+        return fail(UKV_ERR_INVALID_ARG, "%s: src_row_stride_bytes=%lld < row bytes %llu", who,
+                    (long long)src_row_stride_bytes, (unsigned long long)q.row_bytes);
+    StoreArgs a;
+    std::memset(&a, 0, sizeof(a));
+    ukv_view vk, vv;
+    ukv::view_of(pool->plan, s, sub, layer, 0, &vk);
+    vv = vk;
+    if (nkv == 2) ukv::view_of(pool->plan, s, sub, layer, 1, &vv);
+    a.pool = pool->raw;
+    a.base[0] = vk.byte_offset;
+    a.base[1] = vv.byte_offset;
+    a.ids = ids_dev;
+    a.src[0] = (const uint8_t *)k_dev;
+    a.src[1] = (const uint8_t *)(nkv == 2 ? v_dev : k_dev);
+    a.src_stride = src_row_stride_bytes;
+    a.n = n;
+    a.n_rows = (uint32_t)q.n_rows;
+    a.page_stride = (uint32_t)(pool->plan.page_size * q.blocks_per_page);
+    a.ps = (uint32_t)pool->plan.page_size;
+    a.row_bytes = (uint32_t)q.row_bytes;
+    a.flags = pool->flags_dev;
+    const int vb = vec_bytes_for({q.row_bytes, vk.byte_offset, vv.byte_offset, (uint64_t)(uintptr_t)pool->raw,
+                                  (uint64_t)(uintptr_t)k_dev, (uint64_t)(uintptr_t)a.src[1],
+                                  (uint64_t)src_row_stride_bytes});
+    a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
+    const int64_t grid = (n + kWavesPerBlock - 1) / kWavesPerBlock;
+    auto launch = [&](auto *tag) {
+        using V = std::remove_pointer_t<decltype(tag)>;
+        if (nkv == 2)
+            hipLaunchKernelGGL((store_kernel<V, 2>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        else
+            hipLaunchKernelGGL((store_kernel<V, 1>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        return check_launch(who);
+    };
+    return dispatch_vec<2>(vb, launch);
+}
+
+int ukv_gather_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t *block_table_dev,
+                  int64_t bt_stride, const int32_t *seq_lens_dev, const int64_t *cu_out_dev, int32_t num_reqs,
+                  int32_t window, void *k_out_dev, void *v_out_dev, int64_t out_rows, hipStream_t stream) {
+    const char *who = "ukv_gather_kv";
+    int rc = check_pool_call(pool, sub, who);
+    if (rc != UKV_OK) return rc;
+    const ukv_subpool_spec &s = pool->spec[sub];
+    const ukv_subpool_plan &q = pool->plan.sub[sub];
+    if (layer < 0 || layer >= s.layer_num)
+        return fail(UKV_ERR_INVALID_ARG, "%s: layer %d outside [0, %d)", who, layer, s.layer_num);
+    if (num_reqs < 0 || window < 0 || out_rows < 0 || out_rows > kMaxGrid)
+        return fail(UKV_ERR_INVALID_ARG, "%s: num_reqs=%d window=%d out_rows=%lld out of range", who, num_reqs,
+                    window, (long long)out_rows);
+    const int nkv = s.kind == UKV_MHA ? 2 : 1;
+    if (nkv == 1 && v_out_dev != nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: MLA sub-pool has no V output", who);
+    if (out_rows == 0) return UKV_OK;
+    if (cu_out_dev == nullptr || k_out_dev == nullptr || (nkv == 2 && v_out_dev == nullptr))
+        return fail(UKV_ERR_INVALID_ARG, "%s: null cu_out or output", who);
+    if (num_reqs > 0 && (block_table_dev == nullptr || seq_lens_dev == nullptr || bt_stride < 1))
+        return fail(UKV_ERR_INVALID_ARG, "%s: null block table / seq_lens or bt_stride < 1", who);
+    GatherArgs a;
+    std::memset(&a, 0, sizeof(a));
+    ukv_view vk, vv;
+    ukv::view_of(pool->plan, s, sub, layer, 0, &vk);
+    vv = vk;
+    if (nkv == 2) ukv::view_of(pool->plan, s, sub, layer, 1, &vv);
+    a.pool = pool->raw;
+    a.base[0] = vk.byte_offset;
+    a.base[1] = vv.byte_offset;
+    a.bt = block_table_dev;
+    a.bt_stride = bt_stride;
+    a.seq_lens = seq_lens_dev;
+    a.cu_out = cu_out_dev;
+    a.out[0] = (uint8_t *)k_out_dev;
+    a.out[1] = (uint8_t *)(nkv == 2 ? v_out_dev : k_out_dev);
+    a.out_rows = out_rows;
+    a.num_reqs = num_reqs;
+    a.window = window;
+    a.ps = (uint32_t)pool->plan.page_size;
+    a.bpp = (uint32_t)q.blocks_per_page;
+    a.num_pages = (uint32_t)s.num_pages;
+    a.row_bytes = (uint32_t)q.row_bytes;
+    a.rows_per_wave = 8;
+    a.flags = pool->flags_dev;
+    const int vb = vec_bytes_for({q.row_bytes, vk.byte_offset, vv.byte_offset, (uint64_t)(uintptr_t)pool->raw,
+                                  (uint64_t)(uintptr_t)k_out_dev, (uint64_t)(uintptr_t)a.out[1]});
+    a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
+    const int64_t waves = (out_rows + a.rows_per_wave - 1) / a.rows_per_wave;
+    const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    auto launch = [&](auto *tag) {
+        using V = std::remove_pointer_t<decltype(tag)>;
+        if (nkv == 2)
+            hipLaunchKernelGGL((gather_kernel<V, 2>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gather_kernel<V, 1>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        return check_launch(who);
+    };
+    return dispatch_vec<2>(vb, launch);
+}
+
+int ukv_move_kv(const ukv_pool *pool, int32_t sub, const int32_t *dst_dev, const int32_t *src_dev, int64_t n,
+                int32_t layer_begin, int32_t layer_end, hipStream_t stream) {
+    const char *who = "ukv_move_kv";
+    int rc = check_pool_call(pool, sub, who);
+    if (rc != UKV_OK) return rc;
+    const ukv_subpool_spec &s = pool->spec[sub];
+    const ukv_subpool_plan &q = pool->plan.sub[sub];
+    if (layer_begin < 0 || layer_begin > layer_end || layer_end > s.layer_num)
+        return fail(UKV_ERR_INVALID_ARG, "%s: layer range [%d, %d) outside [0, %d]", who, layer_begin, layer_end,
+                    s.layer_num);
+    if (n < 0 || n > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n=%lld outside [0, 2^31)", who, (long long)n);
+    const int32_t nl = layer_end - layer_begin;
+    if (n == 0 || nl == 0) return UKV_OK;
+    if (dst_dev == nullptr || src_dev == nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: null dst or src", who);
+    const int64_t waves = n * (int64_t)nl;
+    const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n * layers too large for one launch", who);
+    const int nkv = s.kind == UKV_MHA ? 2 : 1;
+    ukv_view v0;
+    ukv::view_of(pool->plan, s, sub, layer_begin, 0, &v0);
+    MoveArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.pool = pool->raw;
+    a.base0 = v0.byte_offset;
+    a.kv_step = (uint64_t)pool->plan.page_size * q.row_bytes;
+    a.layer_step = (uint64_t)nkv * a.kv_step;
+    a.dst = dst_dev;
+    a.src = src_dev;
+    a.n = n;
+    a.nl = nl;
+    a.n_rows = (uint32_t)q.n_rows;
+    a.page_stride = (uint32_t)(pool->plan.page_size * q.blocks_per_page);
+    a.ps = (uint32_t)pool->plan.page_size;
+    a.row_bytes = (uint32_t)q.row_bytes;
+    a.flags = pool->flags_dev;
+    const int vb = vec_bytes_for({q.row_bytes, v0.byte_offset, a.kv_step, (uint64_t)(uintptr_t)pool->raw});
+    a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
+    auto launch = [&](auto *tag) {
+        using V = std::remove_pointer_t<decltype(tag)>;
+        if (nkv == 2)
+            hipLaunchKernelGGL((move_kernel<V, 2>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        else
+            hipLaunchKernelGGL((move_kernel<V, 1>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        return check_launch(who);
+    };
+    return dispatch_vec<2>(vb, launch);
+}
+
+int ukv_pool_error_flags(ukv_pool *pool, hipStream_t stream, uint32_t *out_and_clear) {
+    if (pool == nullptr || out_and_clear == nullptr)
+        return fail(UKV_ERR_INVALID_ARG, "ukv_pool_error_flags: null argument");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != pool->device)
+        return fail(UKV_ERR_INVALID_ARG, "ukv_pool_error_flags: current device %d is not the pool's device %d", dev,
+                    pool->device);
+    hipLaunchKernelGGL(flags_fetch_clear_kernel, dim3(1), dim3(kWave), 0, stream, pool->flags_dev);
+    int rc = check_launch("ukv_pool_error_flags");
+    if (rc != UKV_OK) return rc;
+    uint32_t host = 0;
+    hipError_t e = hipMemcpyAsync(&host, pool->flags_dev + 1, sizeof(uint32_t), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(UKV_ERR_HIP, "ukv_pool_error_flags: %s", hipGetErrorString(e));
+    *out_and_clear = host;
+    return UKV_OK;
+}
+
+const char *ukv_last_error(void) { return ukv::last_error(); }
+
+const char *ukv_status_name(int status) {
+    switch (status) {
+        case UKV_OK: return "UKV_OK";
+        case UKV_ERR_INVALID_ARG: return "UKV_ERR_INVALID_ARG";
+        case UKV_ERR_ASYMMETRIC_KV: return "UKV_ERR_ASYMMETRIC_KV";
+        case UKV_ERR_KERNEL_ID_BOUND: return "UKV_ERR_KERNEL_ID_BOUND";
+        case UKV_ERR_OVERFLOW: return "UKV_ERR_OVERFLOW";
+        case UKV_ERR_ALIGNMENT: return "UKV_ERR_ALIGNMENT";
+        case UKV_ERR_TAIL_PAD: return "UKV_ERR_TAIL_PAD";
+        case UKV_ERR_HIP: return "UKV_ERR_HIP";
+        default: return "UKV_ERR_UNKNOWN";
+    }
+}
+
+}  // extern "C"

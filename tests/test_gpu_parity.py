@@ -1,0 +1,398 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle.
+
+Integer / byte work, so the bar is bit-exact on every byte of the pool and of
+every output, with one documented exception: the sink row (id 0 of each view)
+that tombstoned store entries all write, where each 4-byte word must come from
+one of those entries' source rows.  Sizes here span several waves and blocks
+with ragged tails; the workload-sized cases are in test_gpu_full.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import store_gather_amd as U
+import ukv_workloads as W
+from parity_util import Pair, bf16_rows, log, rows_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    log(f"\n[gpu] {request.node.name}")
+    torch.cuda.synchronize()
+    yield
+    torch.cuda.synchronize()
+
+
+def test_device_fill_matches_host_fill():
+    t = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    W.fill_pattern_device(t, 11, byte_start=4096, chunk_words=3000)
+    assert np.array_equal(t.cpu().numpy(), W.fill_pattern_host(11, 4096, 1 << 20))
+
+
+# ---------------------------------------------------------------------------
+# translate
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape,ps", [(W.mha(2, 2, 8, 16), 4), (W.mha(32, 8, 128, 300), 16), (W.mla(24, 77), 64),
+                                      (W.mha(3, 1, 8, 9), 1)])
+def test_translate_parity(shape, ps):
+    pair = Pair([shape], ps)
+    P = shape.num_pages
+    g = np.random.default_rng(5)
+    n = 3000
+    slots = g.integers(-3, P * ps + 40, size=n).astype(np.int64)
+    slots[:5] = [-1, 0, P * ps - 1, P * ps, (1 << 40)]
+    ids = U.ukv_translate_loc_for_kernel(pair.gpu, 0, to_dev(slots))
+    exp, ef = pair.orc.translate(0, slots)
+    assert np.array_equal(ids.cpu().numpy(), exp)
+    assert U.ukv_pool_error_flags(pair.gpu) == ef == {"slot_range"}
+    # virtual-to-physical table with unmapped entries and entries past the pool
+    v2p = g.integers(-2, P + 3, size=P + 5).astype(np.int32)
+    slots = g.integers(-2, (P + 7) * ps, size=n).astype(np.int64)
+    ids = U.ukv_translate_loc_for_kernel(pair.gpu, 0, to_dev(slots), v2p=to_dev(v2p))
+    exp, ef = pair.orc.translate(0, slots, v2p)
+    assert np.array_equal(ids.cpu().numpy(), exp)
+    assert U.ukv_pool_error_flags(pair.gpu) == ef
+    # all in range: no flag
+    live = W.live_slots(1, P, ps, min(500, (P - 1) * ps))
+    ids = U.ukv_translate_loc_for_kernel(pair.gpu, 0, to_dev(live))
+    exp, ef = pair.orc.translate(0, live)
+    assert np.array_equal(ids.cpu().numpy(), exp) and ef == frozenset()
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+
+
+def test_translate_pages_parity_and_in_place():
+    pair = Pair([W.mha(4, 2, 8, 50)], 8)
+    g = np.random.default_rng(9)
+    pages = g.integers(-2, 60, size=(37, 11)).astype(np.int32)
+    kp = U.ukv_translate_pages_for_kernel(pair.gpu, 0, to_dev(pages))
+    exp, ef = pair.orc.translate_pages(0, pages)
+    assert np.array_equal(kp.cpu().numpy(), exp)
+    assert U.ukv_pool_error_flags(pair.gpu) == ef == {"slot_range"}
+    # in place (same buffer) is allowed for pages
+    d = to_dev(np.clip(pages, -1, 49))
+    U.ukv_translate_pages_for_kernel(pair.gpu, 0, d, out=d)
+    exp, ef = pair.orc.translate_pages(0, np.clip(pages, -1, 49))
+    assert np.array_equal(d.cpu().numpy(), exp) and ef == frozenset()
+    v2p = g.integers(-1, 50, size=40).astype(np.int32)
+    kp = U.ukv_translate_pages_for_kernel(pair.gpu, 0, to_dev(pages), v2p=to_dev(v2p))
+    exp, ef = pair.orc.translate_pages(0, pages, v2p)
+    assert np.array_equal(kp.cpu().numpy(), exp)
+    assert U.ukv_pool_error_flags(pair.gpu) == ef
+
+
+def test_translate_rejects_overlapping_output():
+    pair = Pair([W.mha(2, 2, 8, 16)], 4)
+    buf = torch.zeros(64, dtype=torch.int64, device="cuda")
+    out = buf.view(torch.int32)[:64]
+    with pytest.raises(U.UkvError) as e:
+        U.ukv_translate_loc_for_kernel(pair.gpu, 0, buf, out=out)
+    assert e.value.status == "UKV_ERR_INVALID_ARG"
+
+
+# ---------------------------------------------------------------------------
+# the tiny pool: store, gather, move
+# ---------------------------------------------------------------------------
+
+def test_tiny_store_gather_move():
+    w = W.tiny_mha(seed=0)
+    pair = Pair(w.shapes, w.page_size)
+    rb = pair.rb(0)
+    slots = w.store_slots[0]
+    ids_d = U.ukv_translate_loc_for_kernel(pair.gpu, 0, to_dev(slots))
+    ids, ef = pair.orc.translate(0, slots)
+    assert np.array_equal(ids_d.cpu().numpy(), ids) and ef == frozenset()
+    for layer in range(2):
+        k = bf16_rows(100 + layer, slots.size, rb)
+        v = bf16_rows(200 + layer, slots.size, rb)
+        U.ukv_store_kv(pair.gpu, 0, layer, ids_d, rows_dev(k), rows_dev(v))
+        assert pair.orc.store(0, layer, ids, k, v) == frozenset()
+        pair.record_store(0, layer, ids, k, v)
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    pair.assert_pools_equal()
+
+    pages, lens = w.req_pages[0], w.req_lens[0]
+    table = W.padded_table(pages)
+    bt_d = U.ukv_translate_pages_for_kernel(pair.gpu, 0, to_dev(table))
+    bt, _ = pair.orc.translate_pages(0, table)
+    assert np.array_equal(bt_d.cpu().numpy(), bt)
+    for window in (0, 3, 8):
+        cu = W.out_offsets(lens, window)
+        for layer in range(2):
+            ko = torch.zeros((int(cu[-1]), rb), dtype=torch.uint8, device="cuda")
+            vo = torch.zeros_like(ko)
+            U.ukv_gather_kv(pair.gpu, 0, layer, bt_d, to_dev(lens), to_dev(cu), window, ko, vo)
+            eko = np.zeros((int(cu[-1]), rb), np.uint8)
+            evo = np.zeros_like(eko)
+            assert pair.orc.gather(0, layer, bt, lens, cu, window, eko, evo) == frozenset()
+            assert np.array_equal(ko.cpu().numpy(), eko) and np.array_equal(vo.cpu().numpy(), evo)
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+
+    src, _ = pair.orc.translate(0, w.move_src[0])
+    dst, _ = pair.orc.translate(0, w.move_dst[0])
+    U.ukv_move_kv(pair.gpu, 0, to_dev(dst), to_dev(src))
+    assert pair.orc.move(0, dst, src, 0, 2) == frozenset()
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    pair.assert_pools_equal()
+
+
+# ---------------------------------------------------------------------------
+# scaled-down workloads: the real row shapes, fewer pages and requests
+# ---------------------------------------------------------------------------
+
+def _store_all_layers(pair, sub, slots, seed, layers=None):
+    rb = pair.rb(sub)
+    ids_d = U.ukv_translate_loc_for_kernel(pair.gpu, sub, to_dev(slots))
+    ids, ef = pair.orc.translate(sub, slots)
+    assert np.array_equal(ids_d.cpu().numpy(), ids) and ef == frozenset()
+    for layer in (range(pair.shapes[sub].layer_num) if layers is None else layers):
+        k = bf16_rows(seed + 2 * layer, slots.size, rb)
+        v = bf16_rows(seed + 2 * layer + 1, slots.size, rb) if pair.kvs(sub) == 2 else None
+        U.ukv_store_kv(pair.gpu, sub, layer, ids_d, rows_dev(k), None if v is None else rows_dev(v))
+        assert pair.orc.store(sub, layer, ids, k, v) == frozenset()
+        pair.record_store(sub, layer, ids, k, v)
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+
+
+def _gather_all_layers(pair, sub, pages, lens, windows, layers=None):
+    rb = pair.rb(sub)
+    table = W.padded_table(pages)
+    bt_d = U.ukv_translate_pages_for_kernel(pair.gpu, sub, to_dev(table))
+    bt, _ = pair.orc.translate_pages(sub, table)
+    lens = np.asarray(lens, dtype=np.int32)
+    lens_d = to_dev(lens)
+    for layer in (range(pair.shapes[sub].layer_num) if layers is None else layers):
+        win = windows[layer]
+        cu = W.out_offsets(lens, win)
+        ko = torch.empty((int(cu[-1]), rb), dtype=torch.uint8, device="cuda")
+        vo = torch.empty_like(ko) if pair.kvs(sub) == 2 else None
+        U.ukv_gather_kv(pair.gpu, sub, layer, bt_d, lens_d, to_dev(cu), win, ko, vo)
+        eko = np.zeros((int(cu[-1]), rb), np.uint8)
+        evo = np.zeros_like(eko) if vo is not None else None
+        assert pair.orc.gather(sub, layer, bt, lens, cu, win, eko, evo) == frozenset()
+        assert np.array_equal(ko.cpu().numpy(), eko), f"layer {layer} K"
+        if vo is not None:
+            assert np.array_equal(vo.cpu().numpy(), evo), f"layer {layer} V"
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+
+
+def test_scaled_decode_8b():
+    w = W.decode_8b(num_pages=64, num_reqs=7, len_lo=50, len_hi=700, new_tokens=37)
+    pair = Pair(w.shapes, w.page_size)
+    _store_all_layers(pair, 0, w.store_slots[0], 1000)
+    pair.assert_pools_equal()
+    _gather_all_layers(pair, 0, w.req_pages[0], w.req_lens[0], w.windows[0])
+
+
+def test_scaled_prefill_8b_with_tombstones_and_move():
+    w = W.prefill_8b(num_pages=96, tokens=900, num_reqs=5, move_rows=150)
+    assert (w.store_slots[0] < 0).sum() == 9
+    pair = Pair(w.shapes, w.page_size)
+    _store_all_layers(pair, 0, w.store_slots[0], 2000)
+    pair.assert_pools_equal()
+    _gather_all_layers(pair, 0, w.req_pages[0], w.req_lens[0], w.windows[0], layers=[0, 13, 31])
+    src, _ = pair.orc.translate(0, w.move_src[0])
+    dst, _ = pair.orc.translate(0, w.move_dst[0])
+    U.ukv_move_kv(pair.gpu, 0, to_dev(dst), to_dev(src))
+    pair.orc.move(0, dst, src, 0, 32)
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    pair.assert_pools_equal()
+
+
+def test_scaled_hybrid_mha_swa_and_mla():
+    w = W.hybrid(num_reqs=6, len_lo=20, len_hi=700, layer_num=24, window=128)
+    pair = Pair(w.shapes, w.page_size)
+    for sub in (0, 1):
+        _store_all_layers(pair, sub, w.store_slots[sub], 3000 + 100 * sub)
+    pair.assert_pools_equal()
+    for sub in (0, 1):
+        _gather_all_layers(pair, sub, w.req_pages[sub], w.req_lens[sub], w.windows[sub])
+    # move within the MLA sub-pool, a partial layer range
+    mv = W.live_slots(4, w.shapes[1].num_pages, 64, 60, sub=77)
+    src, _ = pair.orc.translate(1, mv[:30])
+    dst, _ = pair.orc.translate(1, mv[30:])
+    U.ukv_move_kv(pair.gpu, 1, to_dev(dst), to_dev(src), 5, 19)
+    pair.orc.move(1, dst, src, 5, 19)
+    pair.assert_pools_equal()
+
+
+def test_scaled_move_70b():
+    w = W.move_70b(num_pages=40, rows=200)
+    pair = Pair(w.shapes, w.page_size)
+    src, _ = pair.orc.translate(0, w.move_src[0])
+    dst, _ = pair.orc.translate(0, w.move_dst[0])
+    U.ukv_move_kv(pair.gpu, 0, to_dev(dst), to_dev(src))
+    pair.orc.move(0, dst, src, 0, 80)
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    pair.assert_pools_equal()
+
+
+# ---------------------------------------------------------------------------
+# row widths that need narrower vectors, strided / misaligned sources
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape,ps", [
+    (W.mha(3, 1, 3, 11), 3),                  # 6-byte rows: 2-byte vectors
+    (W.mha(2, 1, 7, 9, elem_bytes=1), 4),     # 7-byte rows: bytes
+    (W.mha(2, 2, 2, 9), 5),                   # 8-byte rows
+    (W.mla(3, 13, latent_dim=20), 2),         # 40-byte rows: 8-byte vectors
+    (W.mha(2, 4, 96, 10, elem_bytes=4), 4),   # 1536-byte rows, fp32 itemsize
+])
+def test_odd_row_sizes(shape, ps):
+    pair = Pair([shape], ps)
+    P = shape.num_pages
+    slots = W.live_slots(3, P, ps, min(40, (P - 1) * ps))
+    _store_all_layers(pair, 0, slots, 4000)
+    pair.assert_pools_equal()
+    g = np.random.default_rng(1)
+    lens = np.array([1, ps, 2 * ps + 1, 0, 3 * ps - 1], dtype=np.int32)
+    pages = [g.integers(1, P, size=max(1, -(-int(n) // ps))).astype(np.int32) for n in lens]
+    _gather_all_layers(pair, 0, pages, lens, [0, 2, 0][: shape.layer_num])
+    mv = W.live_slots(8, P, ps, 20, sub=9)
+    src, _ = pair.orc.translate(0, mv[:10])
+    dst, _ = pair.orc.translate(0, mv[10:])
+    U.ukv_move_kv(pair.gpu, 0, to_dev(dst), to_dev(src))
+    pair.orc.move(0, dst, src, 0, shape.layer_num)
+    pair.assert_pools_equal()
+
+
+def test_strided_and_misaligned_sources():
+    pair = Pair([W.mha(4, 2, 64, 20)], 8)
+    rb = pair.rb(0)
+    slots = W.live_slots(2, 20, 8, 50)
+    ids_d = U.ukv_translate_loc_for_kernel(pair.gpu, 0, to_dev(slots))
+    ids, _ = pair.orc.translate(0, slots)
+    # K and V as halves of one fused [n, 2, rb] tensor: row stride 2 * rb
+    kv = bf16_rows(50, 2 * slots.size, rb).reshape(slots.size, 2, rb)
+    fused = to_dev(kv)
+    U.ukv_store_kv(pair.gpu, 0, 1, ids_d, fused[:, 0], fused[:, 1])
+    pair.orc.store(0, 1, ids, kv[:, 0], kv[:, 1])
+    # sources that start 2 bytes past a 16-byte boundary: narrower vectors
+    big = torch.zeros(slots.size * rb + 2, dtype=torch.uint8, device="cuda")
+    k = bf16_rows(60, slots.size, rb)
+    big[2:].copy_(torch.from_numpy(k.reshape(-1)).cuda())
+    kmis = big[2:].view(slots.size, rb)
+    assert kmis.data_ptr() % 16 == 2
+    U.ukv_store_kv(pair.gpu, 0, 2, ids_d, kmis, kmis)
+    pair.orc.store(0, 2, ids, k, k)
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    pair.assert_pools_equal()
+
+
+# ---------------------------------------------------------------------------
+# device-side conditions: flags raised, rows skipped, exactly as the oracle
+# ---------------------------------------------------------------------------
+
+def test_bad_ids_and_tables_are_flagged_and_skipped():
+    pair = Pair([W.mha(2, 2, 8, 6)], 4)
+    rb = pair.rb(0)
+    # block 1 of page 0, offset 5 >= ps on page 5, block 3 of page 0, negative, past the pool, huge; then a valid id
+    ids = np.array([4, 5 * 16 + 5, 15, -7, 6 * 16, 1 << 30, 16 + 2], dtype=np.int32)
+    k = bf16_rows(1, ids.size, rb)
+    v = bf16_rows(2, ids.size, rb)
+    U.ukv_store_kv(pair.gpu, 0, 1, to_dev(ids), rows_dev(k), rows_dev(v))
+    assert pair.orc.store(0, 1, ids, k, v) == {"bad_id"}
+    assert U.ukv_pool_error_flags(pair.gpu) == {"bad_id"}
+    pair.assert_pools_equal()
+    # move with one bad pair among good ones
+    dst = np.array([16 + 1, 37, 2 * 16 + 3], dtype=np.int32)  # 37 is block 0, offset 5 >= ps
+    src = np.array([3 * 16, 4 * 16 + 2, 5 * 16], dtype=np.int32)
+    U.ukv_move_kv(pair.gpu, 0, to_dev(dst), to_dev(src))
+    assert pair.orc.move(0, dst, src, 0, 2) == {"bad_id"}
+    assert U.ukv_pool_error_flags(pair.gpu) == {"bad_id"}
+    pair.assert_pools_equal()
+    # gather: a block entry that is not a multiple of blocks_per_page, one past the pool,
+    # a table too narrow for the length, and an inconsistent cu_out
+    lens = np.array([5, 3, 9, 2], dtype=np.int32)
+    bt = np.array([[4, 9], [6, 0], [8, 12], [24, 0]], dtype=np.int32)
+    for cu in (W.out_offsets(lens), np.array([0, 5, 7, 16, 19], dtype=np.int64)):
+        rows = int(cu[-1])
+        ko = torch.zeros((rows, rb), dtype=torch.uint8, device="cuda")
+        vo = torch.zeros_like(ko)
+        U.ukv_gather_kv(pair.gpu, 0, 0, to_dev(bt), to_dev(lens), to_dev(cu), 0, ko, vo)
+        eko = np.zeros((rows, rb), np.uint8)
+        evo = np.zeros_like(eko)
+        ef = pair.orc.gather(0, 0, bt, lens, cu, 0, eko, evo)
+        assert U.ukv_pool_error_flags(pair.gpu) == ef and "bad_block" in ef
+        assert np.array_equal(ko.cpu().numpy(), eko) and np.array_equal(vo.cpu().numpy(), evo)
+    # out_rows larger than cu_out[-1]
+    cu = W.out_offsets(lens)
+    ko = torch.zeros((int(cu[-1]) + 3, rb), dtype=torch.uint8, device="cuda")
+    vo = torch.zeros_like(ko)
+    okbt = np.array([[4, 8, 0], [12, 0, 0], [16, 20, 4], [4, 0, 0]], dtype=np.int32)
+    U.ukv_gather_kv(pair.gpu, 0, 1, to_dev(okbt), to_dev(lens), to_dev(cu), 0, ko, vo)
+    eko = np.zeros(ko.shape, np.uint8)
+    evo = np.zeros_like(eko)
+    ef = pair.orc.gather(0, 1, okbt, lens, cu, 0, eko, evo)
+    assert ef == {"layout"} and U.ukv_pool_error_flags(pair.gpu) == ef
+    assert np.array_equal(ko.cpu().numpy(), eko) and np.array_equal(vo.cpu().numpy(), evo)
+
+
+def test_empty_and_degenerate_calls():
+    pair = Pair([W.mha(2, 2, 8, 6), W.mla(2, 5, latent_dim=8)], 4)
+    e64 = torch.empty(0, dtype=torch.int64, device="cuda")
+    e32 = torch.empty(0, dtype=torch.int32, device="cuda")
+    assert U.ukv_translate_loc_for_kernel(pair.gpu, 0, e64).numel() == 0
+    U.ukv_store_kv(pair.gpu, 0, 0, e32, torch.empty((0, 32), dtype=torch.uint8, device="cuda"),
+                   torch.empty((0, 32), dtype=torch.uint8, device="cuda"))
+    U.ukv_move_kv(pair.gpu, 0, e32, e32)
+    ids = to_dev(np.array([17], dtype=np.int32))
+    U.ukv_move_kv(pair.gpu, 0, ids, ids, 1, 1)  # empty layer range
+    # a zero-length request between two others, and an all-tombstone store
+    lens = np.array([3, 0, 2], dtype=np.int32)
+    bt = np.array([[4], [0], [8]], dtype=np.int32)
+    cu = W.out_offsets(lens)
+    ko = torch.zeros((5, 32), dtype=torch.uint8, device="cuda")
+    vo = torch.zeros_like(ko)
+    U.ukv_gather_kv(pair.gpu, 0, 1, to_dev(bt), to_dev(lens), to_dev(cu), 0, ko, vo)
+    eko = np.zeros((5, 32), np.uint8)
+    evo = np.zeros_like(eko)
+    assert pair.orc.gather(0, 1, bt, lens, cu, 0, eko, evo) == frozenset()
+    assert np.array_equal(ko.cpu().numpy(), eko) and np.array_equal(vo.cpu().numpy(), evo)
+    tomb = np.full(5, -1, dtype=np.int64)
+    ids_d = U.ukv_translate_loc_for_kernel(pair.gpu, 1, to_dev(tomb))
+    ids, _ = pair.orc.translate(1, tomb)
+    k = bf16_rows(9, 5, 16)
+    U.ukv_store_kv(pair.gpu, 1, 1, ids_d, rows_dev(k))
+    pair.orc.store(1, 1, ids, k, None)
+    pair.record_store(1, 1, ids, k, None)
+    # no requests, no rows
+    U.ukv_gather_kv(pair.gpu, 1, 0, to_dev(np.zeros((0, 1), np.int32)), e32, to_dev(np.zeros(1, np.int64)), 0,
+                    torch.empty((0, 16), dtype=torch.uint8, device="cuda"))
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    pair.assert_pools_equal()
+
+
+def test_host_argument_errors():
+    pair = Pair([W.mha(2, 2, 8, 6), W.mla(2, 5, latent_dim=8)], 4)
+    ids = to_dev(np.array([16], dtype=np.int32))
+    rows = torch.zeros((1, 32), dtype=torch.uint8, device="cuda")
+    for call in (
+        lambda: U.ukv_store_kv(pair.gpu, 0, 2, ids, rows, rows),           # layer out of range
+        lambda: U.ukv_store_kv(pair.gpu, 1, 0, ids, rows[:, :16], rows[:, :16]),  # MLA takes no V
+        lambda: U.ukv_move_kv(pair.gpu, 0, ids, ids, 1, 3),                # layer range
+    ):
+        with pytest.raises(U.UkvError) as e:
+            call()
+        assert e.value.status == "UKV_ERR_INVALID_ARG"
+    with pytest.raises(U.UkvError) as e:
+        U.ukv_move_kv(pair.gpu, 2, ids, ids, 0, 1)  # no such sub-pool
+    assert e.value.status == "UKV_ERR_INVALID_ARG"
+    with pytest.raises(ValueError):
+        U.ukv_store_kv(pair.gpu, 0, 0, ids.cpu(), rows, rows)  # host tensor never reaches the library
+    # a raw buffer one byte short of the tail pad
+    plan = U.ukv_pool_plan([W.mha(2, 2, 8, 16)], 4)
+    short = torch.empty(int(plan.required_bytes) - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(U.UkvError) as e:
+        U.ukv_pool_create([W.mha(2, 2, 8, 16)], 4, short)
+    assert e.value.status == "UKV_ERR_TAIL_PAD"
+    # host memory is refused before any launch
+    import ctypes
+    host = np.zeros(int(plan.required_bytes), dtype=np.uint8)
+    h = ctypes.c_void_p()
+    rc = U.lib().ukv_pool_create(U._specs_array([W.mha(2, 2, 8, 16)]), 1, 4, host.ctypes.data, host.size,
+                                 ctypes.byref(h))
+    assert rc == -1 and "not device memory" in U.ukv_last_error()
