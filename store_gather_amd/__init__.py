@@ -315,7 +315,7 @@ def ukv_gather_kv(pool: Pool, sub: int, layer: int, block_table: torch.Tensor, s
     _dev_ptr(block_table, "block_table", d, torch.int32)
     _dev_ptr(seq_lens, "seq_lens", d, torch.int32)
     _dev_ptr(cu_out, "cu_out", d, torch.int64)
-    if block_table.dim() != 2 or block_table.stride(1) != 1:
+    if block_table.dim() != 2 or (block_table.numel() > 0 and block_table.stride(1) != 1):
         raise ValueError("block_table must be [num_reqs, width] with unit inner stride")
     num_reqs = seq_lens.numel()
     if block_table.shape[0] != num_reqs or cu_out.numel() != num_reqs + 1:
@@ -332,7 +332,8 @@ def ukv_gather_kv(pool: Pool, sub: int, layer: int, block_table: torch.Tensor, s
     if v_out is not None and v_out.numel() * v_out.element_size() // rb != out_rows:
         raise ValueError("k_out and v_out differ in rows")
     _check(_lib.ukv_gather_kv(pool.handle, sub, layer, block_table.data_ptr(),
-                              block_table.stride(0) if num_reqs else 1, seq_lens.data_ptr(), cu_out.data_ptr(),
+                              block_table.stride(0) if block_table.numel() else 0, seq_lens.data_ptr(),
+                              cu_out.data_ptr(),
                               num_reqs, int(window), k_out.data_ptr(),
                               None if v_out is None else v_out.data_ptr(), out_rows, _stream_handle(stream)))
 
