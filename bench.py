@@ -114,22 +114,23 @@ class DecodeStep:
     def bytes_step(self):
         return self.bytes_translate() + self.L * (self.bytes_store_launch() + self.bytes_gather_launch())
 
-    def run(self, events=None):
+    def run(self, timers=None):
+        """One step; ``timers`` (optional) is an iterator of (store, gather) event pairs,
+        recorded around every launch on the stream the kernels run on."""
         U = self.U
         U.ukv_translate_loc_for_kernel(self.pool, 0, self.slots, out=self.ids)
         U.ukv_translate_pages_for_kernel(self.pool, 0, self.table, out=self.bt)
         for l in range(self.L):
-            if events is not None:
-                events["store"][0].record()
+            ev = next(timers) if timers is not None else None
+            if ev:
+                ev[0][0].record()
             U.ukv_store_kv(self.pool, 0, l, self.ids, self.k_new[l], self.v_new[l])
-            if events is not None:
-                events["store"][1].record()
-                events["store"] = events["store"][2:] if len(events["store"]) > 2 else events["store"]
-                events["gather"][0].record()
+            if ev:
+                ev[0][1].record()
+                ev[1][0].record()
             U.ukv_gather_kv(self.pool, 0, l, self.bt, self.lens, self.cu, 0, self.k_out, self.v_out)
-            if events is not None:
-                events["gather"][1].record()
-                events["gather"] = events["gather"][2:] if len(events["gather"]) > 2 else events["gather"]
+            if ev:
+                ev[1][1].record()
 
 
 def cpu_baseline(W, budget_s=12.0, seed=0):
@@ -186,6 +187,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (3 times), the reference kernel for "
+                         "scaling hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no cross-GPU exchange (each GPU holds its own pool); "
@@ -201,6 +205,14 @@ def main():
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
     step = DecodeStep(torch, U, W, device)
+    if args.copy_calibration:
+        src = torch.full((1 << 30,), 7, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step.run()
@@ -215,18 +227,9 @@ def main():
     start, end = mk(), mk()
     torch.cuda.synchronize()
     start.record()
-    i = 0
+    timers = iter(list(zip(ev_store, ev_gather)))
     for _ in range(args.steps):
-        U.ukv_translate_loc_for_kernel(step.pool, 0, step.slots, out=step.ids)
-        U.ukv_translate_pages_for_kernel(step.pool, 0, step.table, out=step.bt)
-        for l in range(step.L):
-            ev_store[i][0].record()
-            U.ukv_store_kv(step.pool, 0, l, step.ids, step.k_new[l], step.v_new[l])
-            ev_store[i][1].record()
-            ev_gather[i][0].record()
-            U.ukv_gather_kv(step.pool, 0, l, step.bt, step.lens, step.cu, 0, step.k_out, step.v_out)
-            ev_gather[i][1].record()
-            i += 1
+        step.run(timers)
     end.record()
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
