@@ -40,6 +40,11 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def num(x, nd):
+    """Rounded float, or None for a figure that was not measured."""
+    return None if x != x else round(x, nd)
+
+
 def kernel_source_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -122,14 +127,15 @@ class DecodeStep:
         U.ukv_translate_pages_for_kernel(self.pool, 0, self.table, out=self.bt)
         for l in range(self.L):
             ev = next(timers) if timers is not None else None
-            if ev:
+            if ev and ev[0]:
                 ev[0][0].record()
             U.ukv_store_kv(self.pool, 0, l, self.ids, self.k_new[l], self.v_new[l])
-            if ev:
+            if ev and ev[0]:
                 ev[0][1].record()
+            if ev and ev[1]:
                 ev[1][0].record()
             U.ukv_gather_kv(self.pool, 0, l, self.bt, self.lens, self.cu, 0, self.k_out, self.v_out)
-            if ev:
+            if ev and ev[1]:
                 ev[1][1].record()
 
 
@@ -187,6 +193,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch-events", choices=("gather", "all", "none"), default="gather",
+                    help="HIP events recorded around launches inside the timed region: around every "
+                         "gather (default), around gathers and stores, or none")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (3 times), the reference kernel for "
                          "scaling hardware byte counters")
@@ -222,8 +231,8 @@ def main():
 
     n_ev = args.steps * step.L
     mk = lambda: torch.cuda.Event(enable_timing=True)
-    ev_store = [(mk(), mk()) for _ in range(n_ev)]
-    ev_gather = [(mk(), mk()) for _ in range(n_ev)]
+    ev_store = [(mk(), mk()) if args.launch_events == "all" else None for _ in range(n_ev)]
+    ev_gather = [(mk(), mk()) if args.launch_events != "none" else None for _ in range(n_ev)]
     start, end = mk(), mk()
     torch.cuda.synchronize()
     start.record()
@@ -234,8 +243,8 @@ def main():
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    g_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_gather]))
-    s_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_store]))
+    g_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_gather])) if ev_gather[0] else float("nan")
+    s_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_store])) if ev_store[0] else float("nan")
     flags = U.ukv_pool_error_flags(step.pool)
     assert flags == frozenset(), f"device flags raised: {flags}"
 
@@ -280,16 +289,16 @@ def main():
             "stored": round(step.n_new * step.L / (ms_step * 1e-3), 1),
         },
         "per_launch": {
-            "gather_ms": round(g_ms, 4), "gather_GBps": round(g_gbps, 1),
-            "store_ms": round(s_ms, 5), "store_GBps": round(s_gbps, 1),
+            "gather_ms": num(g_ms, 4), "gather_GBps": num(g_gbps, 1),
+            "store_ms": num(s_ms, 5), "store_GBps": num(s_gbps, 1),
         },
         "roofline": {
             "bound": "hbm",
             "kernel": "gather_kernel",
-            "achieved": round(g_gbps, 1),
+            "achieved": num(g_gbps, 1),
             "peak": PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(g_gbps / PEAK_GBPS, 4),
+            "frac": num(g_gbps / PEAK_GBPS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": step.bytes_gather_launch(),
         },
