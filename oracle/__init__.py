@@ -117,6 +117,14 @@ def lib() -> ctypes.CDLL:
         L.orc_gather.restype = None
         L.orc_move.argtypes = [ctypes.POINTER(_Pool), vp, vp, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32)]
         L.orc_move.restype = ctypes.c_int
+        L.orc_store_map.argtypes = [ctypes.POINTER(_Pool), ctypes.c_int, vp, i64, vp, vp, ctypes.POINTER(ctypes.c_uint32)]
+        L.orc_store_map.restype = None
+        L.orc_gather_map.argtypes = [ctypes.POINTER(_Pool), ctypes.c_int, vp, i64, vp, vp, i32, i32, i64, vp, vp,
+                                     ctypes.POINTER(ctypes.c_uint32)]
+        L.orc_gather_map.restype = None
+        L.orc_move_map.argtypes = [ctypes.POINTER(_Pool), vp, vp, i64, ctypes.c_int, ctypes.c_int, vp, vp,
+                                   ctypes.POINTER(ctypes.c_uint32)]
+        L.orc_move_map.restype = None
         for fn in ("orc_sizeof_pool", "orc_sizeof_sub_plan", "orc_sizeof_spec"):
             getattr(L, fn).restype = ctypes.c_int
         assert L.orc_sizeof_pool() == ctypes.sizeof(_Pool)
@@ -208,23 +216,35 @@ def translate_pages(pages, page_size, blocks_per_page, num_pages, v2p=None):
 
 
 class OraclePool:
-    """A pool over a host uint8 buffer (the raw envelope + tail pad)."""
+    """A pool over a host uint8 buffer (the raw envelope + tail pad).
 
-    def __init__(self, specs: Sequence[Spec], page_size: int, raw: Optional[np.ndarray] = None):
+    ``raw`` may be ``None`` together with ``addresses_only=True``: the pool then
+    only answers the *_map queries (byte offsets), which never touch the buffer,
+    so pools of any size can be described without host memory."""
+
+    def __init__(self, specs: Sequence[Spec], page_size: int, raw: Optional[np.ndarray] = None,
+                 addresses_only: bool = False):
         self.specs = tuple(specs)
         self.page_size = page_size
         self.plan = plan(self.specs, page_size)
         if self.plan.code != "ok":
             raise ValueError(f"oracle plan rejected: {self.plan.code}")
-        if raw is None:
-            raw = np.zeros(self.plan.required_bytes, dtype=np.uint8)
-        assert raw.dtype == np.uint8 and raw.ndim == 1 and raw.flags.c_contiguous
-        assert raw.size >= self.plan.required_bytes
+        self.addresses_only = addresses_only
+        if addresses_only:
+            raw = None
+        else:
+            if raw is None:
+                raw = np.zeros(self.plan.required_bytes, dtype=np.uint8)
+            assert raw.dtype == np.uint8 and raw.ndim == 1 and raw.flags.c_contiguous
+            assert raw.size >= self.plan.required_bytes
         self.raw = raw
 
     def _pool(self, sub: int) -> _Pool:
         s, sp = self.specs[sub], self.plan.subs[sub]
-        return _Pool(self.raw.ctypes.data, self.raw.size, s.kind, s.layer_num, self.page_size, s.num_pages,
+        # addresses-only pools: a null base, so row pointers are plain byte offsets
+        base = 0 if self.raw is None else self.raw.ctypes.data
+        size = self.plan.required_bytes if self.raw is None else self.raw.size
+        return _Pool(base, size, s.kind, s.layer_num, self.page_size, s.num_pages,
                      _SubPlan(sp.row_bytes, sp.blocks_per_page, sp.page_bytes, sp.n_rows, sp.anchor_bytes,
                               sp.envelope_bytes, sp.tail_pad_bytes))
 
@@ -280,6 +300,47 @@ class OraclePool:
         lib().orc_gather(ctypes.byref(pool), layer, _ptr(bt), bt.shape[1], _ptr(lens), _ptr(cu), lens.size,
                          window, _ptr(k_out), _ptr(v_out), out_rows, ctypes.byref(flags))
         return flag_names(flags.value)
+
+    # -- address maps: byte offsets into raw, -1 for a skipped row --------------
+    def store_map(self, sub: int, layer: int, ids):
+        """(K offsets, V offsets or None, flags) of each store entry."""
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        k_off = np.empty(ids.size, np.int64)
+        v_off = np.empty(ids.size, np.int64) if self.specs[sub].kind == MHA else None
+        flags = ctypes.c_uint32(0)
+        pool = self._pool(sub)
+        lib().orc_store_map(ctypes.byref(pool), layer, _ptr(ids), ids.size, _ptr(k_off), _ptr(v_off),
+                            ctypes.byref(flags))
+        return k_off, v_off, flag_names(flags.value)
+
+    def gather_map(self, sub: int, layer: int, block_table, seq_lens, cu_out, window: int, out_rows: int):
+        """(K source offsets, V source offsets or None, flags) of every output row."""
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        if bt.ndim == 1:
+            bt = bt.reshape(len(seq_lens), -1)
+        lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        cu = np.ascontiguousarray(cu_out, dtype=np.int64)
+        k_src = np.empty(out_rows, np.int64)
+        v_src = np.empty(out_rows, np.int64) if self.specs[sub].kind == MHA else None
+        flags = ctypes.c_uint32(0)
+        pool = self._pool(sub)
+        lib().orc_gather_map(ctypes.byref(pool), layer, _ptr(bt), bt.shape[1], _ptr(lens), _ptr(cu), lens.size,
+                             window, out_rows, _ptr(k_src), _ptr(v_src), ctypes.byref(flags))
+        return k_src, v_src, flag_names(flags.value)
+
+    def move_map(self, sub: int, dst, src, layer_begin: int, layer_end: int):
+        """(dst offsets, src offsets, flags) for every (layer, kv, pair), in that order."""
+        dst = np.ascontiguousarray(dst, dtype=np.int32)
+        src = np.ascontiguousarray(src, dtype=np.int32)
+        kvs = 2 if self.specs[sub].kind == MHA else 1
+        total = dst.size * (layer_end - layer_begin) * kvs
+        d_off = np.empty(total, np.int64)
+        s_off = np.empty(total, np.int64)
+        flags = ctypes.c_uint32(0)
+        pool = self._pool(sub)
+        lib().orc_move_map(ctypes.byref(pool), _ptr(dst), _ptr(src), dst.size, layer_begin, layer_end, _ptr(d_off),
+                           _ptr(s_off), ctypes.byref(flags))
+        return d_off, s_off, flag_names(flags.value)
 
     def move(self, sub: int, dst, src, layer_begin: int, layer_end: int):
         dst = np.ascontiguousarray(dst, dtype=np.int32)

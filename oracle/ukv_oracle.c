@@ -302,35 +302,59 @@ typedef struct {
     orc_sub_plan sp;
 } orc_pool;
 
-static uint8_t *row_ptr(const orc_pool *p, int layer, int kv, int64_t id)
+/* Byte offset of row `id` of the (layer, kv) dense view inside raw. */
+static int64_t row_off(const orc_pool *p, int layer, int kv, int64_t id)
 {
     uint64_t base = 0;
     orc_view_base(&p->sp, p->kind, p->page_size, p->layer_num, layer, kv, &base);
-    return p->raw + base + (uint64_t)id * p->sp.row_bytes;
+    return (int64_t)(base + (uint64_t)id * p->sp.row_bytes);
 }
 
 /*
  * Per-layer store (DKV/files: _store_kv_layer is a plain 3-D row
  * assignment): k_view[layer][ids] = k, v_view[layer][ids] = v.  MLA stores
- * the latent row only (v is NULL).  Entries run in order, so among repeated
- * ids the last one wins.  An id off the kernel-facing id space is not
- * written and raises ORC_F_BAD_ID.
+ * the latent row only (v is NULL).  An id off the kernel-facing id space is
+ * not written and raises ORC_F_BAD_ID.
+ *
+ * orc_store_map gives, for entry i, the byte offset its K (and V) row lands
+ * at, or -1 when the entry is skipped; orc_store copies the rows there, in
+ * entry order, so among repeated ids the last one wins.
  */
-void orc_store(const orc_pool *p, int layer, const int32_t *ids, int64_t n, const uint8_t *k,
-               const uint8_t *v, int64_t src_row_stride, uint32_t *flags)
+void orc_store_map(const orc_pool *p, int layer, const int32_t *ids, int64_t n, int64_t *k_off, int64_t *v_off,
+                   uint32_t *flags)
 {
-    int kvs = p->kind == 0 ? 2 : 1;
     for (int64_t i = 0; i < n; i++) {
         int64_t id = ids[i];
         if (!is_kernel_facing(id, p->page_size, (int64_t)p->sp.blocks_per_page, p->num_pages)) {
             *flags |= ORC_F_BAD_ID;
+            k_off[i] = -1;
+            if (v_off != NULL)
+                v_off[i] = -1;
             continue;
         }
-        for (int kv = 0; kv < kvs; kv++) {
-            const uint8_t *src = (kv == 0 ? k : v) + i * src_row_stride;
-            memcpy(row_ptr(p, layer, kv, id), src, p->sp.row_bytes);
-        }
+        k_off[i] = row_off(p, layer, 0, id);
+        if (v_off != NULL)
+            v_off[i] = p->kind == 0 ? row_off(p, layer, 1, id) : -1;
     }
+}
+
+void orc_store(const orc_pool *p, int layer, const int32_t *ids, int64_t n, const uint8_t *k, const uint8_t *v,
+               int64_t src_row_stride, uint32_t *flags)
+{
+    int64_t *k_off = (int64_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
+    int64_t *v_off = (int64_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
+    if (k_off == NULL || v_off == NULL)
+        abort();
+    orc_store_map(p, layer, ids, n, k_off, v_off, flags);
+    for (int64_t i = 0; i < n; i++) {
+        if (k_off[i] < 0)
+            continue;
+        memcpy(p->raw + k_off[i], k + i * src_row_stride, p->sp.row_bytes);
+        if (p->kind == 0)
+            memcpy(p->raw + v_off[i], v + i * src_row_stride, p->sp.row_bytes);
+    }
+    free(k_off);
+    free(v_off);
 }
 
 /*
@@ -344,16 +368,21 @@ void orc_store(const orc_pool *p, int layer, const int32_t *ids, int64_t n, cons
  *   view, whose block-table entries are kernel-facing page indices.
  * Rows not covered (or past their request's length) raise ORC_F_LAYOUT,
  * bad block-table entries ORC_F_BAD_BLOCK; such rows are not written.
+ *
+ * orc_gather_map gives the byte offsets each output row is read from (-1 for
+ * a skipped row); orc_gather copies them.
  */
-void orc_gather(const orc_pool *p, int layer, const int32_t *bt, int64_t bt_stride,
-                const int32_t *seq_lens, const int64_t *cu_out, int32_t num_reqs, int32_t window,
-                uint8_t *k_out, uint8_t *v_out, int64_t out_rows, uint32_t *flags)
+void orc_gather_map(const orc_pool *p, int layer, const int32_t *bt, int64_t bt_stride, const int32_t *seq_lens,
+                    const int64_t *cu_out, int32_t num_reqs, int32_t window, int64_t out_rows, int64_t *k_src,
+                    int64_t *v_src, uint32_t *flags)
 {
-    int kvs = p->kind == 0 ? 2 : 1;
     int64_t bpp = (int64_t)p->sp.blocks_per_page;
     if (cu_out[0] != 0 || cu_out[num_reqs] != out_rows)
         *flags |= ORC_F_LAYOUT;
     for (int64_t o = 0; o < out_rows; o++) {
+        k_src[o] = -1;
+        if (v_src != NULL)
+            v_src[o] = -1;
         int32_t r = 0;
         while (r < num_reqs && !(o < cu_out[r + 1]))
             r++;
@@ -380,11 +409,31 @@ void orc_gather(const orc_pool *p, int layer, const int32_t *bt, int64_t bt_stri
             continue;
         }
         int64_t row = kp * p->page_size + j % p->page_size;
-        for (int kv = 0; kv < kvs; kv++) {
-            uint8_t *dst = (kv == 0 ? k_out : v_out) + o * (int64_t)p->sp.row_bytes;
-            memcpy(dst, row_ptr(p, layer, kv, row), p->sp.row_bytes);
-        }
+        k_src[o] = row_off(p, layer, 0, row);
+        if (v_src != NULL && p->kind == 0)
+            v_src[o] = row_off(p, layer, 1, row);
     }
+}
+
+void orc_gather(const orc_pool *p, int layer, const int32_t *bt, int64_t bt_stride, const int32_t *seq_lens,
+                const int64_t *cu_out, int32_t num_reqs, int32_t window, uint8_t *k_out, uint8_t *v_out,
+                int64_t out_rows, uint32_t *flags)
+{
+    int64_t *k_src = (int64_t *)malloc((size_t)(out_rows > 0 ? out_rows : 1) * sizeof(int64_t));
+    int64_t *v_src = (int64_t *)malloc((size_t)(out_rows > 0 ? out_rows : 1) * sizeof(int64_t));
+    if (k_src == NULL || v_src == NULL)
+        abort();
+    orc_gather_map(p, layer, bt, bt_stride, seq_lens, cu_out, num_reqs, window, out_rows, k_src, v_src, flags);
+    uint64_t rb = p->sp.row_bytes;
+    for (int64_t o = 0; o < out_rows; o++) {
+        if (k_src[o] < 0)
+            continue;
+        memcpy(k_out + o * (int64_t)rb, p->raw + k_src[o], rb);
+        if (p->kind == 0)
+            memcpy(v_out + o * (int64_t)rb, p->raw + v_src[o], rb);
+    }
+    free(k_src);
+    free(v_src);
 }
 
 /*
@@ -393,32 +442,59 @@ void orc_gather(const orc_pool *p, int layer, const int32_t *bt, int64_t bt_stri
  * layer_end).  The right-hand side is read whole before any write, as a
  * tensor assignment does.  A pair with either id off the kernel-facing id
  * space is skipped and raises ORC_F_BAD_ID.
+ *
+ * orc_move_map lists, for every (layer, kv, i) in that order, the byte
+ * offsets a row is read from and written to (-1 for a skipped pair).
  */
-int orc_move(const orc_pool *p, const int32_t *dst, const int32_t *src, int64_t n, int layer_begin,
-             int layer_end, uint32_t *flags)
+void orc_move_map(const orc_pool *p, const int32_t *dst, const int32_t *src, int64_t n, int layer_begin,
+                  int layer_end, int64_t *dst_off, int64_t *src_off, uint32_t *flags)
 {
     int kvs = p->kind == 0 ? 2 : 1;
     int64_t bpp = (int64_t)p->sp.blocks_per_page;
-    uint64_t rb = p->sp.row_bytes;
-    uint8_t *snap = (uint8_t *)malloc(n > 0 ? (size_t)n * rb : 1);
-    if (snap == NULL)
-        return ORC_INVALID;
+    int64_t at = 0;
     for (int layer = layer_begin; layer < layer_end; layer++) {
         for (int kv = 0; kv < kvs; kv++) {
-            for (int64_t i = 0; i < n; i++) {
-                if (is_kernel_facing(src[i], p->page_size, bpp, p->num_pages))
-                    memcpy(snap + i * rb, row_ptr(p, layer, kv, src[i]), rb);
-            }
-            for (int64_t i = 0; i < n; i++) {
+            for (int64_t i = 0; i < n; i++, at++) {
                 if (!is_kernel_facing(src[i], p->page_size, bpp, p->num_pages) ||
                     !is_kernel_facing(dst[i], p->page_size, bpp, p->num_pages)) {
                     *flags |= ORC_F_BAD_ID;
+                    dst_off[at] = -1;
+                    src_off[at] = -1;
                     continue;
                 }
-                memcpy(row_ptr(p, layer, kv, dst[i]), snap + i * rb, rb);
+                src_off[at] = row_off(p, layer, kv, src[i]);
+                dst_off[at] = row_off(p, layer, kv, dst[i]);
             }
         }
     }
+}
+
+int orc_move(const orc_pool *p, const int32_t *dst, const int32_t *src, int64_t n, int layer_begin, int layer_end,
+             uint32_t *flags)
+{
+    int kvs = p->kind == 0 ? 2 : 1;
+    int64_t total = n * (int64_t)(layer_end - layer_begin) * kvs;
+    uint64_t rb = p->sp.row_bytes;
+    if (total < 0)
+        total = 0;
+    int64_t *dst_off = (int64_t *)malloc((size_t)(total > 0 ? total : 1) * sizeof(int64_t));
+    int64_t *src_off = (int64_t *)malloc((size_t)(total > 0 ? total : 1) * sizeof(int64_t));
+    uint8_t *snap = (uint8_t *)malloc(total > 0 ? (size_t)total * rb : 1);
+    if (dst_off == NULL || src_off == NULL || snap == NULL) {
+        free(dst_off);
+        free(src_off);
+        free(snap);
+        return ORC_INVALID;
+    }
+    orc_move_map(p, dst, src, n, layer_begin, layer_end, dst_off, src_off, flags);
+    for (int64_t a = 0; a < total; a++)
+        if (src_off[a] >= 0)
+            memcpy(snap + a * rb, p->raw + src_off[a], rb);
+    for (int64_t a = 0; a < total; a++)
+        if (dst_off[a] >= 0)
+            memcpy(p->raw + dst_off[a], snap + a * rb, rb);
+    free(dst_off);
+    free(src_off);
     free(snap);
     return ORC_OK;
 }

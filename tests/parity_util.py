@@ -105,3 +105,75 @@ def gather_inputs(pair: Pair, sub: int, pages_per_req, lens, window: int):
     table = W.padded_table(pages_per_req)
     cu = W.out_offsets(lens, window)
     return table, np.asarray(lens, dtype=np.int32), cu
+
+
+# ---------------------------------------------------------------------------
+# pool-sized checks on the device (oracle addresses, regenerated pre-fill)
+# ---------------------------------------------------------------------------
+
+def rows_view(raw: torch.Tensor, anchor: int, envelope: int, rb: int) -> torch.Tensor:
+    """A sub-pool's envelope as [rows, row_bytes] (rows counted from its anchor)."""
+    return raw[anchor: anchor + envelope].view(-1, rb)
+
+
+def offsets_to_rows(off: np.ndarray, anchor: int, rb: int) -> np.ndarray:
+    off = np.asarray(off, dtype=np.int64)
+    assert (off >= anchor).all() and ((off - anchor) % rb == 0).all()
+    return (off - anchor) // rb
+
+
+def pattern_mismatch_rows(raw: torch.Tensor, seed: int, anchor: int, envelope: int, rb: int,
+                          chunk_bytes: int = 1 << 30) -> torch.Tensor:
+    """Rows of [anchor, anchor + envelope) whose bytes differ from the pre-fill pattern."""
+    rows_per_chunk = max(1, chunk_bytes // rb)
+    nrows = envelope // rb
+    out = []
+    scratch = torch.empty(rows_per_chunk * rb, dtype=torch.uint8, device=raw.device)
+    for r0 in range(0, nrows, rows_per_chunk):
+        n = min(rows_per_chunk, nrows - r0)
+        b0 = anchor + r0 * rb
+        exp = scratch[: n * rb]
+        fill_at(exp, seed, b0)
+        diff = (raw[b0: b0 + n * rb].view(n, rb) != exp.view(n, rb)).any(dim=1)
+        out.append(diff.nonzero().flatten() + r0)
+    return torch.cat(out) if out else torch.empty(0, dtype=torch.int64, device=raw.device)
+
+
+def fill_at(t: torch.Tensor, seed: int, byte_start: int) -> None:
+    """The pre-fill pattern for bytes [byte_start, byte_start + t.numel()) of a pool,
+    for any byte alignment (the generator works on 8-byte words)."""
+    lo = byte_start - byte_start % 8
+    hi = byte_start + t.numel()
+    hi8 = (hi + 7) // 8 * 8
+    if lo == byte_start and hi8 == hi:
+        W.fill_pattern_device(t, seed, byte_start=lo)
+        return
+    tmp = torch.empty(hi8 - lo, dtype=torch.uint8, device=t.device)
+    W.fill_pattern_device(tmp, seed, byte_start=lo)
+    t.copy_(tmp[byte_start - lo: byte_start - lo + t.numel()])
+
+
+def assert_bytes_are_pattern(raw: torch.Tensor, seed: int, start: int, end: int) -> None:
+    if end <= start:
+        return
+    exp = torch.empty(end - start, dtype=torch.uint8, device=raw.device)
+    fill_at(exp, seed, start)
+    assert torch.equal(raw[start:end], exp), f"bytes [{start}, {end}) changed"
+
+
+def assert_rows_subset(changed: torch.Tensor, allowed_mask: torch.Tensor, what: str) -> None:
+    """Every changed row is one the operation was meant to write."""
+    if changed.numel() == 0:
+        return
+    bad = changed[~allowed_mask[changed]]
+    assert bad.numel() == 0, f"{what}: {bad.numel()} rows changed that no operation writes, e.g. {bad[:8].tolist()}"
+
+
+def equal_rows_chunked(a: torch.Tensor, a_idx: torch.Tensor, b: torch.Tensor, b_idx, chunk: int = 1 << 20) -> bool:
+    """a[a_idx] == b[b_idx] row for row (b_idx None: b itself), in chunks."""
+    for c0 in range(0, a_idx.numel(), chunk):
+        x = a.index_select(0, a_idx[c0: c0 + chunk])
+        y = b[c0: c0 + chunk] if b_idx is None else b.index_select(0, b_idx[c0: c0 + chunk])
+        if not torch.equal(x, y):
+            return False
+    return True

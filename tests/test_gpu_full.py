@@ -1,0 +1,247 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+The oracle cannot hold a 32-160 GiB envelope on the host, so it answers with
+addresses: for every row a store / gather / move touches, the byte offsets it
+reads and writes (oracle/ukv_oracle.c *_map, an addresses-only pool).  On the
+device the test then checks
+  * every written row against its source (a torch index of the input, never
+    of the HIP path's output),
+  * every gathered row against the envelope row at the oracle's address,
+  * every byte nothing may write against the pre-fill pattern, regenerated
+    from its definition (SplitMix64 over 8-byte words) chunk by chunk,
+  * the sink rows with the tombstone rule (each 4-byte word from one of the
+    tombstoned entries of that call).
+Every output row of every layer is compared; nothing is sampled.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import store_gather_amd as U
+import ukv_workloads as W
+from parity_util import (assert_bytes_are_pattern, assert_rows_subset, equal_rows_chunked, log, offsets_to_rows,
+                         ospecs, pattern_mismatch_rows, round8, rows_view)
+
+pytestmark = pytest.mark.gpu
+SEED = 21
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    log(f"\n[gpu-full] {request.node.name}")
+    torch.cuda.synchronize()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _make(w):
+    plan = U.ukv_pool_plan(w.shapes, w.page_size)
+    n = round8(int(plan.required_bytes))
+    pool = U.allocate_pool(w.shapes, w.page_size, extra_bytes=n - int(plan.required_bytes))
+    W.fill_pattern_device(pool.raw, SEED)
+    orc = oracle.OraclePool(ospecs(w.shapes), w.page_size, addresses_only=True)
+    torch.cuda.synchronize()
+    log(f"  pool {n / 2**30:.2f} GiB filled")
+    return pool, orc
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _translate(pool, orc, sub, slots):
+    ids = U.ukv_translate_loc_for_kernel(pool, sub, _dev(slots))
+    exp, ef = orc.translate(sub, slots)
+    assert np.array_equal(ids.cpu().numpy(), exp) and ef == frozenset()
+    return ids, exp
+
+
+def _block_table(pool, orc, sub, pages):
+    table = W.padded_table(pages)
+    bt = U.ukv_translate_pages_for_kernel(pool, sub, _dev(table))
+    exp, ef = orc.translate_pages(sub, table)
+    assert np.array_equal(bt.cpu().numpy(), exp) and ef == frozenset()
+    return bt, exp
+
+
+def _sub_geom(pool, sub):
+    q = pool.plan.sub[sub]
+    return int(q.anchor_bytes), int(q.envelope_bytes), int(q.row_bytes)
+
+
+def _store_layers(pool, orc, sub, ids_d, ids, slots, masks, value_seed):
+    """Store every layer; check written rows against the sources and the sink rows
+    against the tombstone rule; mark written rows in masks[sub]."""
+    anchor, env, rb = _sub_geom(pool, sub)
+    rows = rows_view(pool.raw, anchor, env, rb)
+    shape = pool.specs[sub]
+    nkv = 2 if shape.kind == W.MHA else 1
+    live = torch.from_numpy(np.nonzero(slots >= 0)[0]).cuda()
+    tomb = torch.from_numpy(np.nonzero(slots < 0)[0]).cuda()
+    n = ids.size
+    for layer in range(shape.layer_num):
+        src = [W.normal_bf16_device((n, rb // 2), value_seed + 2 * layer + h, "cuda").view(torch.uint8)
+               for h in range(nkv)]
+        U.ukv_store_kv(pool, sub, layer, ids_d, src[0], src[1] if nkv == 2 else None)
+        maps = orc.store_map(sub, layer, ids)
+        assert maps[2] == frozenset()
+        for h in range(nkv):
+            r = torch.from_numpy(offsets_to_rows(maps[h], anchor, rb)).cuda()
+            masks[sub][r] = True
+            assert equal_rows_chunked(rows, r[live], src[h], live), f"layer {layer} kv {h}: stored rows"
+            if tomb.numel():
+                sink = rows[int(r[tomb[0]])].view(torch.int32)
+                cand = src[h].index_select(0, tomb).view(tomb.numel(), -1, 4).view(torch.int32).squeeze(-1)
+                assert bool((cand == sink.unsqueeze(0)).any(dim=0).all()), f"layer {layer} kv {h}: sink row"
+    torch.cuda.synchronize()
+
+
+def _check_untouched(pool, masks):
+    for sub in range(len(pool.specs)):
+        anchor, env, rb = _sub_geom(pool, sub)
+        changed = pattern_mismatch_rows(pool.raw, SEED, anchor, env, rb)
+        assert_rows_subset(changed, masks[sub], f"sub-pool {sub}")
+    end = int(pool.plan.envelope_bytes)
+    assert_bytes_are_pattern(pool.raw, SEED, end, pool.raw.numel())  # the tail pad
+
+
+def _gather_layers(pool, orc, sub, bt_d, bt, lens, windows, layers):
+    anchor, env, rb = _sub_geom(pool, sub)
+    rows = rows_view(pool.raw, anchor, env, rb)
+    nkv = 2 if pool.specs[sub].kind == W.MHA else 1
+    lens = np.asarray(lens, dtype=np.int32)
+    lens_d = _dev(lens)
+    for layer in layers:
+        win = windows[layer]
+        cu = W.out_offsets(lens, win)
+        n_out = int(cu[-1])
+        outs = [torch.empty((n_out, rb), dtype=torch.uint8, device="cuda") for _ in range(nkv)]
+        U.ukv_gather_kv(pool, sub, layer, bt_d, lens_d, _dev(cu), win, outs[0], outs[1] if nkv == 2 else None)
+        maps = orc.gather_map(sub, layer, bt, lens, cu, win, n_out)
+        assert maps[2] == frozenset()
+        for h in range(nkv):
+            r = torch.from_numpy(offsets_to_rows(maps[h], anchor, rb)).cuda()
+            assert equal_rows_chunked(rows, r, outs[h], None), f"layer {layer} kv {h}: gathered rows"
+        del outs
+
+
+def _masks(pool):
+    out = []
+    for sub in range(len(pool.specs)):
+        _, env, rb = _sub_geom(pool, sub)
+        out.append(torch.zeros(env // rb, dtype=torch.bool, device="cuda"))
+    return out
+
+
+def test_full_decode_8b_store_and_gather_all_layers():
+    """Llama-3-8B-shape pool (8 GiB), 256 new rows per layer, 256 requests gathered in full, 32 layers."""
+    w = W.decode_8b()
+    pool, orc = _make(w)
+    slots = w.store_slots[0]
+    ids_d, ids = _translate(pool, orc, 0, slots)
+    masks = _masks(pool)
+    _store_layers(pool, orc, 0, ids_d, ids, slots, masks, 500)
+    log("  stores checked")
+    _check_untouched(pool, masks)
+    log("  untouched bytes checked")
+    bt_d, bt = _block_table(pool, orc, 0, w.req_pages[0])
+    _gather_layers(pool, orc, 0, bt_d, bt, w.req_lens[0], w.windows[0], range(32))
+    log("  gathers checked (32 layers x 1,179,779 rows)")
+    assert U.ukv_pool_error_flags(pool) == frozenset()
+
+
+def test_full_prefill_8b_store_gather_move():
+    """32 GiB pool; 32,768 tokens (1% tombstones) stored on 32 layers, gathered back,
+    then 65,536 rows moved to disjoint rows on every layer."""
+    w = W.prefill_8b()
+    pool, orc = _make(w)
+    slots = w.store_slots[0]
+    ids_d, ids = _translate(pool, orc, 0, slots)
+    masks = _masks(pool)
+    _store_layers(pool, orc, 0, ids_d, ids, slots, masks, 900)
+    log("  stores checked")
+    _check_untouched(pool, masks)
+    log("  untouched bytes checked")
+    bt_d, bt = _block_table(pool, orc, 0, w.req_pages[0])
+    _gather_layers(pool, orc, 0, bt_d, bt, w.req_lens[0], w.windows[0], range(32))
+    log("  gathers checked")
+    src_d, src = _translate(pool, orc, 0, w.move_src[0])
+    dst_d, dst = _translate(pool, orc, 0, w.move_dst[0])
+    before = pool.raw.clone()
+    U.ukv_move_kv(pool, 0, dst_d, src_d)
+    d_off, s_off, fl = orc.move_map(0, dst, src, 0, 32)
+    assert fl == frozenset()
+    anchor, env, rb = _sub_geom(pool, 0)
+    d_rows = torch.from_numpy(offsets_to_rows(d_off, anchor, rb)).cuda()
+    s_rows = torch.from_numpy(offsets_to_rows(s_off, anchor, rb)).cuda()
+    rows_after = rows_view(pool.raw, anchor, env, rb)
+    rows_before = rows_view(before, anchor, env, rb)
+    assert equal_rows_chunked(rows_after, d_rows, rows_before, s_rows), "moved rows"
+    allowed = torch.zeros(env // rb, dtype=torch.bool, device="cuda")
+    allowed[d_rows] = True
+    for c0 in range(0, env // rb, 1 << 19):
+        c1 = min(env // rb, c0 + (1 << 19))
+        changed = (rows_after[c0:c1] != rows_before[c0:c1]).any(dim=1).nonzero().flatten() + c0
+        assert_rows_subset(changed, allowed, "move")
+    assert torch.equal(pool.raw[anchor + env:], before[anchor + env:])
+    del before
+    log("  move checked")
+    assert U.ukv_pool_error_flags(pool) == frozenset()
+
+
+def test_full_hybrid_mha_swa_and_mla():
+    """MHA (24 layers, 8x64, page 64, odd layers window 128) and MLA (24 layers, 576 latent)
+    sub-pools holding 128 requests of 256..16384 tokens; every token stored on every layer of
+    both sub-pools, every layer gathered back."""
+    w = W.hybrid()
+    pool, orc = _make(w)
+    masks = _masks(pool)
+    for sub in (0, 1):
+        slots = w.store_slots[sub]
+        ids_d, ids = _translate(pool, orc, sub, slots)
+        _store_layers(pool, orc, sub, ids_d, ids, slots, masks, 1300 + 100 * sub)
+        log(f"  sub-pool {sub} stores checked")
+    _check_untouched(pool, masks)
+    log("  untouched bytes checked")
+    for sub in (0, 1):
+        bt_d, bt = _block_table(pool, orc, sub, w.req_pages[sub])
+        _gather_layers(pool, orc, sub, bt_d, bt, w.req_lens[sub], w.windows[sub], range(24))
+        log(f"  sub-pool {sub} gathers checked")
+    assert U.ukv_pool_error_flags(pool) == frozenset()
+
+
+def test_full_move_70b():
+    """Llama-3-70B-shape pool, 32,768 pages (160 GiB): 65,536 rows moved to 65,536 disjoint rows
+    on all 80 layers, K and V, in one launch."""
+    w = W.move_70b()
+    pool, orc = _make(w)
+    src_d, src = _translate(pool, orc, 0, w.move_src[0])
+    dst_d, dst = _translate(pool, orc, 0, w.move_dst[0])
+    U.ukv_move_kv(pool, 0, dst_d, src_d)
+    d_off, s_off, fl = orc.move_map(0, dst, src, 0, 80)
+    assert fl == frozenset()
+    anchor, env, rb = _sub_geom(pool, 0)
+    rows = rows_view(pool.raw, anchor, env, rb)
+    d_rows = torch.from_numpy(offsets_to_rows(d_off, anchor, rb)).cuda()
+    s_rows = torch.from_numpy(offsets_to_rows(s_off, anchor, rb)).cuda()
+    # sources are disjoint from destinations, so they still hold their pre-fill bytes
+    assert equal_rows_chunked(rows, d_rows, rows, s_rows), "moved rows"
+    allowed = torch.zeros(env // rb, dtype=torch.bool, device="cuda")
+    allowed[d_rows] = True
+    changed = pattern_mismatch_rows(pool.raw, SEED, anchor, env, rb)
+    assert changed.numel() == d_rows.numel()
+    assert_rows_subset(changed, allowed, "move")
+    assert_bytes_are_pattern(pool.raw, SEED, anchor + env, pool.raw.numel())
+    assert U.ukv_pool_error_flags(pool) == frozenset()
+    log("  move checked (10,485,760 rows)")
+
+
+def test_full_bound_rejected_without_allocation():
+    """The 70B-shape spec whose kernel-facing rows would reach 2^31 is rejected by the host
+    plan; no device memory is touched (allocation stays where it was)."""
+    before = torch.cuda.memory_allocated()
+    assert U.plan_status([W.mha(80, 8, 128, 838861)], 16) == "UKV_ERR_KERNEL_ID_BOUND"
+    assert U.plan_status([W.mha(80, 8, 128, 838860)], 16) == "UKV_OK"
+    assert torch.cuda.memory_allocated() == before

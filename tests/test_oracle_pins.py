@@ -437,3 +437,47 @@ def test_layer_view_4d_agrees_with_dense_rows():
             kid = oracle.kernel_id(p * 2 + o, 2, 6)
             dense = raw[base + kid * 32: base + kid * 32 + 32].view(np.uint16).reshape(2, 8)
             assert np.array_equal(v4[p, o], dense)
+
+
+def test_address_maps_match_strided_reference_and_need_no_buffer():
+    """The store / gather / move address maps (used for pool-sized checks) give the
+    strided reference's row addresses, and an addresses-only pool gives the same."""
+    w = W.hybrid(num_reqs=4, len_lo=3, len_hi=200, layer_num=3, window=5)
+    pool, raw = _filled_pool(w.shapes, w.page_size)
+    bare = oracle.OraclePool(pool.specs, w.page_size, addresses_only=True)
+    for sub in (0, 1):
+        ref = _strided(pool, sub)
+        kvs = (0, 1) if sub == 0 else (0,)
+        slots = w.store_slots[sub]
+        ids, _ = pool.translate(sub, slots)
+        for layer in range(3):
+            maps = pool.store_map(sub, layer, ids)
+            assert all(np.array_equal(a, b) for a, b in zip(maps[:2], bare.store_map(sub, layer, ids)[:2]) if a is not None)
+            for kv in kvs:
+                exp = [ref.row_address(layer, kv, *divmod(int(t), w.page_size)) for t in slots]
+                assert maps[kv].tolist() == exp
+            lens = w.req_lens[sub]
+            bt, _ = pool.translate_pages(sub, W.padded_table(w.req_pages[sub]))
+            win = w.windows[sub][layer]
+            cu = W.out_offsets(lens, win)
+            gm = pool.gather_map(sub, layer, bt, lens, cu, win, int(cu[-1]))
+            assert gm[2] == frozenset()
+            exp_k = []
+            for pages, n in zip(w.req_pages[sub], lens):
+                j0 = n - win if 0 < win < n else 0
+                exp_k += [ref.row_address(layer, 0, int(pages[j // w.page_size]), j % w.page_size) for j in range(j0, n)]
+            assert gm[0].tolist() == exp_k
+            assert np.array_equal(gm[0], bare.gather_map(sub, layer, bt, lens, cu, win, int(cu[-1]))[0])
+        mv = W.live_slots(3, w.shapes[sub].num_pages, w.page_size, 10, sub=31)
+        src, _ = pool.translate(sub, mv[:5])
+        dst, _ = pool.translate(sub, mv[5:])
+        d_off, s_off, fl = pool.move_map(sub, dst, src, 1, 3)
+        assert fl == frozenset()
+        at = 0
+        for layer in (1, 2):
+            for kv in kvs:
+                for i in range(5):
+                    assert s_off[at] == ref.row_address(layer, kv, *divmod(int(mv[i]), w.page_size))
+                    assert d_off[at] == ref.row_address(layer, kv, *divmod(int(mv[5 + i]), w.page_size))
+                    at += 1
+        assert at == d_off.size
