@@ -1,19 +1,24 @@
 """Throughput of the unified page-major KV pool's hot path on one MI355X.
 
-A step is one pass of the whole path over one batch: translate the batch's
-token slots once, translate its block table once, then for every layer
-store the batch's new K/V rows and gather every request's K/V through the
-block table (plus, for the workloads that have one, the move).
+A step is one pass of the whole path over one batch of a workload: translate
+the batch's token slots and its block table once, then, layer by layer, the
+stores and gathers, then the move where the workload has one.  Every launch
+goes through the C ABI (libukv.so) on torch's current stream.
 
-Default workload (decode_8b): Llama-3-8B-shape pool, 32 layers x 8 KV heads
-x head dim 128, bf16, page size 16, 4,096 pages = 65,536 slots (8 GiB of
-envelopes); 256 requests with lengths uniform in [1024, 8192]; per layer
-store 256 new rows and gather every request in full.
+Default workload (decode_8b, the configuration the metric is quoted on):
+Llama-3-8B-shape pool, 32 layers x 8 KV heads x head dim 128, bf16, page
+size 16, 4,096 pages = 65,536 slots (8 GiB of envelopes); 256 requests with
+lengths uniform in [1024, 8192]; per layer store 256 new rows and gather every
+request in full.  `--workload` selects the others (prefill_8b, hybrid,
+move_70b, tiny); each prints its own JSON line.
 
-Prints one JSON line.  `value` is algorithmic GB/s (bytes the method must
-read and write, 1e9 B/s) over the whole step with inputs resident in HBM;
-`roofline` reports the dominant kernel (the gather) per launch, timed with
-HIP events around each launch on the stream it runs on.
+Output: one JSON line per workload.  `value` is algorithmic GB/s (bytes the
+method must read and write, 1e9 B/s) over the whole step with inputs resident
+in HBM.  `roofline` reports the dominant kernel per launch, from HIP events
+recorded around each of its launches inside the timed region, on the stream
+the kernels run on.  `ops` gives every launch kind's mean time from one extra
+step with events around all launches (outside the timed region).
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -24,6 +29,8 @@ import os
 import re
 import sys
 import time
+from dataclasses import dataclass, field
+from typing import Callable, Dict, List
 
 import numpy as np
 
@@ -32,8 +39,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+METRIC = "KV store/gather/move HBM GB/s and % of peak, Llama-3-8B-shape pool"
 KERNEL_SRC = os.path.join(ROOT, "store_gather_amd", "csrc", "ukv_runtime.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gather_decode_8b_counters.txt")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+WORKLOADS = ("decode_8b", "prefill_8b", "hybrid", "move_70b", "tiny")
 
 
 def log(msg):
@@ -42,7 +51,7 @@ def log(msg):
 
 def num(x, nd):
     """Rounded float, or None for a figure that was not measured."""
-    return None if x != x else round(x, nd)
+    return None if x is None or x != x else round(float(x), nd)
 
 
 def kernel_source_hash() -> str:
@@ -50,12 +59,13 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile():
-    """HBM bytes per gather launch from the committed counter summary, or None when
-    the summary is missing or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_from_profile(workload: str, kernel: str):
+    """HBM bytes per launch of the roofline kernel from the committed counter summary,
+    or None when there is none or it was taken on a different kernel source."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_counters.txt")
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
@@ -64,156 +74,281 @@ def traffic_from_profile():
 
 
 # ----------------------------------------------------------------------------
-# the decode_8b workload on the GPU
+# A workload's step as a script of operations, run on the GPU (libukv) or the CPU oracle
 # ----------------------------------------------------------------------------
 
-class DecodeStep:
-    def __init__(self, torch, U, W, device, seed=0):
-        self.torch = torch
+@dataclass
+class Op:
+    kind: str  # translate | translate_pages | store | gather | move
+    sub: int
+    label: str
+    args: dict
+    nbytes: int = 0  # algorithmic bytes (reads + writes the method must do)
+
+
+@dataclass
+class Script:
+    name: str
+    description: str
+    shapes: list
+    page_size: int
+    arrays: Dict[str, np.ndarray]  # host inputs: slots, tables, lens, cu_out
+    buffers: Dict[str, tuple]  # name -> (rows, row_bytes): store sources and gather outputs
+    ops: List[Op]
+    roofline: Callable[[Op], bool]
+    roofline_kernel: str
+    counts: dict = field(default_factory=dict)
+
+
+def _pages_read(pages_per_req, lens, window, ps):
+    n = 0
+    for pages, ln in zip(pages_per_req, lens):
+        ln = int(ln)
+        j0 = ln - window if 0 < window < ln else 0
+        if ln > j0:
+            n += (ln - 1) // ps - j0 // ps + 1
+    return n
+
+
+DESCRIPTIONS = {
+    "decode_8b": "decode_8b: Llama-3-8B-shape pool (32 layers, 8 KV heads x 128, bf16, page 16, 4096 pages = 65,536 "
+                 "slots, 8 GiB); 256 requests, lengths U[1024, 8192], pages shared cyclically from one seeded "
+                 "permutation; per step: translate 256 slots and the block table once, then per layer store 256 new "
+                 "K/V rows and gather every request in full",
+    "prefill_8b": "prefill_8b: Llama-3-8B-shape pool (16,384 pages = 262,144 slots, 32 GiB); 32,768 new tokens over "
+                  "16 requests (Dirichlet split, runs of whole pages, 1% tombstones); per step: translate, then per "
+                  "layer store all 32,768 tokens and gather the 16 requests back, then move 65,536 rows to disjoint "
+                  "rows on all 32 layers",
+    "hybrid": "hybrid: MHA sub-pool (24 layers, 8 KV heads x 64, bf16, page 64, odd layers sliding-window 128) and "
+              "MLA sub-pool (24 layers, 576-wide latent) holding 128 requests of U[256, 16384] tokens apart (16,538 "
+              "pages each, ~76 GiB); per step: translate both, then per layer store every token in both sub-pools "
+              "and gather every request (MHA full or its last 128, MLA full); one set of source rows serves every "
+              "layer",
+    "move_70b": "move_70b: Llama-3-70B-shape pool (80 layers, 8 KV heads x 128, bf16, page 16, 32,768 pages, "
+                "160 GiB); per step: translate 131,072 slots, move 65,536 rows to 65,536 disjoint rows on all 80 "
+                "layers, K and V, in one launch",
+    "tiny": "tiny: 2 layers, 2 KV heads x 8, bf16, page 4, 16 pages; store 37 entries (3 tombstones), gather 3 "
+            "requests of 5/11/21 tokens, move 8 rows",
+}
+
+
+def build_script(name: str, W, reduced: bool = False) -> Script:
+    """The step of workload `name`.  `reduced` shrinks the pools (same row and page geometry,
+    envelopes of at most ~8 GiB) for the CPU-oracle sample."""
+    if name == "decode_8b":
+        w = W.decode_8b()
+    elif name == "prefill_8b":
+        w = W.prefill_8b(num_pages=4096, move_rows=16384) if reduced else W.prefill_8b()
+    elif name == "hybrid":
+        w = W.hybrid(num_reqs=12) if reduced else W.hybrid()
+    elif name == "move_70b":
+        w = W.move_70b(num_pages=1600, rows=8192) if reduced else W.move_70b()
+    elif name == "tiny":
+        w = W.tiny_mha()
+    else:
+        raise ValueError(name)
+
+    ps = w.page_size
+    arrays: Dict[str, np.ndarray] = {}
+    buffers: Dict[str, tuple] = {}
+    ops: List[Op] = []
+    nsub = len(w.shapes)
+    rb = [s.row_bytes for s in w.shapes]
+    nkv = [2 if s.kind == W.MHA else 1 for s in w.shapes]
+    kind_name = ["mha" if k == 2 else "mla" for k in nkv]
+
+    # translation, once per batch
+    for sub in range(nsub):
+        if sub in w.store_slots:
+            arrays[f"slots{sub}"] = w.store_slots[sub].astype(np.int64)
+            n = arrays[f"slots{sub}"].size
+            ops.append(Op("translate", sub, f"translate sub{sub}", {"inp": f"slots{sub}", "out": f"ids{sub}"}, n * 12))
+        if sub in w.req_pages:
+            arrays[f"table{sub}"] = W.padded_table(w.req_pages[sub])
+            arrays[f"lens{sub}"] = w.req_lens[sub].astype(np.int32)
+            t = arrays[f"table{sub}"]
+            ops.append(Op("translate_pages", sub, f"translate_pages sub{sub}", {"inp": f"table{sub}", "out": f"bt{sub}"},
+                          t.size * 8))
+        if sub in w.move_src:
+            arrays[f"msrc{sub}"] = w.move_src[sub].astype(np.int64)
+            arrays[f"mdst{sub}"] = w.move_dst[sub].astype(np.int64)
+            m = arrays[f"msrc{sub}"].size
+            ops.append(Op("translate", sub, f"translate move src sub{sub}", {"inp": f"msrc{sub}", "out": f"msrcid{sub}"},
+                          m * 12))
+            ops.append(Op("translate", sub, f"translate move dst sub{sub}", {"inp": f"mdst{sub}", "out": f"mdstid{sub}"},
+                          m * 12))
+
+    # sources and outputs
+    per_layer_sources = name in ("decode_8b", "prefill_8b", "tiny")
+    for sub in range(nsub):
+        if sub in w.store_slots:
+            n = arrays[f"slots{sub}"].size
+            L = w.shapes[sub].layer_num if per_layer_sources else 1
+            for h in range(nkv[sub]):
+                buffers[f"src{sub}_{h}"] = (L * n, rb[sub])
+        if sub in w.req_pages:
+            wins = sorted(set(w.windows[sub]))
+            for win in wins:
+                arrays[f"cu{sub}_{win}"] = W.out_offsets(arrays[f"lens{sub}"], win)
+            rows = max(int(arrays[f"cu{sub}_{win}"][-1]) for win in wins)
+            for h in range(nkv[sub]):
+                buffers[f"out{sub}_{h}"] = (rows, rb[sub])
+
+    # per layer: stores, then gathers
+    layer_num = max(s.layer_num for s in w.shapes)
+    for layer in range(layer_num):
+        for sub in range(nsub):
+            if layer >= w.shapes[sub].layer_num or sub not in w.store_slots:
+                continue
+            n = arrays[f"slots{sub}"].size
+            row0 = layer * n if per_layer_sources else 0
+            ops.append(Op("store", sub, f"store {kind_name[sub]} sub{sub}",
+                          {"layer": layer, "ids": f"ids{sub}", "row0": row0, "n": n},
+                          n * (2 * nkv[sub] * rb[sub] + 4)))
+        for sub in range(nsub):
+            if layer >= w.shapes[sub].layer_num or sub not in w.req_pages:
+                continue
+            win = w.windows[sub][layer]
+            cu = arrays[f"cu{sub}_{win}"]
+            rows = int(cu[-1])
+            R = arrays[f"lens{sub}"].size
+            pr = _pages_read(w.req_pages[sub], arrays[f"lens{sub}"], win, ps)
+            ops.append(Op("gather", sub, f"gather {kind_name[sub]}{' swa' if win else ''} sub{sub}",
+                          {"layer": layer, "window": win, "cu": f"cu{sub}_{win}", "rows": rows},
+                          rows * 2 * nkv[sub] * rb[sub] + pr * 4 + R * 12 + 8))
+    # the move, over every layer in one launch
+    for sub in range(nsub):
+        if sub in w.move_src:
+            m = arrays[f"msrc{sub}"].size
+            L = w.shapes[sub].layer_num
+            ops.append(Op("move", sub, f"move sub{sub}", {"l0": 0, "l1": L}, m * L * 2 * nkv[sub] * rb[sub] + m * 8))
+
+    roof = {
+        "decode_8b": (lambda op: op.kind == "gather", "gather"),
+        "prefill_8b": (lambda op: op.kind == "move", "move"),
+        "hybrid": (lambda op: op.label.startswith("store mha"), "store"),
+        "move_70b": (lambda op: op.kind == "move", "move"),
+        "tiny": (lambda op: op.kind == "gather", "gather"),
+    }[name]
+    counts = {"layers": layer_num}
+    for sub in range(nsub):
+        if sub in w.store_slots:
+            counts[f"stored_rows_per_layer_sub{sub}"] = int(arrays[f"slots{sub}"].size)
+        if sub in w.req_lens:
+            counts[f"requests_sub{sub}"] = int(arrays[f"lens{sub}"].size)
+            counts[f"gathered_rows_per_full_layer_sub{sub}"] = int(arrays[f"lens{sub}"].astype(np.int64).sum())
+        if sub in w.move_src:
+            counts[f"moved_rows_sub{sub}"] = int(arrays[f"msrc{sub}"].size)
+    return Script(name, DESCRIPTIONS[name], list(w.shapes), ps, arrays, buffers, ops, roof[0], roof[1], counts)
+
+
+_OUT_OF = {"slots": "ids", "msrc": "msrcid", "mdst": "mdstid", "table": "bt"}
+
+
+class GpuRunner:
+    """Runs a script through libukv on the current device and stream."""
+
+    def __init__(self, script: Script, torch, U, W, device, fill: bool = True):
+        self.s = script
         self.U = U
-        w = W.decode_8b(seed=seed)
-        self.w = w
-        shape = w.shapes[0]
-        self.L = shape.layer_num
-        self.ps = w.page_size
-        plan = U.ukv_pool_plan(w.shapes, self.ps)
+        plan = U.ukv_pool_plan(script.shapes, script.page_size)
         n = (int(plan.required_bytes) + 7) // 8 * 8
-        t0 = time.time()
-        self.pool = U.allocate_pool(w.shapes, self.ps, device=device, extra_bytes=n - int(plan.required_bytes))
-        W.fill_pattern_device(self.pool.raw, 1)
-        self.rb = self.pool.row_bytes(0)
-        slots = w.store_slots[0]
-        self.n_new = slots.size
-        self.slots = torch.from_numpy(slots).to(device)
-        table = W.padded_table(w.req_pages[0])
-        self.table = torch.from_numpy(table).to(device)
-        self.lens_np = w.req_lens[0].astype(np.int32)
-        self.lens = torch.from_numpy(self.lens_np).to(device)
-        cu = W.out_offsets(self.lens_np)
-        self.cu = torch.from_numpy(cu).to(device)
-        self.out_rows = int(cu[-1])
-        self.pages_read = int(sum(len(p) for p in w.req_pages[0]))
-        H, D = shape.head_num, shape.head_dim
-        # new K / V rows of every layer: bf16 N(0,1), drawn on the device
-        self.k_new = W.normal_bf16_device((self.L, self.n_new, H, D), seed + 101, device)
-        self.v_new = W.normal_bf16_device((self.L, self.n_new, H, D), seed + 202, device)
-        self.k_out = torch.empty((self.out_rows, H, D), dtype=torch.bfloat16, device=device)
-        self.v_out = torch.empty_like(self.k_out)
-        self.ids = torch.empty(self.n_new, dtype=torch.int32, device=device)
-        self.bt = torch.empty_like(self.table)
+        self.pool = U.allocate_pool(script.shapes, script.page_size, device=device,
+                                    extra_bytes=n - int(plan.required_bytes))
+        if fill:
+            W.fill_pattern_device(self.pool.raw, 1)
+        self.t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device) for k, v in script.arrays.items()}
+        for k, v in script.arrays.items():
+            stem = re.match(r"[a-z]+", k).group(0)
+            if stem in _OUT_OF:
+                self.t[_OUT_OF[stem] + k[len(stem):]] = torch.empty(v.shape, dtype=torch.int32, device=device)
+        for i, (k, (rows, rb)) in enumerate(script.buffers.items()):
+            if k.startswith("src"):
+                self.t[k] = W.normal_bf16_device((rows, rb // 2), 100 + i, device).view(torch.uint8)
+            else:
+                self.t[k] = torch.empty((rows, rb), dtype=torch.uint8, device=device)
         torch.cuda.synchronize()
-        log(f"[bench] decode_8b setup {time.time() - t0:.1f}s: pool {plan.required_bytes / 2**30:.2f} GiB, "
-            f"{len(self.lens_np)} requests, {self.out_rows} gathered rows per layer, {self.n_new} new rows")
+        self.required = int(plan.required_bytes)
 
-    # algorithmic bytes (reads + writes the method must do)
-    def bytes_translate(self):
-        return self.n_new * (8 + 4) + self.table.numel() * (4 + 4)
-
-    def bytes_store_launch(self):
-        return self.n_new * (4 * self.rb + 4)
-
-    def bytes_gather_launch(self):
-        R = len(self.lens_np)
-        return self.out_rows * 4 * self.rb + self.pages_read * 4 + R * 4 + (R + 1) * 8
-
-    def bytes_step(self):
-        return self.bytes_translate() + self.L * (self.bytes_store_launch() + self.bytes_gather_launch())
-
-    def run(self, timers=None):
-        """One step; ``timers`` (optional) is an iterator of (store, gather) event pairs,
-        recorded around every launch on the stream the kernels run on."""
-        U = self.U
-        U.ukv_translate_loc_for_kernel(self.pool, 0, self.slots, out=self.ids)
-        U.ukv_translate_pages_for_kernel(self.pool, 0, self.table, out=self.bt)
-        for l in range(self.L):
-            ev = next(timers) if timers is not None else None
-            if ev and ev[0]:
-                ev[0][0].record()
-            U.ukv_store_kv(self.pool, 0, l, self.ids, self.k_new[l], self.v_new[l])
-            if ev and ev[0]:
-                ev[0][1].record()
-            if ev and ev[1]:
-                ev[1][0].record()
-            U.ukv_gather_kv(self.pool, 0, l, self.bt, self.lens, self.cu, 0, self.k_out, self.v_out)
-            if ev and ev[1]:
-                ev[1][1].record()
+    def launch(self, op: Op) -> None:
+        U, t, a, sub = self.U, self.t, op.args, op.sub
+        nkv = 2 if self.s.shapes[sub].kind == 0 else 1
+        if op.kind == "translate":
+            U.ukv_translate_loc_for_kernel(self.pool, sub, t[a["inp"]], out=t[a["out"]])
+        elif op.kind == "translate_pages":
+            U.ukv_translate_pages_for_kernel(self.pool, sub, t[a["inp"]], out=t[a["out"]])
+        elif op.kind == "store":
+            r0, n = a["row0"], a["n"]
+            k = t[f"src{sub}_0"][r0: r0 + n]
+            v = t[f"src{sub}_1"][r0: r0 + n] if nkv == 2 else None
+            U.ukv_store_kv(self.pool, sub, a["layer"], t[a["ids"]], k, v)
+        elif op.kind == "gather":
+            rows = a["rows"]
+            ko = t[f"out{sub}_0"][:rows]
+            vo = t[f"out{sub}_1"][:rows] if nkv == 2 else None
+            U.ukv_gather_kv(self.pool, sub, a["layer"], t[f"bt{sub}"], t[f"lens{sub}"], t[a["cu"]], a["window"], ko, vo)
+        elif op.kind == "move":
+            U.ukv_move_kv(self.pool, sub, t[f"mdstid{sub}"], t[f"msrcid{sub}"], a["l0"], a["l1"])
+        else:
+            raise ValueError(op.kind)
 
 
-def cpu_baseline(W, budget_s=12.0, seed=0):
-    """The CPU oracle, as written, on a bounded sample of the same workload: translate
-    the batch and the block table, then store + gather layer by layer until the
-    time budget is spent.  Same pool geometry (8 GiB host envelope)."""
+def cpu_baseline(name: str, W, budget_s: float = 12.0) -> dict:
+    """The CPU oracle, as written (single-threaded C), on a bounded sample of the same
+    workload: the step's operations in order until the time budget is spent, on a host
+    envelope of the same row and page geometry (at most ~8 GiB)."""
     import oracle
 
-    w = W.decode_8b(seed=seed)
-    shape = w.shapes[0]
-    ps = w.page_size
-    spec = oracle.Spec(shape.kind, shape.layer_num, shape.head_num, shape.head_dim, shape.v_head_dim,
-                       shape.elem_bytes, shape.num_pages)
-    req = oracle.plan([spec], ps).required_bytes
-    raw = np.full(req, 0x5A, dtype=np.uint8)  # touched, so the timing sees no first-touch faults
-    pool = oracle.OraclePool([spec], ps, raw)
-    rb = pool.row_bytes(0)
-    slots = w.store_slots[0]
-    table = W.padded_table(w.req_pages[0])
-    lens = w.req_lens[0]
-    cu = W.out_offsets(lens)
-    rows = int(cu[-1])
-    k_out = np.full((rows, rb), 1, np.uint8)
-    v_out = np.full((rows, rb), 2, np.uint8)
-    k_new = np.full((slots.size, rb), 3, np.uint8)
-    v_new = np.full((slots.size, rb), 4, np.uint8)
-    pages_read = int(sum(len(p) for p in w.req_pages[0]))
+    s = build_script(name, W, reduced=True)
+    specs = [oracle.Spec(x.kind, x.layer_num, x.head_num, x.head_dim, x.v_head_dim, x.elem_bytes, x.num_pages)
+             for x in s.shapes]
+    req = oracle.plan(specs, s.page_size).required_bytes
+    pool = oracle.OraclePool(specs, s.page_size, np.full(req, 0x5A, dtype=np.uint8))  # pages touched up front
+    h = dict(s.arrays)
+    bufs = {k: np.full((rows, rb), 7, dtype=np.uint8) for k, (rows, rb) in s.buffers.items()}
+    done_bytes = 0
+    done_ops = 0
     t0 = time.perf_counter()
-    ids, _ = pool.translate(0, slots)
-    bt, _ = pool.translate_pages(0, table)
-    nbytes = slots.size * 12 + table.size * 8
-    layers = 0
-    while layers < shape.layer_num:
-        pool.store(0, layers, ids, k_new, v_new)
-        pool.gather(0, layers, bt, lens, cu, 0, k_out, v_out)
-        nbytes += slots.size * (4 * rb + 4) + rows * 4 * rb + pages_read * 4 + len(lens) * 12 + 8
-        layers += 1
-        if time.perf_counter() - t0 > budget_s:
+    for op in s.ops:
+        a, sub = op.args, op.sub
+        nkv = 2 if s.shapes[sub].kind == 0 else 1
+        if op.kind == "translate":
+            h[a["out"]], _ = pool.translate(sub, h[a["inp"]])
+        elif op.kind == "translate_pages":
+            h[a["out"]], _ = pool.translate_pages(sub, h[a["inp"]])
+        elif op.kind == "store":
+            r0, n = a["row0"], a["n"]
+            pool.store(sub, a["layer"], h[a["ids"]], bufs[f"src{sub}_0"][r0: r0 + n],
+                       bufs[f"src{sub}_1"][r0: r0 + n] if nkv == 2 else None)
+        elif op.kind == "gather":
+            rows = a["rows"]
+            pool.gather(sub, a["layer"], h[f"bt{sub}"], h[f"lens{sub}"], h[a["cu"]], a["window"],
+                        bufs[f"out{sub}_0"][:rows], bufs[f"out{sub}_1"][:rows] if nkv == 2 else None)
+        elif op.kind == "move":
+            pool.move(sub, h[f"mdstid{sub}"], h[f"msrcid{sub}"], a["l0"], a["l1"])
+        done_bytes += op.nbytes
+        done_ops += 1
+        if time.perf_counter() - t0 > budget_s and op.kind not in ("translate", "translate_pages"):
             break
     dt = time.perf_counter() - t0
+    envelope = sum(p.envelope_bytes for p in pool.plan.subs)
+    shrunk = " (same row and page geometry, fewer pages)" if name in ("prefill_8b", "hybrid", "move_70b") else ""
     return {
-        "value": round(nbytes / dt / 1e9, 3),
+        "value": round(done_bytes / dt / 1e9, 3),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"decode_8b: translate + {layers} of {shape.layer_num} layers of (store 256 rows + gather "
-                  f"{rows} rows) on an 8 GiB host envelope, single-threaded C oracle, {dt:.1f} s",
+        "sample": f"{name}: the first {done_ops} of {len(s.ops)} operations of one step ({done_bytes / 1e9:.2f} GB) "
+                  f"in {dt:.1f} s, single-threaded C oracle, host envelope {envelope / 2**30:.2f} GiB{shrunk}",
     }
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--launch-events", choices=("gather", "all", "none"), default="gather",
-                    help="HIP events recorded around launches inside the timed region: around every "
-                         "gather (default), around gathers and stores, or none")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (3 times), the reference kernel for "
-                         "scaling hardware byte counters")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this path has no cross-GPU exchange (each GPU holds its own pool); "
-              "run it with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    import store_gather_amd as U
-    import ukv_workloads as W
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    device = torch.device("cuda:0")
-    torch.cuda.set_device(device)
-    step = DecodeStep(torch, U, W, device)
+def run_workload(name, args, torch, U, W, device) -> dict:
+    script = build_script(name, W)
+    t0 = time.time()
+    g = GpuRunner(script, torch, U, W, device)
+    log(f"[bench] {name}: setup {time.time() - t0:.1f}s, pool {g.required / 2**30:.2f} GiB, "
+        f"{len(script.ops)} launches per step")
     if args.copy_calibration:
         src = torch.full((1 << 30,), 7, dtype=torch.uint8, device=device)
         dst = torch.empty_like(src)
@@ -224,42 +359,75 @@ def main():
         del src, dst
 
     for _ in range(args.warmup):
-        step.run()
+        for op in script.ops:
+            g.launch(op)
     torch.cuda.synchronize()
-    flags = U.ukv_pool_error_flags(step.pool)
+    flags = U.ukv_pool_error_flags(g.pool)
     assert flags == frozenset(), f"device flags raised: {flags}"
 
-    n_ev = args.steps * step.L
     mk = lambda: torch.cuda.Event(enable_timing=True)
-    ev_store = [(mk(), mk()) if args.launch_events == "all" else None for _ in range(n_ev)]
-    ev_gather = [(mk(), mk()) if args.launch_events != "none" else None for _ in range(n_ev)]
+    use_ev = args.launch_events == "roofline"
+    timed = [(op, mk(), mk()) for _ in range(args.steps) for op in script.ops if use_ev and script.roofline(op)]
+    it = iter(timed)
     start, end = mk(), mk()
     torch.cuda.synchronize()
     start.record()
-    timers = iter(list(zip(ev_store, ev_gather)))
     for _ in range(args.steps):
-        step.run(timers)
+        for op in script.ops:
+            if use_ev and script.roofline(op):
+                _, e0, e1 = next(it)
+                e0.record()
+                g.launch(op)
+                e1.record()
+            else:
+                g.launch(op)
     end.record()
     torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
-    g_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_gather])) if ev_gather[0] else float("nan")
-    s_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_store])) if ev_store[0] else float("nan")
-    flags = U.ukv_pool_error_flags(step.pool)
+    ms_step = start.elapsed_time(end) / args.steps
+    flags = U.ukv_pool_error_flags(g.pool)
     assert flags == frozenset(), f"device flags raised: {flags}"
 
-    value = step.bytes_step() / (ms_step * 1e-3) / 1e9
-    g_gbps = step.bytes_gather_launch() / (g_ms * 1e-3) / 1e9
-    s_gbps = step.bytes_store_launch() / (s_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile()
+    step_bytes = sum(op.nbytes for op in script.ops)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    roof_ms = roof_bytes = achieved = None
+    if timed:
+        roof_ms = float(np.mean([e0.elapsed_time(e1) for _, e0, e1 in timed]))
+        roof_bytes = float(np.mean([op.nbytes for op, _, _ in timed]))
+        achieved = roof_bytes / (roof_ms * 1e-3) / 1e9
+
+    # one more step with events around every launch: per-kind launch times (outside the timed region)
+    per = [(op, mk(), mk()) for op in script.ops]
+    torch.cuda.synchronize()
+    for op, e0, e1 in per:
+        e0.record()
+        g.launch(op)
+        e1.record()
+    torch.cuda.synchronize()
+    agg: Dict[str, dict] = {}
+    for op, e0, e1 in per:
+        key = op.label.split(" sub")[0]
+        d = agg.setdefault(key, {"launches": 0, "ms": 0.0, "bytes": 0})
+        d["launches"] += 1
+        d["ms"] += e0.elapsed_time(e1)
+        d["bytes"] += op.nbytes
+    ops_out = {}
+    for k, d in agg.items():
+        gbps = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+        ops_out[k] = {"launches": d["launches"], "ms_per_launch": num(d["ms"] / d["launches"], 5),
+                      "bytes_per_launch": int(d["bytes"] // d["launches"]), "GBps": num(gbps, 1),
+                      "pct_of_peak": num(100 * gbps / PEAK_GBPS, 2)}
+    flags = U.ukv_pool_error_flags(g.pool)
+    assert flags == frozenset(), f"device flags raised: {flags}"
+    del g
+    torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(W)
+        log(f"[bench] {name}: timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(name, W)
 
-    out = {
-        "metric": "KV store/gather/move HBM GB/s and % of peak, Llama-3-8B-shape pool",
+    return {
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -271,40 +439,58 @@ def main():
         "vs_baseline": None,
         "dtype": "u8",
         "data": "synthetic",
-        "config": {
-            "workload": "decode_8b: Llama-3-8B-shape pool (32 layers, 8 KV heads x 128, bf16, page 16, "
-                        "4096 pages = 65,536 slots, 8 GiB); 256 requests, lengths U[1024, 8192], pages shared "
-                        "cyclically from one seeded permutation; per step: translate 256 slots and the block "
-                        "table once, then per layer store 256 new K/V rows and gather every request in full",
-            "kv_dtype": "bf16",
-            "global_batch": len(step.lens_np),
-            "gathered_rows_per_layer": step.out_rows,
-            "new_rows_per_layer": step.n_new,
-            "layers": step.L,
-            "parallelism": "single GPU",
-        },
+        "config": dict({"workload": script.description, "kv_dtype": "bf16", "parallelism": "single GPU",
+                        "step_bytes": step_bytes, "launches_per_step": len(script.ops)}, **script.counts),
         "pct_of_peak": round(100.0 * value / PEAK_GBPS, 2),
-        "tokens_per_s": {
-            "gathered": round(step.out_rows * step.L / (ms_step * 1e-3), 1),
-            "stored": round(step.n_new * step.L / (ms_step * 1e-3), 1),
-        },
-        "per_launch": {
-            "gather_ms": num(g_ms, 4), "gather_GBps": num(g_gbps, 1),
-            "store_ms": num(s_ms, 5), "store_GBps": num(s_gbps, 1),
-        },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gather_kernel",
-            "achieved": num(g_gbps, 1),
+            "kernel": f"{script.roofline_kernel}_kernel",
+            "achieved": num(achieved, 1),
             "peak": PEAK_GBPS,
             "unit": "GB/s",
-            "frac": num(g_gbps / PEAK_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": step.bytes_gather_launch(),
+            "frac": num(achieved / PEAK_GBPS if achieved else None, 4),
+            "traffic": traffic_from_profile(name, script.roofline_kernel),
+            "algorithmic_bytes_per_launch": int(roof_bytes) if roof_bytes else None,
+            "ms_per_launch": num(roof_ms, 5),
         },
+        "ops": ops_out,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(out), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode_8b", help=f"one of {WORKLOADS}, a comma list, or 'all'")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch-events", choices=("roofline", "none"), default="roofline",
+                    help="HIP events recorded inside the timed region around every launch of the roofline "
+                         "kernel (default), or none")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (3 times), the reference kernel for scaling "
+                         "hardware byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no cross-GPU exchange (each GPU holds its own pool); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    names = WORKLOADS if args.workload == "all" else tuple(args.workload.split(","))
+    for n in names:
+        if n not in WORKLOADS:
+            ap.error(f"unknown workload {n}")
+
+    import torch
+
+    import store_gather_amd as U
+    import ukv_workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    for n in names:
+        print(json.dumps(run_workload(n, args, torch, U, W, device)), flush=True)
 
 
 if __name__ == "__main__":

@@ -64,9 +64,6 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int64_t kMaxGrid = 0x7fffffff;
-// Output rows per gather wave (64 KiB of K+V at 2 KiB rows); measured
-// against 4, 8 and 32 on the decode-shape gather.
-constexpr int kGatherRowsPerWave = 16;
 
 // The wave's index inside the block, made uniform so that everything derived
 // from it is computed in scalar registers.
@@ -201,6 +198,16 @@ __global__ __launch_bounds__(kBlock) void translate_pages_kernel(TranslateArgs a
 // ----------------------------------------------------------------------------
 // store (DKV 关键文件: _store_kv_layer, a plain 3-D row assignment)
 // ----------------------------------------------------------------------------
+// Store and gather move rows in tiles.  A tile is `tile_rows` rows whose
+// 16-byte chunks are spread over the wave: lane k first resolves row k of
+// the tile (its id or block-table entry), the row numbers are broadcast with
+// ds_bpermute (__shfl), then every lane copies up to TPL chunks of K and V of
+// the tile, loads first, then stores (several rounds when the tile holds more
+// than 64 * TPL chunks).  The host sizes tiles by loads in flight per lane
+// (tiling_for), so every row size keeps about the same bytes in flight per
+// wave: e.g. 2 rows of 2 KiB K+V per gather tile, 5 MLA latents of 1,152 B.
+constexpr int kTasksPerLane = 4;
+
 struct StoreArgs {
     uint8_t *pool;
     uint64_t base[2];  // byte offsets of the K and V views of the layer
@@ -212,29 +219,66 @@ struct StoreArgs {
     uint32_t page_stride;
     uint32_t ps;
     uint32_t row_bytes;
-    int32_t vecs;  // row_bytes / sizeof(V)
+    int32_t vecs;          // row_bytes / sizeof(V)
+    int32_t tile_rows;     // rows per tile, <= 64
+    int32_t tiles_per_wave;
     uint32_t *flags;
 };
 
-// One wave per token: K_view[ids[i]] = k[i], V_view[ids[i]] = v[i].
-template <typename V, int NKV>
+// K_view[ids[i]] = k[i], V_view[ids[i]] = v[i]; waves own runs of tiles.
+template <typename V, int NKV, int TPL = kTasksPerLane>
 __global__ __launch_bounds__(kBlock) void store_kernel(StoreArgs a) {
-    const int64_t i = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
-    if (i >= a.n) return;
     const int lane = lane_id();
-    const int32_t id = a.ids[i];
-    if (!kernel_facing(id, a.n_rows, a.page_stride, a.ps)) {
-        if (lane == 0) atomicOr(a.flags, UKV_FLAG_BAD_ID);
-        return;
-    }
-    V *dst[NKV];
-    const V *src[NKV];
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int64_t per_wave = (int64_t)a.tile_rows * a.tiles_per_wave;
+    const int64_t i_begin = wave * per_wave;
+    if (i_begin >= a.n) return;
+    const int64_t i_end = i_begin + per_wave < a.n ? i_begin + per_wave : a.n;
+    const int tasks = a.tile_rows * a.vecs;
+    bool bad = false;
+    for (int64_t i0 = i_begin; i0 < i_end; i0 += a.tile_rows) {
+        // lane k: the destination row of entry i0 + k (-1: skipped)
+        int32_t id = -1;
+        if (lane < a.tile_rows && i0 + lane < i_end) {
+            const int32_t v = a.ids[i0 + lane];
+            if (kernel_facing(v, a.n_rows, a.page_stride, a.ps))
+                id = v;
+            else
+                bad = true;
+        }
+        for (int base = 0; base < tasks; base += kWave * TPL) {
+            V buf[NKV][TPL];
+            int32_t rows[TPL];
+            int32_t ks[TPL];
+            int32_t cs[TPL];
 #pragma unroll
-    for (int h = 0; h < NKV; ++h) {
-        dst[h] = reinterpret_cast<V *>(a.pool + a.base[h] + (uint64_t)(uint32_t)id * a.row_bytes);
-        src[h] = reinterpret_cast<const V *>(a.src[h] + i * a.src_stride);
+            for (int j = 0; j < TPL; ++j) {
+                const int t = base + lane + j * kWave;
+                const int k = t / a.vecs;
+                const int c = t - k * a.vecs;
+                const int32_t row = __shfl(id, k < kWave ? k : 0);
+                rows[j] = (t < tasks) ? row : -1;
+                ks[j] = k;
+                cs[j] = c;
+                if (rows[j] >= 0) {
+#pragma unroll
+                    for (int h = 0; h < NKV; ++h)
+                        buf[h][j] = reinterpret_cast<const V *>(a.src[h] + (i0 + k) * a.src_stride)[c];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < TPL; ++j) {
+                if (rows[j] >= 0) {
+#pragma unroll
+                    for (int h = 0; h < NKV; ++h)
+                        reinterpret_cast<V *>(a.pool + a.base[h] + (uint64_t)(uint32_t)rows[j] * a.row_bytes)[cs[j]] =
+                            buf[h][j];
+                }
+            }
+            (void)ks;
+        }
     }
-    copy_rows<V, NKV, 2, false>(dst, src, a.vecs, lane);
+    if (bad) atomicOr(a.flags, UKV_FLAG_BAD_ID);
 }
 
 // ----------------------------------------------------------------------------
@@ -256,70 +300,110 @@ struct GatherArgs {
     uint32_t num_pages;
     uint32_t row_bytes;
     int32_t vecs;
-    int32_t rows_per_wave;
+    int32_t tile_rows;
+    int32_t tiles_per_wave;
     uint32_t *flags;
 };
 
-// One wave per run of `rows_per_wave` consecutive output rows.  The request
-// of the first row is found by binary search over cu_out; later rows advance
-// it.  Row o of request r holds position j = j0 + (o - cu_out[r]) and reads
-// dense row bt[r][j / ps] * ps + j % ps.
-template <typename V, int NKV>
+// Source row of output row o (in request r, found by the caller), or -1 with
+// the reason added to `bad`.  Row o of request r holds position
+// j = j0 + (o - cu_out[r]) and reads dense row bt[r][j / ps] * ps + j % ps.
+__device__ __forceinline__ int32_t gather_source_row(const GatherArgs &a, int64_t o, int32_t r, uint32_t &bad) {
+    if (r >= a.num_reqs || o < a.cu_out[r]) {
+        bad |= UKV_FLAG_LAYOUT;
+        return -1;
+    }
+    const int64_t len = a.seq_lens[r];
+    const int64_t j0 = (a.window > 0 && len > a.window) ? len - a.window : 0;
+    const int64_t q = o - a.cu_out[r];
+    if (q >= len - j0) {
+        bad |= UKV_FLAG_LAYOUT;
+        return -1;
+    }
+    const uint32_t j = (uint32_t)(j0 + q);  // < seq_lens[r] <= INT32_MAX
+    const uint32_t page_idx = j / a.ps;
+    if ((int64_t)page_idx >= a.bt_stride) {
+        bad |= UKV_FLAG_BAD_BLOCK;
+        return -1;
+    }
+    const int32_t kp = a.bt[(int64_t)r * a.bt_stride + page_idx];
+    if (kp < 0 || (uint32_t)kp % a.bpp != 0 || (uint32_t)kp / a.bpp >= a.num_pages) {
+        bad |= UKV_FLAG_BAD_BLOCK;
+        return -1;
+    }
+    return (int32_t)((uint32_t)kp * a.ps + (j - page_idx * a.ps));  // < n_rows < 2^31
+}
+
+// A wave owns a run of output rows.  The request of its first row is found
+// by binary search over cu_out (scalar); each tile's lanes advance from there
+// to their own row's request.
+template <typename V, int NKV, int TPL = kTasksPerLane>
 __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
     const int lane = lane_id();
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (a.cu_out[0] != 0 || a.cu_out[a.num_reqs] != a.out_rows) atomicOr(a.flags, UKV_FLAG_LAYOUT);
     }
-    const int64_t o0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave_in_block()) * a.rows_per_wave;
-    if (o0 >= a.out_rows) return;
-    const int64_t o1 = o0 + a.rows_per_wave < a.out_rows ? o0 + a.rows_per_wave : a.out_rows;
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int64_t per_wave = (int64_t)a.tile_rows * a.tiles_per_wave;
+    const int64_t o_begin = wave * per_wave;
+    if (o_begin >= a.out_rows) return;
+    const int64_t o_end = o_begin + per_wave < a.out_rows ? o_begin + per_wave : a.out_rows;
 
-    // r = number of requests r' >= 1 with cu_out[r'] <= o0 (upper bound).
+    // r = number of requests r' >= 1 with cu_out[r'] <= o_begin (upper bound)
     int32_t lo = 0, hi = a.num_reqs;
     while (lo < hi) {
         const int32_t mid = (lo + hi) >> 1;
-        if (a.cu_out[mid + 1] <= o0)
+        if (a.cu_out[mid + 1] <= o_begin)
             lo = mid + 1;
         else
             hi = mid;
     }
     int32_t r = lo;
     uint32_t bad = 0;
-    for (int64_t o = o0; o < o1; ++o) {
-        while (r < a.num_reqs && a.cu_out[r + 1] <= o) ++r;
-        if (r >= a.num_reqs || o < a.cu_out[r]) {
-            bad |= UKV_FLAG_LAYOUT;
-            continue;
+    const int tasks = a.tile_rows * a.vecs;
+    for (int64_t o0 = o_begin; o0 < o_end; o0 += a.tile_rows) {
+        // lane k: the source row of output row o0 + k (-1: skipped)
+        int32_t src_row = -1;
+        int32_t rk = r;
+        const int64_t o = o0 + lane;
+        if (lane < a.tile_rows && o < o_end) {
+            while (rk < a.num_reqs && a.cu_out[rk + 1] <= o) ++rk;
+            src_row = gather_source_row(a, o, rk, bad);
         }
-        const int64_t len = a.seq_lens[r];
-        const int64_t j0 = (a.window > 0 && len > a.window) ? len - a.window : 0;
-        const int64_t q = o - a.cu_out[r];
-        if (q >= len - j0) {
-            bad |= UKV_FLAG_LAYOUT;
-            continue;
-        }
-        const uint32_t j = (uint32_t)(j0 + q);  // < seq_lens[r] <= INT32_MAX
-        const uint32_t page_idx = j / a.ps;
-        if ((int64_t)page_idx >= a.bt_stride) {
-            bad |= UKV_FLAG_BAD_BLOCK;
-            continue;
-        }
-        const int32_t kp = a.bt[(int64_t)r * a.bt_stride + page_idx];
-        if (kp < 0 || (uint32_t)kp % a.bpp != 0 || (uint32_t)kp / a.bpp >= a.num_pages) {
-            bad |= UKV_FLAG_BAD_BLOCK;
-            continue;
-        }
-        const uint64_t row = (uint64_t)(uint32_t)kp * a.ps + (j - page_idx * a.ps);
-        V *dst[NKV];
-        const V *src[NKV];
+        r = __builtin_amdgcn_readlane(rk, a.tile_rows - 1);  // rows grow with the lane: the tile's last request
+        for (int base = 0; base < tasks; base += kWave * TPL) {
+            V buf[NKV][TPL];
+            int32_t rows[TPL];
+            int32_t ks[TPL];
+            int32_t cs[TPL];
 #pragma unroll
-        for (int h = 0; h < NKV; ++h) {
-            src[h] = reinterpret_cast<const V *>(a.pool + a.base[h] + row * a.row_bytes);
-            dst[h] = reinterpret_cast<V *>(a.out[h] + (uint64_t)o * a.row_bytes);
+            for (int j = 0; j < TPL; ++j) {
+                const int t = base + lane + j * kWave;
+                const int k = t / a.vecs;
+                const int c = t - k * a.vecs;
+                const int32_t row = __shfl(src_row, k < kWave ? k : 0);
+                rows[j] = (t < tasks) ? row : -1;
+                ks[j] = k;
+                cs[j] = c;
+                if (rows[j] >= 0) {
+#pragma unroll
+                    for (int h = 0; h < NKV; ++h)
+                        buf[h][j] = reinterpret_cast<const V *>(a.pool + a.base[h] +
+                                                                (uint64_t)(uint32_t)rows[j] * a.row_bytes)[c];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < TPL; ++j) {
+                if (rows[j] >= 0) {
+#pragma unroll
+                    for (int h = 0; h < NKV; ++h)
+                        put<true>(&reinterpret_cast<V *>(a.out[h] + (uint64_t)(o0 + ks[j]) * a.row_bytes)[cs[j]],
+                                  buf[h][j]);
+                }
+            }
         }
-        copy_rows<V, NKV, 2, true>(dst, src, a.vecs, lane);
     }
-    if (bad != 0 && lane == 0) atomicOr(a.flags, bad);
+    if (bad != 0) atomicOr(a.flags, bad);
 }
 
 // ----------------------------------------------------------------------------
@@ -415,6 +499,34 @@ int dispatch_vec(int vb, F &&f) {
         case 2: return f((uint16_t *)nullptr);
         default: return f((uint8_t *)nullptr);
     }
+}
+
+// Tile shape of a store / gather launch.  One tile per wave; the tile's rows
+// are chosen so that each lane has a few 16-byte loads in flight: about 6
+// (K and V together) for a gather, about 3 for a store, whose sources are
+// plain contiguous rows.  Chunks per lane per round (TPL) is 4, or 8 when a
+// tile needs more than 4.  Measured on MI355X against 1-8 rows per tile,
+// 1-16 tiles per wave and TPL 2-8, for 2,048-byte (K+V), 1,024-byte (K+V)
+// and 1,152-byte (MLA) rows at 32 K to 1.2 M rows per launch: within a few
+// percent of the best shape for every one.
+struct Tiling {
+    int32_t tile_rows;
+    int32_t tiles_per_wave;
+    int32_t tpl;
+    int64_t grid;
+};
+
+Tiling tiling_for(int32_t vecs, int32_t nkv, int64_t rows, bool gather) {
+    Tiling t;
+    const int64_t target = gather ? 6 * kWave : 3 * kWave;  // 16-byte loads per wave per round, K and V together
+    int64_t tr = gather ? (target + (int64_t)nkv * vecs / 2) / ((int64_t)nkv * vecs)  // rounded
+                        : target / ((int64_t)nkv * vecs);                             // rounded down
+    t.tile_rows = (int32_t)(tr < 1 ? 1 : (tr > kWave ? kWave : tr));
+    t.tpl = gather && (int64_t)t.tile_rows * vecs > 4 * kWave ? 8 : (gather ? 4 : 8);
+    t.tiles_per_wave = 1;
+    const int64_t waves = (rows + t.tile_rows - 1) / t.tile_rows;
+    t.grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    return t;
 }
 
 }  // namespace
@@ -600,13 +712,22 @@ int ukv_store_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t
                                   (uint64_t)(uintptr_t)k_dev, (uint64_t)(uintptr_t)a.src[1],
                                   (uint64_t)src_row_stride_bytes});
     a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
-    const int64_t grid = (n + kWavesPerBlock - 1) / kWavesPerBlock;
+    const Tiling tl = tiling_for(a.vecs, nkv, n, false);
+    a.tile_rows = tl.tile_rows;
+    a.tiles_per_wave = tl.tiles_per_wave;
+    const int64_t grid = tl.grid;
+    if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n too large for one launch", who);
     auto launch = [&](auto *tag) {
         using V = std::remove_pointer_t<decltype(tag)>;
-        if (nkv == 2)
-            hipLaunchKernelGGL((store_kernel<V, 2>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        const dim3 g((unsigned)grid), b(kBlock);
+        if (nkv == 2 && tl.tpl == 8)
+            hipLaunchKernelGGL((store_kernel<V, 2, 8>), g, b, 0, stream, a);
+        else if (nkv == 2)
+            hipLaunchKernelGGL((store_kernel<V, 2, 4>), g, b, 0, stream, a);
+        else if (tl.tpl == 8)
+            hipLaunchKernelGGL((store_kernel<V, 1, 8>), g, b, 0, stream, a);
         else
-            hipLaunchKernelGGL((store_kernel<V, 1>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+            hipLaunchKernelGGL((store_kernel<V, 1, 4>), g, b, 0, stream, a);
         return check_launch(who);
     };
     return dispatch_vec<2>(vb, launch);
@@ -654,19 +775,26 @@ int ukv_gather_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_
     a.bpp = (uint32_t)q.blocks_per_page;
     a.num_pages = (uint32_t)s.num_pages;
     a.row_bytes = (uint32_t)q.row_bytes;
-    a.rows_per_wave = kGatherRowsPerWave;
     a.flags = pool->flags_dev;
     const int vb = vec_bytes_for({q.row_bytes, vk.byte_offset, vv.byte_offset, (uint64_t)(uintptr_t)pool->raw,
                                   (uint64_t)(uintptr_t)k_out_dev, (uint64_t)(uintptr_t)a.out[1]});
     a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
-    const int64_t waves = (out_rows + a.rows_per_wave - 1) / a.rows_per_wave;
-    const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    const Tiling tl = tiling_for(a.vecs, nkv, out_rows, true);
+    a.tile_rows = tl.tile_rows;
+    a.tiles_per_wave = tl.tiles_per_wave;
+    const int64_t grid = tl.grid;
+    if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: out_rows too large for one launch", who);
     auto launch = [&](auto *tag) {
         using V = std::remove_pointer_t<decltype(tag)>;
-        if (nkv == 2)
-            hipLaunchKernelGGL((gather_kernel<V, 2>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        const dim3 g((unsigned)grid), b(kBlock);
+        if (nkv == 2 && tl.tpl == 8)
+            hipLaunchKernelGGL((gather_kernel<V, 2, 8>), g, b, 0, stream, a);
+        else if (nkv == 2)
+            hipLaunchKernelGGL((gather_kernel<V, 2, 4>), g, b, 0, stream, a);
+        else if (tl.tpl == 8)
+            hipLaunchKernelGGL((gather_kernel<V, 1, 8>), g, b, 0, stream, a);
         else
-            hipLaunchKernelGGL((gather_kernel<V, 1>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+            hipLaunchKernelGGL((gather_kernel<V, 1, 4>), g, b, 0, stream, a);
         return check_launch(who);
     };
     return dispatch_vec<2>(vb, launch);
