@@ -16,8 +16,8 @@ Output: one JSON line per workload.  `value` is algorithmic GB/s (bytes the
 method must read and write, 1e9 B/s) over the whole step with inputs resident
 in HBM.  `roofline` reports the dominant kernel per launch, from HIP events
 recorded around each of its launches inside the timed region, on the stream
-the kernels run on.  `ops` gives every launch kind's mean time from one extra
-step with events around all launches (outside the timed region).
+the kernels run on.  `ops` gives every launch kind's time per launch, from
+all its launches in step order run back to back (outside the timed region).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -42,7 +42,7 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "KV store/gather/move HBM GB/s and % of peak, Llama-3-8B-shape pool"
 KERNEL_SRC = os.path.join(ROOT, "store_gather_amd", "csrc", "ukv_runtime.hip")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-WORKLOADS = ("decode_8b", "prefill_8b", "hybrid", "move_70b", "tiny")
+WORKLOADS = ("decode_8b", "prefill_8b", "hybrid", "move_70b", "tiny", "decode_8b_fused", "prefill_8b_fused")
 
 
 def log(msg):
@@ -129,12 +129,19 @@ DESCRIPTIONS = {
                 "layers, K and V, in one launch",
     "tiny": "tiny: 2 layers, 2 KV heads x 8, bf16, page 4, 16 pages; store 37 entries (3 tombstones), gather 3 "
             "requests of 5/11/21 tokens, move 8 rows",
+    "decode_8b_fused": "decode_8b_fused: the decode_8b batch with the 256 new rows of all 32 layers stored in one "
+                       "launch (ukv_store_kv_layers), then the per-layer gathers",
+    "prefill_8b_fused": "prefill_8b_fused: the prefill_8b batch with all 32 layers stored in one launch and gathered "
+                        "back in one launch (ukv_store_kv_layers / ukv_gather_kv_layers), then the move",
 }
 
 
 def build_script(name: str, W, reduced: bool = False) -> Script:
     """The step of workload `name`.  `reduced` shrinks the pools (same row and page geometry,
     envelopes of at most ~8 GiB) for the CPU-oracle sample."""
+    if name.endswith("_fused"):
+        return fuse_layers(build_script(name[: -len("_fused")], W, reduced), name,
+                           gathers=name.startswith("prefill"))
     if name == "decode_8b":
         w = W.decode_8b()
     elif name == "prefill_8b":
@@ -242,6 +249,45 @@ def build_script(name: str, W, reduced: bool = False) -> Script:
     return Script(name, DESCRIPTIONS[name], list(w.shapes), ps, arrays, buffers, ops, roof[0], roof[1], counts)
 
 
+def fuse_layers(s: Script, name: str, gathers: bool) -> Script:
+    """The same step with each sub-pool's per-layer stores (and, if asked, its per-layer
+    gathers, when they share one window) replaced by one launch over all layers."""
+    ops: List[Op] = []
+    for op in s.ops:
+        if op.kind == "store":
+            prev = next((o for o in ops if o.kind == "store_layers" and o.sub == op.sub), None)
+            if prev is None:
+                ops.append(Op("store_layers", op.sub, op.label.replace("store", "store_layers"),
+                              {"layer": op.args["layer"], "count": 1, "ids": op.args["ids"], "n": op.args["n"]},
+                              op.nbytes))
+            else:
+                prev.args["count"] += 1
+                prev.nbytes += op.nbytes
+        elif op.kind == "gather" and gathers:
+            prev = next((o for o in ops if o.kind == "gather_layers" and o.sub == op.sub), None)
+            if prev is None:
+                ops.append(Op("gather_layers", op.sub, op.label.replace("gather", "gather_layers"),
+                              dict(op.args, count=1), op.nbytes))
+            else:
+                assert prev.args["window"] == op.args["window"]
+                prev.args["count"] += 1
+                prev.nbytes += op.nbytes
+        else:
+            ops.append(op)
+    buffers = dict(s.buffers)
+    if gathers:
+        for k, (rows, rb) in s.buffers.items():
+            if k.startswith("out"):
+                count = next(o.args["count"] for o in ops if o.kind == "gather_layers" and f"out{o.sub}_" in k)
+                buffers[k] = (rows * count, rb)
+    totals: Dict[str, int] = {}
+    for op in ops:
+        totals[op.kind] = totals.get(op.kind, 0) + op.nbytes
+    top = max(totals, key=totals.get)  # the roofline kernel: the kind that moves the most bytes
+    return Script(name, DESCRIPTIONS[name], s.shapes, s.page_size, s.arrays, buffers, ops,
+                  lambda op: op.kind == top, top.split("_")[0], dict(s.counts))
+
+
 _OUT_OF = {"slots": "ids", "msrc": "msrcid", "mdst": "mdstid", "table": "bt"}
 
 
@@ -289,6 +335,17 @@ class GpuRunner:
             U.ukv_gather_kv(self.pool, sub, a["layer"], t[f"bt{sub}"], t[f"lens{sub}"], t[a["cu"]], a["window"], ko, vo)
         elif op.kind == "move":
             U.ukv_move_kv(self.pool, sub, t[f"mdstid{sub}"], t[f"msrcid{sub}"], a["l0"], a["l1"])
+        elif op.kind == "store_layers":
+            n, c, l0 = a["n"], a["count"], a["layer"]
+            k = t[f"src{sub}_0"][l0 * n: (l0 + c) * n].view(c, n, -1)
+            v = t[f"src{sub}_1"][l0 * n: (l0 + c) * n].view(c, n, -1) if nkv == 2 else None
+            U.ukv_store_kv_layers(self.pool, sub, l0, c, t[a["ids"]], k, v)
+        elif op.kind == "gather_layers":
+            rows, c = a["rows"], a["count"]
+            ko = t[f"out{sub}_0"][: c * rows].view(c, rows, -1)
+            vo = t[f"out{sub}_1"][: c * rows].view(c, rows, -1) if nkv == 2 else None
+            U.ukv_gather_kv_layers(self.pool, sub, a["layer"], c, t[f"bt{sub}"], t[f"lens{sub}"], t[a["cu"]],
+                                   a["window"], ko, vo)
         else:
             raise ValueError(op.kind)
 
@@ -326,13 +383,26 @@ def cpu_baseline(name: str, W, budget_s: float = 12.0) -> dict:
                         bufs[f"out{sub}_0"][:rows], bufs[f"out{sub}_1"][:rows] if nkv == 2 else None)
         elif op.kind == "move":
             pool.move(sub, h[f"mdstid{sub}"], h[f"msrcid{sub}"], a["l0"], a["l1"])
+        elif op.kind == "store_layers":
+            n = a["n"]
+            for i in range(a["count"]):
+                r0 = (a["layer"] + i) * n
+                pool.store(sub, a["layer"] + i, h[a["ids"]], bufs[f"src{sub}_0"][r0: r0 + n],
+                           bufs[f"src{sub}_1"][r0: r0 + n] if nkv == 2 else None)
+        elif op.kind == "gather_layers":
+            rows = a["rows"]
+            for i in range(a["count"]):
+                pool.gather(sub, a["layer"] + i, h[f"bt{sub}"], h[f"lens{sub}"], h[a["cu"]], a["window"],
+                            bufs[f"out{sub}_0"][i * rows:(i + 1) * rows],
+                            bufs[f"out{sub}_1"][i * rows:(i + 1) * rows] if nkv == 2 else None)
         done_bytes += op.nbytes
         done_ops += 1
         if time.perf_counter() - t0 > budget_s and op.kind not in ("translate", "translate_pages"):
             break
     dt = time.perf_counter() - t0
     envelope = sum(p.envelope_bytes for p in pool.plan.subs)
-    shrunk = " (same row and page geometry, fewer pages)" if name in ("prefill_8b", "hybrid", "move_70b") else ""
+    shrunk = " (same row and page geometry, fewer pages)" if name.split("_fused")[0] in (
+        "prefill_8b", "hybrid", "move_70b") else ""
     return {
         "value": round(done_bytes / dt / 1e9, 3),
         "unit": "GB/s",
@@ -395,26 +465,31 @@ def run_workload(name, args, torch, U, W, device) -> dict:
         roof_bytes = float(np.mean([op.nbytes for op, _, _ in timed]))
         achieved = roof_bytes / (roof_ms * 1e-3) / 1e9
 
-    # one more step with events around every launch: per-kind launch times (outside the timed region)
-    per = [(op, mk(), mk()) for op in script.ops]
-    torch.cuda.synchronize()
-    for op, e0, e1 in per:
-        e0.record()
-        g.launch(op)
-        e1.record()
-    torch.cuda.synchronize()
+    # per-kind launch times, outside the timed region: all launches of a kind in step order
+    # (distinct layers, so no launch re-reads what the previous one left in cache), back to
+    # back between two events; a kind with a single launch per step is run three times
     agg: Dict[str, dict] = {}
-    for op, e0, e1 in per:
-        key = op.label.split(" sub")[0]
-        d = agg.setdefault(key, {"launches": 0, "ms": 0.0, "bytes": 0})
-        d["launches"] += 1
-        d["ms"] += e0.elapsed_time(e1)
-        d["bytes"] += op.nbytes
+    kinds: Dict[str, List[Op]] = {}
+    for op in script.ops:
+        kinds.setdefault(op.label.split(" sub")[0], []).append(op)
+    for key, group in kinds.items():
+        seq = group if len(group) > 1 else group * 3
+        for op in seq[:2]:
+            g.launch(op)
+        e0, e1 = mk(), mk()
+        torch.cuda.synchronize()
+        e0.record()
+        for op in seq:
+            g.launch(op)
+        e1.record()
+        torch.cuda.synchronize()
+        agg[key] = {"launches": len(group), "ms": e0.elapsed_time(e1) / len(seq),
+                    "bytes": sum(op.nbytes for op in seq) / len(seq)}
     ops_out = {}
     for k, d in agg.items():
         gbps = d["bytes"] / (d["ms"] * 1e-3) / 1e9
-        ops_out[k] = {"launches": d["launches"], "ms_per_launch": num(d["ms"] / d["launches"], 5),
-                      "bytes_per_launch": int(d["bytes"] // d["launches"]), "GBps": num(gbps, 1),
+        ops_out[k] = {"launches_per_step": d["launches"], "ms_per_launch": num(d["ms"], 5),
+                      "bytes_per_launch": int(d["bytes"]), "GBps": num(gbps, 1),
                       "pct_of_peak": num(100 * gbps / PEAK_GBPS, 2)}
     flags = U.ukv_pool_error_flags(g.pool)
     assert flags == frozenset(), f"device flags raised: {flags}"

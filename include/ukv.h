@@ -211,6 +211,19 @@ int ukv_store_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t
                  const void *k_dev, const void *v_dev, int64_t src_row_stride_bytes, hipStream_t stream);
 
 /*
+ * The store on several layers in one launch: layers layer_begin + i*layer_step
+ * for i < layer_count (step >= 1, all inside the sub-pool), each exactly as
+ * ukv_store_kv, with layer i's K / V source rows at
+ * k_dev / v_dev + i * src_layer_stride_bytes + entry * src_row_stride_bytes.
+ * The ids are translated once for the batch and serve every layer (DKV
+ * 实现拆解 and 关联脉络: the write location is translated once per forward
+ * batch, #35245).  layer_count = 0 is a no-op; at most 65535 layers.
+ */
+int ukv_store_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin, int32_t layer_count,
+                        int32_t layer_step, const int32_t *ids_dev, int64_t n, const void *k_dev, const void *v_dev,
+                        int64_t src_row_stride_bytes, int64_t src_layer_stride_bytes, hipStream_t stream);
+
+/*
  * Block-table gather into contiguous ragged K / V (DKV 功能与动机: a backend
  * reads a layer through one contiguous tensor plus one shared block table).
  * Output row o belongs to request r with cu_out[r] <= o < cu_out[r+1] and holds
@@ -230,6 +243,20 @@ int ukv_store_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t
 int ukv_gather_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t *block_table_dev,
                   int64_t bt_stride, const int32_t *seq_lens_dev, const int64_t *cu_out_dev, int32_t num_reqs,
                   int32_t window, void *k_out_dev, void *v_out_dev, int64_t out_rows, hipStream_t stream);
+
+/*
+ * The gather on several layers in one launch: layers layer_begin + i*layer_step
+ * for i < layer_count, each exactly as ukv_gather_kv with one block table,
+ * seq_lens, cu_out and window for all of them; layer i's rows go to
+ * k_out_dev / v_out_dev + i * out_layer_stride_bytes.  With more than one
+ * layer, |out_layer_stride_bytes| must be at least out_rows * row_bytes (the
+ * layers' outputs may not overlap), else UKV_ERR_INVALID_ARG.
+ */
+int ukv_gather_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin, int32_t layer_count,
+                         int32_t layer_step, const int32_t *block_table_dev, int64_t bt_stride,
+                         const int32_t *seq_lens_dev, const int64_t *cu_out_dev, int32_t num_reqs, int32_t window,
+                         void *k_out_dev, void *v_out_dev, int64_t out_rows, int64_t out_layer_stride_bytes,
+                         hipStream_t stream);
 
 /*
  * Row move on every layer in [layer_begin, layer_end), K and V (DKV 关键文件,

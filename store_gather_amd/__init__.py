@@ -39,8 +39,9 @@ FLAGS = {1: "slot_range", 2: "bad_id", 4: "bad_block", 8: "layout"}
 
 EXPORTS = (
     "ukv_pool_plan", "ukv_pool_create", "ukv_pool_destroy", "ukv_pool_get_plan", "ukv_pool_view", "ukv_plan_view",
-    "ukv_translate_loc_for_kernel", "ukv_translate_pages_for_kernel", "ukv_store_kv", "ukv_gather_kv",
-    "ukv_move_kv", "ukv_pool_error_flags", "ukv_last_error", "ukv_status_name",
+    "ukv_translate_loc_for_kernel", "ukv_translate_pages_for_kernel", "ukv_store_kv", "ukv_store_kv_layers",
+    "ukv_gather_kv", "ukv_gather_kv_layers", "ukv_move_kv", "ukv_pool_error_flags", "ukv_last_error",
+    "ukv_status_name",
 )
 
 
@@ -101,7 +102,9 @@ def _load() -> ctypes.CDLL:
         "ukv_translate_loc_for_kernel": [vp, i32, vp, i64, vp, i64, vp, vp],
         "ukv_translate_pages_for_kernel": [vp, i32, vp, i64, vp, i64, vp, vp],
         "ukv_store_kv": [vp, i32, i32, vp, i64, vp, vp, i64, vp],
+        "ukv_store_kv_layers": [vp, i32, i32, i32, i32, vp, i64, vp, vp, i64, i64, vp],
         "ukv_gather_kv": [vp, i32, i32, vp, i64, vp, vp, i32, i32, vp, vp, i64, vp],
+        "ukv_gather_kv_layers": [vp, i32, i32, i32, i32, vp, i64, vp, vp, i32, i32, vp, vp, i64, i64, vp],
         "ukv_move_kv": [vp, i32, vp, vp, i64, i32, i32, vp],
         "ukv_pool_error_flags": [vp, vp, P(ctypes.c_uint32)],
     }
@@ -307,6 +310,33 @@ def ukv_store_kv(pool: Pool, sub: int, layer: int, ids: torch.Tensor, k: torch.T
                              _stream_handle(stream)))
 
 
+def ukv_store_kv_layers(pool: Pool, sub: int, layer_begin: int, layer_count: int, ids: torch.Tensor,
+                        k: torch.Tensor, v: Optional[torch.Tensor] = None, layer_step: int = 1, stream=None) -> None:
+    """Store on layers layer_begin + i*layer_step (i < layer_count) in one launch; k / v are
+    [layer_count, n, ...] with each layer's rows contiguous (MLA: v None)."""
+    d = pool.device
+    _dev_ptr(ids, "ids", d, torch.int32)
+    if not ids.is_contiguous():
+        raise ValueError("ids must be contiguous")
+    n = ids.numel()
+    rb = pool.row_bytes(sub)
+    for name, t in (("k", k), ("v", v)):
+        if t is not None and (t.dim() < 2 or t.shape[0] != layer_count):
+            raise ValueError(f"{name} must be [layer_count, n, ...]")
+    if layer_count == 0 or n == 0:
+        return
+    _, ks = _rows_arg(k[0], "k", n, rb, d)
+    vs = _rows_arg(v[0], "v", n, rb, d)[1] if v is not None else ks
+    if vs != ks:
+        raise ValueError("k and v must share one row stride")
+    kl = k.stride(0) * k.element_size()
+    if v is not None and v.stride(0) * v.element_size() != kl:
+        raise ValueError("k and v must share one layer stride")
+    _check(_lib.ukv_store_kv_layers(pool.handle, sub, layer_begin, layer_count, layer_step, ids.data_ptr(), n,
+                                    k.data_ptr(), None if v is None else v.data_ptr(), ks, kl,
+                                    _stream_handle(stream)))
+
+
 def ukv_gather_kv(pool: Pool, sub: int, layer: int, block_table: torch.Tensor, seq_lens: torch.Tensor,
                   cu_out: torch.Tensor, window: int, k_out: torch.Tensor, v_out: Optional[torch.Tensor] = None,
                   stream=None) -> None:
@@ -338,6 +368,38 @@ def ukv_gather_kv(pool: Pool, sub: int, layer: int, block_table: torch.Tensor, s
                               None if v_out is None else v_out.data_ptr(), out_rows, _stream_handle(stream)))
 
 
+def ukv_gather_kv_layers(pool: Pool, sub: int, layer_begin: int, layer_count: int, block_table: torch.Tensor,
+                         seq_lens: torch.Tensor, cu_out: torch.Tensor, window: int, k_out: torch.Tensor,
+                         v_out: Optional[torch.Tensor] = None, layer_step: int = 1, stream=None) -> None:
+    """Gather layers layer_begin + i*layer_step (i < layer_count) in one launch into
+    k_out / v_out of shape [layer_count, out_rows, ...]."""
+    d = pool.device
+    _dev_ptr(block_table, "block_table", d, torch.int32)
+    _dev_ptr(seq_lens, "seq_lens", d, torch.int32)
+    _dev_ptr(cu_out, "cu_out", d, torch.int64)
+    if block_table.dim() != 2 or (block_table.numel() > 0 and block_table.stride(1) != 1):
+        raise ValueError("block_table must be [num_reqs, width] with unit inner stride")
+    num_reqs = seq_lens.numel()
+    if block_table.shape[0] != num_reqs or cu_out.numel() != num_reqs + 1:
+        raise ValueError("block_table rows / cu_out size do not match seq_lens")
+    rb = pool.row_bytes(sub)
+    for name, t in (("k_out", k_out), ("v_out", v_out)):
+        if t is not None:
+            _dev_ptr(t, name, d)
+            if not t.is_contiguous() or t.dim() < 2 or t.shape[0] != layer_count:
+                raise ValueError(f"{name} must be a contiguous [layer_count, out_rows, ...] tensor")
+            if (t[0].numel() * t.element_size()) % rb != 0:
+                raise ValueError(f"{name} rows must be whole rows of {rb} bytes")
+    out_rows = k_out[0].numel() * k_out.element_size() // rb if layer_count else 0
+    if v_out is not None and v_out.shape != k_out.shape:
+        raise ValueError("k_out and v_out differ in shape")
+    _check(_lib.ukv_gather_kv_layers(pool.handle, sub, layer_begin, layer_count, layer_step, block_table.data_ptr(),
+                                     block_table.stride(0) if block_table.numel() else 0, seq_lens.data_ptr(),
+                                     cu_out.data_ptr(), num_reqs, int(window), k_out.data_ptr(),
+                                     None if v_out is None else v_out.data_ptr(), out_rows,
+                                     k_out.stride(0) * k_out.element_size(), _stream_handle(stream)))
+
+
 def ukv_move_kv(pool: Pool, sub: int, dst: torch.Tensor, src: torch.Tensor, layer_begin: int = 0,
                 layer_end: Optional[int] = None, stream=None) -> None:
     """view[l][dst] = view[l][src] for every layer in [layer_begin, layer_end), K and V."""
@@ -362,6 +424,7 @@ def ukv_pool_error_flags(pool: Pool, stream=None) -> frozenset:
 __all__ = [
     "UKV_MHA", "UKV_MLA", "UkvError", "SubpoolSpec", "Plan", "View", "Pool", "lib", "ukv_pool_plan",
     "plan_status", "ukv_pool_create", "allocate_pool", "ukv_pool_destroy", "ukv_pool_view", "ukv_plan_view", "dense_view",
-    "ukv_translate_loc_for_kernel", "ukv_translate_pages_for_kernel", "ukv_store_kv", "ukv_gather_kv",
-    "ukv_move_kv", "ukv_pool_error_flags", "ukv_last_error", "EXPORTS", "STATUS", "FLAGS",
+    "ukv_translate_loc_for_kernel", "ukv_translate_pages_for_kernel", "ukv_store_kv", "ukv_store_kv_layers",
+    "ukv_gather_kv", "ukv_gather_kv_layers", "ukv_move_kv", "ukv_pool_error_flags", "ukv_last_error", "EXPORTS",
+    "STATUS", "FLAGS",
 ]

@@ -222,10 +222,13 @@ struct StoreArgs {
     int32_t vecs;          // row_bytes / sizeof(V)
     int32_t tile_rows;     // rows per tile, <= 64
     int32_t tiles_per_wave;
+    uint64_t layer_base_step;  // view bytes from one stored layer to the next (grid y)
+    int64_t src_layer_stride;  // source bytes from one stored layer to the next
     uint32_t *flags;
 };
 
-// K_view[ids[i]] = k[i], V_view[ids[i]] = v[i]; waves own runs of tiles.
+// K_view[l][ids[i]] = k[l][i], V_view[l][ids[i]] = v[l][i] for the layer of
+// grid row blockIdx.y; waves own runs of tiles.
 template <typename V, int NKV, int TPL = kTasksPerLane>
 __global__ __launch_bounds__(kBlock) void store_kernel(StoreArgs a) {
     const int lane = lane_id();
@@ -235,6 +238,8 @@ __global__ __launch_bounds__(kBlock) void store_kernel(StoreArgs a) {
     if (i_begin >= a.n) return;
     const int64_t i_end = i_begin + per_wave < a.n ? i_begin + per_wave : a.n;
     const int tasks = a.tile_rows * a.vecs;
+    const uint64_t view0 = (uint64_t)blockIdx.y * a.layer_base_step;
+    const int64_t src0 = (int64_t)blockIdx.y * a.src_layer_stride;
     bool bad = false;
     for (int64_t i0 = i_begin; i0 < i_end; i0 += a.tile_rows) {
         // lane k: the destination row of entry i0 + k (-1: skipped)
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(kBlock) void store_kernel(StoreArgs a) {
                 if (rows[j] >= 0) {
 #pragma unroll
                     for (int h = 0; h < NKV; ++h)
-                        buf[h][j] = reinterpret_cast<const V *>(a.src[h] + (i0 + k) * a.src_stride)[c];
+                        buf[h][j] = reinterpret_cast<const V *>(a.src[h] + src0 + (i0 + k) * a.src_stride)[c];
                 }
             }
 #pragma unroll
@@ -271,14 +276,15 @@ __global__ __launch_bounds__(kBlock) void store_kernel(StoreArgs a) {
                 if (rows[j] >= 0) {
 #pragma unroll
                     for (int h = 0; h < NKV; ++h)
-                        reinterpret_cast<V *>(a.pool + a.base[h] + (uint64_t)(uint32_t)rows[j] * a.row_bytes)[cs[j]] =
+                        reinterpret_cast<V *>(a.pool + a.base[h] + view0 +
+                                              (uint64_t)(uint32_t)rows[j] * a.row_bytes)[cs[j]] =
                             buf[h][j];
                 }
             }
             (void)ks;
         }
     }
-    if (bad) atomicOr(a.flags, UKV_FLAG_BAD_ID);
+    if (bad && blockIdx.y == 0) atomicOr(a.flags, UKV_FLAG_BAD_ID);
 }
 
 // ----------------------------------------------------------------------------
@@ -302,6 +308,8 @@ struct GatherArgs {
     int32_t vecs;
     int32_t tile_rows;
     int32_t tiles_per_wave;
+    uint64_t layer_base_step;  // view bytes from one gathered layer to the next (grid y)
+    int64_t out_layer_stride;  // output bytes from one gathered layer to the next
     uint32_t *flags;
 };
 
@@ -340,12 +348,15 @@ __device__ __forceinline__ int32_t gather_source_row(const GatherArgs &a, int64_
 template <typename V, int NKV, int TPL = kTasksPerLane>
 __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
     const int lane = lane_id();
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
         if (a.cu_out[0] != 0 || a.cu_out[a.num_reqs] != a.out_rows) atomicOr(a.flags, UKV_FLAG_LAYOUT);
     }
     const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
     const int64_t per_wave = (int64_t)a.tile_rows * a.tiles_per_wave;
     const int64_t o_begin = wave * per_wave;
+    const uint64_t view0 = (uint64_t)blockIdx.y * a.layer_base_step;
+    uint8_t *const out_l[2] = {a.out[0] + (int64_t)blockIdx.y * a.out_layer_stride,
+                               a.out[1] + (int64_t)blockIdx.y * a.out_layer_stride};
     if (o_begin >= a.out_rows) return;
     const int64_t o_end = o_begin + per_wave < a.out_rows ? o_begin + per_wave : a.out_rows;
 
@@ -388,7 +399,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
                 if (rows[j] >= 0) {
 #pragma unroll
                     for (int h = 0; h < NKV; ++h)
-                        buf[h][j] = reinterpret_cast<const V *>(a.pool + a.base[h] +
+                        buf[h][j] = reinterpret_cast<const V *>(a.pool + a.base[h] + view0 +
                                                                 (uint64_t)(uint32_t)rows[j] * a.row_bytes)[c];
                 }
             }
@@ -397,13 +408,13 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(GatherArgs a) {
                 if (rows[j] >= 0) {
 #pragma unroll
                     for (int h = 0; h < NKV; ++h)
-                        put<true>(&reinterpret_cast<V *>(a.out[h] + (uint64_t)(o0 + ks[j]) * a.row_bytes)[cs[j]],
+                        put<true>(&reinterpret_cast<V *>(out_l[h] + (uint64_t)(o0 + ks[j]) * a.row_bytes)[cs[j]],
                                   buf[h][j]);
                 }
             }
         }
     }
-    if (bad != 0) atomicOr(a.flags, bad);
+    if (bad != 0 && blockIdx.y == 0) atomicOr(a.flags, bad);
 }
 
 // ----------------------------------------------------------------------------
@@ -671,19 +682,38 @@ int ukv_translate_pages_for_kernel(const ukv_pool *pool, int32_t sub, const int3
                             "ukv_translate_pages_for_kernel");
 }
 
-int ukv_store_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t *ids_dev, int64_t n,
-                 const void *k_dev, const void *v_dev, int64_t src_row_stride_bytes, hipStream_t stream) {
+// Checks a layer range [begin, begin + count*step) with step >= 1 against the
+// sub-pool and returns the view byte step between consecutive layers in it.
+static int check_layer_range(const ukv_pool *pool, int32_t sub, int32_t begin, int32_t count, int32_t step,
+                             const char *who, uint64_t *base_step) {
+    const ukv_subpool_spec &s = pool->spec[sub];
+    if (begin < 0 || count < 0 || step < 1 ||
+        (count > 0 && (int64_t)begin + (int64_t)(count - 1) * step >= (int64_t)s.layer_num))
+        return fail(UKV_ERR_INVALID_ARG, "%s: layers %d + k*%d for k < %d run outside [0, %d)", who, begin, step, count,
+                    s.layer_num);
+    if (count > 65535) return fail(UKV_ERR_INVALID_ARG, "%s: more than 65535 layers in one call", who);
+    const uint64_t blocks_per_layer = s.kind == UKV_MHA ? 2 : 1;
+    *base_step = (uint64_t)step * blocks_per_layer * (uint64_t)pool->plan.page_size * pool->plan.sub[sub].row_bytes;
+    return UKV_OK;
+}
+
+static uint64_t magnitude(int64_t v) { return v < 0 ? (uint64_t)(-(v + 1)) + 1 : (uint64_t)v; }
+
+int ukv_store_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin, int32_t layer_count,
+                        int32_t layer_step, const int32_t *ids_dev, int64_t n, const void *k_dev, const void *v_dev,
+                        int64_t src_row_stride_bytes, int64_t src_layer_stride_bytes, hipStream_t stream) {
     const char *who = "ukv_store_kv";
     int rc = check_pool_call(pool, sub, who);
     if (rc != UKV_OK) return rc;
     const ukv_subpool_spec &s = pool->spec[sub];
     const ukv_subpool_plan &q = pool->plan.sub[sub];
-    if (layer < 0 || layer >= s.layer_num)
-        return fail(UKV_ERR_INVALID_ARG, "%s: layer %d outside [0, %d)", who, layer, s.layer_num);
+    uint64_t base_step = 0;
+    rc = check_layer_range(pool, sub, layer_begin, layer_count, layer_step, who, &base_step);
+    if (rc != UKV_OK) return rc;
     if (n < 0 || n > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n=%lld outside [0, 2^31)", who, (long long)n);
     const int nkv = s.kind == UKV_MHA ? 2 : 1;
     if (nkv == 1 && v_dev != nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: MLA sub-pool takes no V rows", who);
-    if (n == 0) return UKV_OK;
+    if (n == 0 || layer_count == 0) return UKV_OK;
     if (ids_dev == nullptr || k_dev == nullptr || (nkv == 2 && v_dev == nullptr))
         return fail(UKV_ERR_INVALID_ARG, "%s: null ids, K or V", who);
     if (src_row_stride_bytes < (int64_t)q.row_bytes)
@@ -692,9 +722,9 @@ int ukv_store_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t
     StoreArgs a;
     std::memset(&a, 0, sizeof(a));
     ukv_view vk, vv;
-    ukv::view_of(pool->plan, s, sub, layer, 0, &vk);
+    ukv::view_of(pool->plan, s, sub, layer_begin, 0, &vk);
     vv = vk;
-    if (nkv == 2) ukv::view_of(pool->plan, s, sub, layer, 1, &vv);
+    if (nkv == 2) ukv::view_of(pool->plan, s, sub, layer_begin, 1, &vv);
     a.pool = pool->raw;
     a.base[0] = vk.byte_offset;
     a.base[1] = vv.byte_offset;
@@ -707,10 +737,12 @@ int ukv_store_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t
     a.page_stride = (uint32_t)(pool->plan.page_size * q.blocks_per_page);
     a.ps = (uint32_t)pool->plan.page_size;
     a.row_bytes = (uint32_t)q.row_bytes;
+    a.layer_base_step = base_step;
+    a.src_layer_stride = layer_count > 1 ? src_layer_stride_bytes : 0;
     a.flags = pool->flags_dev;
     const int vb = vec_bytes_for({q.row_bytes, vk.byte_offset, vv.byte_offset, (uint64_t)(uintptr_t)pool->raw,
                                   (uint64_t)(uintptr_t)k_dev, (uint64_t)(uintptr_t)a.src[1],
-                                  (uint64_t)src_row_stride_bytes});
+                                  (uint64_t)src_row_stride_bytes, magnitude(a.src_layer_stride)});
     a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
     const Tiling tl = tiling_for(a.vecs, nkv, n, false);
     a.tile_rows = tl.tile_rows;
@@ -719,7 +751,7 @@ int ukv_store_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t
     if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n too large for one launch", who);
     auto launch = [&](auto *tag) {
         using V = std::remove_pointer_t<decltype(tag)>;
-        const dim3 g((unsigned)grid), b(kBlock);
+        const dim3 g((unsigned)grid, (unsigned)layer_count), b(kBlock);
         if (nkv == 2 && tl.tpl == 8)
             hipLaunchKernelGGL((store_kernel<V, 2, 8>), g, b, 0, stream, a);
         else if (nkv == 2)
@@ -733,32 +765,43 @@ int ukv_store_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t
     return dispatch_vec<2>(vb, launch);
 }
 
-int ukv_gather_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t *block_table_dev,
-                  int64_t bt_stride, const int32_t *seq_lens_dev, const int64_t *cu_out_dev, int32_t num_reqs,
-                  int32_t window, void *k_out_dev, void *v_out_dev, int64_t out_rows, hipStream_t stream) {
+int ukv_store_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t *ids_dev, int64_t n,
+                 const void *k_dev, const void *v_dev, int64_t src_row_stride_bytes, hipStream_t stream) {
+    return ukv_store_kv_layers(pool, sub, layer, 1, 1, ids_dev, n, k_dev, v_dev, src_row_stride_bytes, 0, stream);
+}
+
+int ukv_gather_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin, int32_t layer_count,
+                         int32_t layer_step, const int32_t *block_table_dev, int64_t bt_stride,
+                         const int32_t *seq_lens_dev, const int64_t *cu_out_dev, int32_t num_reqs, int32_t window,
+                         void *k_out_dev, void *v_out_dev, int64_t out_rows, int64_t out_layer_stride_bytes,
+                         hipStream_t stream) {
     const char *who = "ukv_gather_kv";
     int rc = check_pool_call(pool, sub, who);
     if (rc != UKV_OK) return rc;
     const ukv_subpool_spec &s = pool->spec[sub];
     const ukv_subpool_plan &q = pool->plan.sub[sub];
-    if (layer < 0 || layer >= s.layer_num)
-        return fail(UKV_ERR_INVALID_ARG, "%s: layer %d outside [0, %d)", who, layer, s.layer_num);
+    uint64_t base_step = 0;
+    rc = check_layer_range(pool, sub, layer_begin, layer_count, layer_step, who, &base_step);
+    if (rc != UKV_OK) return rc;
     if (num_reqs < 0 || window < 0 || out_rows < 0 || out_rows > kMaxGrid)
         return fail(UKV_ERR_INVALID_ARG, "%s: num_reqs=%d window=%d out_rows=%lld out of range", who, num_reqs,
                     window, (long long)out_rows);
     const int nkv = s.kind == UKV_MHA ? 2 : 1;
     if (nkv == 1 && v_out_dev != nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: MLA sub-pool has no V output", who);
-    if (out_rows == 0) return UKV_OK;
+    if (out_rows == 0 || layer_count == 0) return UKV_OK;
     if (cu_out_dev == nullptr || k_out_dev == nullptr || (nkv == 2 && v_out_dev == nullptr))
         return fail(UKV_ERR_INVALID_ARG, "%s: null cu_out or output", who);
     if (num_reqs > 0 && (block_table_dev == nullptr || seq_lens_dev == nullptr || bt_stride < 1))
         return fail(UKV_ERR_INVALID_ARG, "%s: null block table / seq_lens or bt_stride < 1", who);
+    if (layer_count > 1 && magnitude(out_layer_stride_bytes) < (uint64_t)out_rows * q.row_bytes)
+        return fail(UKV_ERR_INVALID_ARG, "%s: out_layer_stride_bytes=%lld makes the layers' outputs overlap", who,
+                    (long long)out_layer_stride_bytes);
     GatherArgs a;
     std::memset(&a, 0, sizeof(a));
     ukv_view vk, vv;
-    ukv::view_of(pool->plan, s, sub, layer, 0, &vk);
+    ukv::view_of(pool->plan, s, sub, layer_begin, 0, &vk);
     vv = vk;
-    if (nkv == 2) ukv::view_of(pool->plan, s, sub, layer, 1, &vv);
+    if (nkv == 2) ukv::view_of(pool->plan, s, sub, layer_begin, 1, &vv);
     a.pool = pool->raw;
     a.base[0] = vk.byte_offset;
     a.base[1] = vv.byte_offset;
@@ -775,9 +818,12 @@ int ukv_gather_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_
     a.bpp = (uint32_t)q.blocks_per_page;
     a.num_pages = (uint32_t)s.num_pages;
     a.row_bytes = (uint32_t)q.row_bytes;
+    a.layer_base_step = base_step;
+    a.out_layer_stride = layer_count > 1 ? out_layer_stride_bytes : 0;
     a.flags = pool->flags_dev;
     const int vb = vec_bytes_for({q.row_bytes, vk.byte_offset, vv.byte_offset, (uint64_t)(uintptr_t)pool->raw,
-                                  (uint64_t)(uintptr_t)k_out_dev, (uint64_t)(uintptr_t)a.out[1]});
+                                  (uint64_t)(uintptr_t)k_out_dev, (uint64_t)(uintptr_t)a.out[1],
+                                  magnitude(a.out_layer_stride)});
     a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
     const Tiling tl = tiling_for(a.vecs, nkv, out_rows, true);
     a.tile_rows = tl.tile_rows;
@@ -786,7 +832,7 @@ int ukv_gather_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_
     if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: out_rows too large for one launch", who);
     auto launch = [&](auto *tag) {
         using V = std::remove_pointer_t<decltype(tag)>;
-        const dim3 g((unsigned)grid), b(kBlock);
+        const dim3 g((unsigned)grid, (unsigned)layer_count), b(kBlock);
         if (nkv == 2 && tl.tpl == 8)
             hipLaunchKernelGGL((gather_kernel<V, 2, 8>), g, b, 0, stream, a);
         else if (nkv == 2)
@@ -798,6 +844,13 @@ int ukv_gather_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_
         return check_launch(who);
     };
     return dispatch_vec<2>(vb, launch);
+}
+
+int ukv_gather_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t *block_table_dev,
+                  int64_t bt_stride, const int32_t *seq_lens_dev, const int64_t *cu_out_dev, int32_t num_reqs,
+                  int32_t window, void *k_out_dev, void *v_out_dev, int64_t out_rows, hipStream_t stream) {
+    return ukv_gather_kv_layers(pool, sub, layer, 1, 1, block_table_dev, bt_stride, seq_lens_dev, cu_out_dev,
+                                num_reqs, window, k_out_dev, v_out_dev, out_rows, 0, stream);
 }
 
 int ukv_move_kv(const ukv_pool *pool, int32_t sub, const int32_t *dst_dev, const int32_t *src_dev, int64_t n,

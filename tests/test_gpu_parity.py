@@ -396,3 +396,80 @@ def test_host_argument_errors():
     rc = U.lib().ukv_pool_create(U._specs_array([W.mha(2, 2, 8, 16)]), 1, 4, host.ctypes.data, host.size,
                                  ctypes.byref(h))
     assert rc == -1 and "not device memory" in U.ukv_last_error()
+
+
+# ---------------------------------------------------------------------------
+# several layers per launch (one translation serves every layer)
+# ---------------------------------------------------------------------------
+
+def test_fused_layer_store_and_gather():
+    w = W.decode_8b(num_pages=48, num_reqs=5, len_lo=30, len_hi=400, new_tokens=61)
+    pair = Pair(w.shapes, w.page_size)
+    rb = pair.rb(0)
+    slots = w.store_slots[0]
+    ids_d = U.ukv_translate_loc_for_kernel(pair.gpu, 0, to_dev(slots))
+    ids, _ = pair.orc.translate(0, slots)
+    layers = list(range(3, 30, 2))  # 14 layers, step 2
+    k = bf16_rows(70, len(layers) * slots.size, rb).reshape(len(layers), slots.size, rb)
+    v = bf16_rows(71, len(layers) * slots.size, rb).reshape(len(layers), slots.size, rb)
+    U.ukv_store_kv_layers(pair.gpu, 0, 3, len(layers), ids_d, to_dev(k), to_dev(v), layer_step=2)
+    for i, layer in enumerate(layers):
+        pair.orc.store(0, layer, ids, k[i], v[i])
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    pair.assert_pools_equal()
+    table = W.padded_table(w.req_pages[0])
+    bt_d = U.ukv_translate_pages_for_kernel(pair.gpu, 0, to_dev(table))
+    bt, _ = pair.orc.translate_pages(0, table)
+    lens = w.req_lens[0]
+    for window, begin, count, step in ((0, 0, 32, 1), (100, 1, 11, 3)):
+        cu = W.out_offsets(lens, window)
+        rows = int(cu[-1])
+        ko = torch.zeros((count, rows, rb), dtype=torch.uint8, device="cuda")
+        vo = torch.zeros_like(ko)
+        U.ukv_gather_kv_layers(pair.gpu, 0, begin, count, bt_d, to_dev(lens), to_dev(cu), window, ko, vo,
+                               layer_step=step)
+        kh, vh = ko.cpu().numpy(), vo.cpu().numpy()
+        for i in range(count):
+            eko = np.zeros((rows, rb), np.uint8)
+            evo = np.zeros_like(eko)
+            pair.orc.gather(0, begin + i * step, bt, lens, cu, window, eko, evo)
+            assert np.array_equal(kh[i], eko) and np.array_equal(vh[i], evo), (window, i)
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+
+
+def test_fused_layers_mla_and_argument_errors():
+    w = W.hybrid(num_reqs=4, len_lo=10, len_hi=300, layer_num=24, window=128)
+    pair = Pair(w.shapes, w.page_size)
+    rb = pair.rb(1)
+    slots = w.store_slots[1]
+    ids_d = U.ukv_translate_loc_for_kernel(pair.gpu, 1, to_dev(slots))
+    ids, _ = pair.orc.translate(1, slots)
+    lat = bf16_rows(80, 24 * slots.size, rb).reshape(24, slots.size, rb)
+    U.ukv_store_kv_layers(pair.gpu, 1, 0, 24, ids_d, to_dev(lat))
+    for layer in range(24):
+        pair.orc.store(1, layer, ids, lat[layer], None)
+    pair.assert_pools_equal()
+    lens = w.req_lens[1]
+    table = W.padded_table(w.req_pages[1])
+    bt_d = U.ukv_translate_pages_for_kernel(pair.gpu, 1, to_dev(table))
+    bt, _ = pair.orc.translate_pages(1, table)
+    cu = W.out_offsets(lens)
+    rows = int(cu[-1])
+    ko = torch.zeros((6, rows, rb), dtype=torch.uint8, device="cuda")
+    U.ukv_gather_kv_layers(pair.gpu, 1, 2, 6, bt_d, to_dev(lens), to_dev(cu), 0, ko, layer_step=4)
+    kh = ko.cpu().numpy()
+    for i in range(6):
+        eko = np.zeros((rows, rb), np.uint8)
+        pair.orc.gather(1, 2 + 4 * i, bt, lens, cu, 0, eko, None)
+        assert np.array_equal(kh[i], eko)
+    # a layer range past the sub-pool, and overlapping per-layer outputs, are refused
+    with pytest.raises(U.UkvError) as e:
+        U.ukv_gather_kv_layers(pair.gpu, 1, 2, 6, bt_d, to_dev(lens), to_dev(cu), 0, ko, layer_step=5)
+    assert e.value.status == "UKV_ERR_INVALID_ARG"
+    rc = U.lib().ukv_gather_kv_layers(pair.gpu.handle, 1, 0, 2, 1, bt_d.data_ptr(), bt_d.stride(0),
+                                      to_dev(lens).data_ptr(), to_dev(cu).data_ptr(), len(lens), 0, ko.data_ptr(),
+                                      None, rows, rb * rows - 1, None)
+    assert rc == -1 and "overlap" in U.ukv_last_error()
+    with pytest.raises(U.UkvError):
+        U.ukv_store_kv_layers(pair.gpu, 1, 20, 5, ids_d, to_dev(lat[:5]))
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
