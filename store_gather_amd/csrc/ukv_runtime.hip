@@ -11,14 +11,17 @@
 //  - rows are moved as 16-byte integer vectors (global_load/store_dwordx4)
 //    whenever the row size, the view bases and the caller's pointers allow,
 //    so bf16 NaN payloads and denormals pass bit-exact;
-//  - one 64-lane wavefront owns a row (or a run of rows): the lanes cover
-//    the row's 16-byte chunks, so every access is a fully coalesced,
-//    contiguous wave-wide transfer;
-//  - per-row bookkeeping (the id, the request, the block-table entry) is
-//    wave-uniform and lives in scalar registers: the wave index is made
-//    uniform with readfirstlane, so those lookups are scalar loads;
-//  - all K and V loads of a row are issued before its stores, to keep
-//    several 1 KiB wave transfers in flight per wave;
+//  - store, gather and move work on tiles of rows: lane k of a 64-lane wave
+//    resolves row k of the tile (its id, its block-table entry, or its move
+//    pair), the row numbers are broadcast with ds_bpermute (__shfl), and the
+//    tile's 16-byte chunks are spread over all lanes, loads before stores.
+//    Tiles are sized by loads in flight per lane, so 32-byte rows, 1 KiB
+//    rows, 1,152-byte MLA latents and 2 KiB rows all keep the memory system
+//    equally busy (tile shapes swept on MI355X);
+//  - destinations written once (gather outputs, stored and moved pool rows)
+//    use the non-temporal store hint;
+//  - one launch can cover a strided range of layers (grid y), so one
+//    translation of a batch serves every layer;
 //  - nothing allocates, nothing synchronises; ids are int32 (the pool plan
 //    guarantees every view has fewer than 2^31 rows) and byte addresses are
 //    64-bit (base + (uint64) id * row_bytes), since pools reach hundreds of GiB.
@@ -92,31 +95,6 @@ __device__ __forceinline__ void put(V *p, V v) {
         __builtin_nontemporal_store(v, p);
     else
         *p = v;
-}
-
-// Copies NKV rows of `vecs` V-sized chunks, lanes striding over the chunks;
-// all loads of one round are issued before its stores.
-template <typename V, int NKV, int U, bool NT>
-__device__ __forceinline__ void copy_rows(V *const (&dst)[NKV], const V *const (&src)[NKV], int vecs, int lane) {
-    for (int c0 = lane; c0 < vecs; c0 += kWave * U) {
-        V buf[NKV][U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + u * kWave;
-            if (c < vecs) {
-#pragma unroll
-                for (int h = 0; h < NKV; ++h) buf[h][u] = src[h][c];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + u * kWave;
-            if (c < vecs) {
-#pragma unroll
-                for (int h = 0; h < NKV; ++h) put<NT>(&dst[h][c], buf[h][u]);
-            }
-        }
-    }
 }
 
 // ----------------------------------------------------------------------------
@@ -229,7 +207,7 @@ struct StoreArgs {
 
 // K_view[l][ids[i]] = k[l][i], V_view[l][ids[i]] = v[l][i] for the layer of
 // grid row blockIdx.y; waves own runs of tiles.
-template <typename V, int NKV, int TPL = kTasksPerLane>
+template <typename V, int NKV, int TPL = kTasksPerLane, bool NT = false>
 __global__ __launch_bounds__(kBlock) void store_kernel(StoreArgs a) {
     const int lane = lane_id();
     const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
@@ -276,9 +254,9 @@ __global__ __launch_bounds__(kBlock) void store_kernel(StoreArgs a) {
                 if (rows[j] >= 0) {
 #pragma unroll
                     for (int h = 0; h < NKV; ++h)
-                        reinterpret_cast<V *>(a.pool + a.base[h] + view0 +
-                                              (uint64_t)(uint32_t)rows[j] * a.row_bytes)[cs[j]] =
-                            buf[h][j];
+                        put<NT>(&reinterpret_cast<V *>(a.pool + a.base[h] + view0 +
+                                                       (uint64_t)(uint32_t)rows[j] * a.row_bytes)[cs[j]],
+                                buf[h][j]);
                 }
             }
             (void)ks;
@@ -434,32 +412,71 @@ struct MoveArgs {
     uint32_t ps;
     uint32_t row_bytes;
     int32_t vecs;
+    int32_t tile_units;  // (pair, layer) units per tile, <= 64
     uint32_t *flags;
 };
 
-// One wave per (row pair i, layer l), layers of one pair adjacent in the grid.
-template <typename V, int NKV>
+// Tiles of `tile_units` units u = (pair i, layer l), u = i * nl + l: lane k
+// resolves unit u0 + k to its source and destination row offsets (K view;
+// V is kv_step further), broadcast as two 32-bit halves with __shfl; then
+// every lane copies up to TPL chunks per round, K and V, loads first.
+template <typename V, int NKV, int TPL>
 __global__ __launch_bounds__(kBlock) void move_kernel(MoveArgs a) {
-    const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
-    if (w >= a.n * a.nl) return;
     const int lane = lane_id();
-    const int64_t i = w / a.nl;
-    const int32_t l = (int32_t)(w - i * a.nl);
-    const int32_t d = a.dst[i];
-    const int32_t s = a.src[i];
-    if (!kernel_facing(d, a.n_rows, a.page_stride, a.ps) || !kernel_facing(s, a.n_rows, a.page_stride, a.ps)) {
-        if (lane == 0 && l == 0) atomicOr(a.flags, UKV_FLAG_BAD_ID);
-        return;
+    const int64_t total = a.n * a.nl;
+    const int64_t u0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave_in_block()) * a.tile_units;
+    if (u0 >= total) return;
+    int64_t s_off = -1, d_off = -1;
+    bool bad = false;
+    if (lane < a.tile_units && u0 + lane < total) {
+        const int64_t u = u0 + lane;
+        const int64_t i = u / a.nl;
+        const int32_t l = (int32_t)(u - i * a.nl);
+        const int32_t d = a.dst[i];
+        const int32_t s = a.src[i];
+        if (kernel_facing(d, a.n_rows, a.page_stride, a.ps) && kernel_facing(s, a.n_rows, a.page_stride, a.ps)) {
+            const uint64_t layer_base = a.base0 + (uint64_t)l * a.layer_step;
+            s_off = (int64_t)(layer_base + (uint64_t)(uint32_t)s * a.row_bytes);
+            d_off = (int64_t)(layer_base + (uint64_t)(uint32_t)d * a.row_bytes);
+        } else {
+            bad = (l == 0);  // one report per pair
+        }
     }
-    uint8_t *layer_base = a.pool + a.base0 + (uint64_t)l * a.layer_step;
-    V *dst[NKV];
-    const V *src[NKV];
+    const int tasks = a.tile_units * a.vecs;
+    for (int base = 0; base < tasks; base += kWave * TPL) {
+        V buf[NKV][TPL];
+        int64_t dst_off[TPL];
+        int32_t cs[TPL];
 #pragma unroll
-    for (int h = 0; h < NKV; ++h) {
-        src[h] = reinterpret_cast<const V *>(layer_base + h * a.kv_step + (uint64_t)(uint32_t)s * a.row_bytes);
-        dst[h] = reinterpret_cast<V *>(layer_base + h * a.kv_step + (uint64_t)(uint32_t)d * a.row_bytes);
+        for (int j = 0; j < TPL; ++j) {
+            const int t = base + lane + j * kWave;
+            const int k = t / a.vecs;
+            const int c = t - k * a.vecs;
+            const int kk = k < kWave ? k : 0;
+            const uint32_t s_lo = (uint32_t)__shfl((int)(uint32_t)s_off, kk);
+            const uint32_t s_hi = (uint32_t)__shfl((int)(uint32_t)(s_off >> 32), kk);
+            const uint32_t d_lo = (uint32_t)__shfl((int)(uint32_t)d_off, kk);
+            const uint32_t d_hi = (uint32_t)__shfl((int)(uint32_t)(d_off >> 32), kk);
+            const int64_t so = (int64_t)(((uint64_t)s_hi << 32) | s_lo);
+            const int64_t dof = (int64_t)(((uint64_t)d_hi << 32) | d_lo);
+            dst_off[j] = (t < tasks && so >= 0) ? dof : -1;
+            cs[j] = c;
+            if (dst_off[j] >= 0) {
+#pragma unroll
+                for (int h = 0; h < NKV; ++h)
+                    buf[h][j] = reinterpret_cast<const V *>(a.pool + so + h * a.kv_step)[c];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) {
+            if (dst_off[j] >= 0) {
+#pragma unroll
+                for (int h = 0; h < NKV; ++h)
+                    put<true>(&reinterpret_cast<V *>(a.pool + dst_off[j] + h * a.kv_step)[cs[j]], buf[h][j]);
+            }
+        }
     }
-    copy_rows<V, NKV, 2, true>(dst, src, a.vecs, lane);
+    if (bad) atomicOr(a.flags, UKV_FLAG_BAD_ID);
 }
 
 __global__ void flags_fetch_clear_kernel(uint32_t *f) {
@@ -753,13 +770,13 @@ int ukv_store_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin, 
         using V = std::remove_pointer_t<decltype(tag)>;
         const dim3 g((unsigned)grid, (unsigned)layer_count), b(kBlock);
         if (nkv == 2 && tl.tpl == 8)
-            hipLaunchKernelGGL((store_kernel<V, 2, 8>), g, b, 0, stream, a);
+            hipLaunchKernelGGL((store_kernel<V, 2, 8, true>), g, b, 0, stream, a);
         else if (nkv == 2)
-            hipLaunchKernelGGL((store_kernel<V, 2, 4>), g, b, 0, stream, a);
+            hipLaunchKernelGGL((store_kernel<V, 2, 4, true>), g, b, 0, stream, a);
         else if (tl.tpl == 8)
-            hipLaunchKernelGGL((store_kernel<V, 1, 8>), g, b, 0, stream, a);
+            hipLaunchKernelGGL((store_kernel<V, 1, 8, true>), g, b, 0, stream, a);
         else
-            hipLaunchKernelGGL((store_kernel<V, 1, 4>), g, b, 0, stream, a);
+            hipLaunchKernelGGL((store_kernel<V, 1, 4, true>), g, b, 0, stream, a);
         return check_launch(who);
     };
     return dispatch_vec<2>(vb, launch);
@@ -867,9 +884,7 @@ int ukv_move_kv(const ukv_pool *pool, int32_t sub, const int32_t *dst_dev, const
     const int32_t nl = layer_end - layer_begin;
     if (n == 0 || nl == 0) return UKV_OK;
     if (dst_dev == nullptr || src_dev == nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: null dst or src", who);
-    const int64_t waves = n * (int64_t)nl;
-    const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n * layers too large for one launch", who);
+    const int64_t units = n * (int64_t)nl;
     const int nkv = s.kind == UKV_MHA ? 2 : 1;
     ukv_view v0;
     ukv::view_of(pool->plan, s, sub, layer_begin, 0, &v0);
@@ -890,12 +905,19 @@ int ukv_move_kv(const ukv_pool *pool, int32_t sub, const int32_t *dst_dev, const
     a.flags = pool->flags_dev;
     const int vb = vec_bytes_for({q.row_bytes, v0.byte_offset, a.kv_step, (uint64_t)(uintptr_t)pool->raw});
     a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
+    // units per tile: about 512 chunks of one view per tile, two rounds of 4 per lane
+    // (4 rows of 2 KiB; measured on MI355X against 1 and 2 units and 2 or 8 per lane)
+    const int64_t tu = (int64_t)2 * kWave * kTasksPerLane / a.vecs;
+    a.tile_units = (int32_t)(tu < 1 ? 1 : (tu > kWave ? kWave : tu));
+    const int64_t waves = (units + a.tile_units - 1) / a.tile_units;
+    const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n * layers too large for one launch", who);
     auto launch = [&](auto *tag) {
         using V = std::remove_pointer_t<decltype(tag)>;
         if (nkv == 2)
-            hipLaunchKernelGGL((move_kernel<V, 2>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+            hipLaunchKernelGGL((move_kernel<V, 2, kTasksPerLane>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
         else
-            hipLaunchKernelGGL((move_kernel<V, 1>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+            hipLaunchKernelGGL((move_kernel<V, 1, kTasksPerLane>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
         return check_launch(who);
     };
     return dispatch_vec<2>(vb, launch);
