@@ -194,6 +194,17 @@ int ukv_translate_pages_for_kernel(const ukv_pool *pool, int32_t sub, const int3
                                    const int32_t *v2p_dev, int64_t v2p_len, int32_t *out_dev, hipStream_t stream);
 
 /*
+ * Token slots -> internal physical slot ids (DKV multi_ended_allocator.py
+ * excerpt: compaction and the in-flight write set keep physical ids; only
+ * kernels see kernel-facing ids): phys * ps + t % ps with phys = v2p[t / ps]
+ * (identity when v2p_dev is NULL).  Tombstones (t < 0) and unmapped pages
+ * give -1; a page past the table or the pool gives -1 and raises
+ * UKV_FLAG_SLOT_RANGE.  slots_dev int64[n] -> out_dev int32[n] (no overlap).
+ */
+int ukv_translate_loc(const ukv_pool *pool, int32_t sub, const int64_t *slots_dev, int64_t n, const int32_t *v2p_dev,
+                      int64_t v2p_len, int32_t *out_dev, hipStream_t stream);
+
+/*
  * Per-layer scatter-store (DKV 关键文件, memory_pool.py: _store_kv_layer is a
  * plain 3-D row assignment): K_view[layer][ids[i]] = k[i] and
  * V_view[layer][ids[i]] = v[i], each a row_bytes byte copy.
@@ -268,6 +279,29 @@ int ukv_gather_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin,
  */
 int ukv_move_kv(const ukv_pool *pool, int32_t sub, const int32_t *dst_dev, const int32_t *src_dev, int64_t n,
                 int32_t layer_begin, int32_t layer_end, hipStream_t stream);
+
+/*
+ * Page relocation for compaction (DKV multi_ended_allocator.py excerpt and
+ * 关键文件: lazy compaction relocates KV with move_kv_cache, then rewrites
+ * the virtual-to-physical table): physical page src_pages[i] is copied to
+ * physical page dst_pages[i] on every layer, K and V.  A page's rows on all
+ * layers are one contiguous page envelope, so this is a copy of page_bytes
+ * per pair; it equals ukv_move_kv on the pages' kernel-facing row ids.
+ * dst_pages_dev, src_pages_dev: int32[n] in [0, num_pages) (a pair outside
+ * is skipped with UKV_FLAG_BAD_ID); the src and dst sets must be disjoint.
+ */
+int ukv_move_pages(const ukv_pool *pool, int32_t sub, const int32_t *dst_pages_dev, const int32_t *src_pages_dev,
+                   int64_t n, hipStream_t stream);
+
+/*
+ * Table rewrite after a relocation: v2p_dev[virt[i]] = phys[i] (-1 unmaps).
+ * v2p_dev: the caller's int32[v2p_len] virtual-to-physical table on the
+ * device; virt_pages_dev, phys_pages_dev: int32[n], virt distinct.  An entry
+ * with virt outside the table or phys outside [-1, num_pages) is skipped
+ * with UKV_FLAG_SLOT_RANGE.  The table may not overlap the page lists.
+ */
+int ukv_remap_pages(const ukv_pool *pool, int32_t sub, int32_t *v2p_dev, int64_t v2p_len,
+                    const int32_t *virt_pages_dev, const int32_t *phys_pages_dev, int64_t n, hipStream_t stream);
 
 /*
  * Reads and clears the pool's sticky flags (UKV_FLAG_*): enqueued on

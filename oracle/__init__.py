@@ -125,6 +125,12 @@ def lib() -> ctypes.CDLL:
         L.orc_move_map.argtypes = [ctypes.POINTER(_Pool), vp, vp, i64, ctypes.c_int, ctypes.c_int, vp, vp,
                                    ctypes.POINTER(ctypes.c_uint32)]
         L.orc_move_map.restype = None
+        L.orc_translate_loc.argtypes = [vp, i64, i64, i64, vp, i64, vp, ctypes.POINTER(ctypes.c_uint32)]
+        L.orc_translate_loc.restype = None
+        L.orc_move_pages.argtypes = [ctypes.POINTER(_Pool), vp, vp, i64, ctypes.POINTER(ctypes.c_uint32)]
+        L.orc_move_pages.restype = ctypes.c_int
+        L.orc_remap_pages.argtypes = [vp, i64, vp, vp, i64, i64, ctypes.POINTER(ctypes.c_uint32)]
+        L.orc_remap_pages.restype = None
         for fn in ("orc_sizeof_pool", "orc_sizeof_sub_plan", "orc_sizeof_spec"):
             getattr(L, fn).restype = ctypes.c_int
         assert L.orc_sizeof_pool() == ctypes.sizeof(_Pool)
@@ -273,6 +279,36 @@ class OraclePool:
     def translate_pages(self, sub: int, pages, v2p=None):
         s, sp = self.specs[sub], self.plan.subs[sub]
         return translate_pages(pages, self.page_size, sp.blocks_per_page, s.num_pages, v2p)
+
+    def translate_loc(self, sub: int, slots, v2p=None):
+        """Token slots -> internal physical slot ids (int32; -1 for tombstones / unmapped)."""
+        slots = np.ascontiguousarray(slots, dtype=np.int64)
+        out = np.empty(slots.shape, dtype=np.int32)
+        flags = ctypes.c_uint32(0)
+        v = None if v2p is None else np.ascontiguousarray(v2p, dtype=np.int32)
+        lib().orc_translate_loc(_ptr(slots), slots.size, self.page_size, self.specs[sub].num_pages, _ptr(v),
+                                0 if v is None else v.size, _ptr(out), ctypes.byref(flags))
+        return out, flag_names(flags.value)
+
+    def move_pages(self, sub: int, dst_pages, src_pages):
+        dst = np.ascontiguousarray(dst_pages, dtype=np.int32)
+        src = np.ascontiguousarray(src_pages, dtype=np.int32)
+        flags = ctypes.c_uint32(0)
+        pool = self._pool(sub)
+        rc = lib().orc_move_pages(ctypes.byref(pool), _ptr(dst), _ptr(src), dst.size, ctypes.byref(flags))
+        if rc != 0:
+            raise MemoryError("oracle page move")
+        return flag_names(flags.value)
+
+    def remap_pages(self, sub: int, v2p: np.ndarray, virt, phys):
+        """In place on the int32 table ``v2p``."""
+        assert v2p.dtype == np.int32 and v2p.flags.c_contiguous
+        virt = np.ascontiguousarray(virt, dtype=np.int32)
+        phys = np.ascontiguousarray(phys, dtype=np.int32)
+        flags = ctypes.c_uint32(0)
+        lib().orc_remap_pages(_ptr(v2p), v2p.size, _ptr(virt), _ptr(phys), virt.size, self.specs[sub].num_pages,
+                              ctypes.byref(flags))
+        return flag_names(flags.value)
 
     def store(self, sub: int, layer: int, ids, k: np.ndarray, v: Optional[np.ndarray]):
         """k, v: uint8 arrays of shape [n, row_bytes] (MLA: v is None)."""

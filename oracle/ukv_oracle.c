@@ -503,3 +503,93 @@ int orc_move(const orc_pool *p, const int32_t *dst, const int32_t *src, int64_t 
 int orc_sizeof_pool(void) { return (int)sizeof(orc_pool); }
 int orc_sizeof_sub_plan(void) { return (int)sizeof(orc_sub_plan); }
 int orc_sizeof_spec(void) { return (int)sizeof(orc_spec); }
+
+/*
+ * translate_kv_loc (DKV/alloc: the allocator's internal mechanisms, such as
+ * compaction and the in-flight write set, keep physical ids; kernel-facing
+ * ids are for kernels only).  READING: the internal id of slot t is the
+ * physical slot phys * ps + t % ps with phys = v2p[t / ps] (identity
+ * without a table); tombstones and unmapped pages stay -1 (internal
+ * bookkeeping must still see them), a page past the table or the pool gives
+ * -1 and raises ORC_F_SLOT_RANGE.
+ */
+void orc_translate_loc(const int64_t *slots, int64_t n, int64_t page_size, int64_t num_pages, const int32_t *v2p,
+                       int64_t v2p_len, int32_t *out, uint32_t *flags)
+{
+    for (int64_t i = 0; i < n; i++) {
+        int64_t t = slots[i];
+        out[i] = -1;
+        if (t < 0)
+            continue;
+        int64_t page = t / page_size;
+        int64_t phys = page;
+        if (v2p != NULL) {
+            if (page >= v2p_len) {
+                *flags |= ORC_F_SLOT_RANGE;
+                continue;
+            }
+            phys = v2p[page];
+        }
+        if (phys < 0)
+            continue;
+        if (phys >= num_pages) {
+            *flags |= ORC_F_SLOT_RANGE;
+            continue;
+        }
+        out[i] = (int32_t)(phys * page_size + t % page_size);
+    }
+}
+
+/*
+ * Page relocation for compaction (DKV 关键文件 and alloc: lazy compaction moves
+ * KV through move_kv_cache and rewrites the virtual-to-physical table).
+ * READING: moving physical page s to physical page d is the row move of all
+ * ps slots of page s to page d on every layer, K and V; here it is stated
+ * exactly that way, through orc_move on the pages' kernel-facing row ids.
+ * Pages must lie in [0, num_pages) (else ORC_F_BAD_ID, pair skipped).
+ */
+int orc_move_pages(const orc_pool *p, const int32_t *dst_pages, const int32_t *src_pages, int64_t n, uint32_t *flags)
+{
+    int64_t ps = p->page_size;
+    int64_t bpp = (int64_t)p->sp.blocks_per_page;
+    int32_t *d = (int32_t *)malloc((size_t)(n > 0 ? n * ps : 1) * sizeof(int32_t));
+    int32_t *s = (int32_t *)malloc((size_t)(n > 0 ? n * ps : 1) * sizeof(int32_t));
+    if (d == NULL || s == NULL) {
+        free(d);
+        free(s);
+        return ORC_INVALID;
+    }
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; i++) {
+        if (dst_pages[i] < 0 || dst_pages[i] >= p->num_pages || src_pages[i] < 0 || src_pages[i] >= p->num_pages) {
+            *flags |= ORC_F_BAD_ID;
+            continue;
+        }
+        for (int64_t o = 0; o < ps; o++) {
+            d[m] = (int32_t)orc_kernel_id((int64_t)dst_pages[i] * ps + o, ps, bpp);
+            s[m] = (int32_t)orc_kernel_id((int64_t)src_pages[i] * ps + o, ps, bpp);
+            m++;
+        }
+    }
+    int rc = orc_move(p, d, s, m, 0, p->layer_num, flags);
+    free(d);
+    free(s);
+    return rc;
+}
+
+/*
+ * Table rewrite after a relocation: v2p[virt[i]] = phys[i], in entry order.
+ * virt past the table or phys outside [-1, num_pages) raise ORC_F_SLOT_RANGE
+ * and the entry is skipped (-1 unmaps a virtual page).
+ */
+void orc_remap_pages(int32_t *v2p, int64_t v2p_len, const int32_t *virt, const int32_t *phys, int64_t n,
+                     int64_t num_pages, uint32_t *flags)
+{
+    for (int64_t i = 0; i < n; i++) {
+        if (virt[i] < 0 || virt[i] >= v2p_len || phys[i] < -1 || phys[i] >= num_pages) {
+            *flags |= ORC_F_SLOT_RANGE;
+            continue;
+        }
+        v2p[virt[i]] = phys[i];
+    }
+}

@@ -41,7 +41,7 @@ EXPORTS = (
     "ukv_pool_plan", "ukv_pool_create", "ukv_pool_destroy", "ukv_pool_get_plan", "ukv_pool_view", "ukv_plan_view",
     "ukv_translate_loc_for_kernel", "ukv_translate_pages_for_kernel", "ukv_store_kv", "ukv_store_kv_layers",
     "ukv_gather_kv", "ukv_gather_kv_layers", "ukv_move_kv", "ukv_pool_error_flags", "ukv_last_error",
-    "ukv_status_name",
+    "ukv_status_name", "ukv_translate_loc", "ukv_move_pages", "ukv_remap_pages",
 )
 
 
@@ -107,6 +107,9 @@ def _load() -> ctypes.CDLL:
         "ukv_gather_kv_layers": [vp, i32, i32, i32, i32, vp, i64, vp, vp, i32, i32, vp, vp, i64, i64, vp],
         "ukv_move_kv": [vp, i32, vp, vp, i64, i32, i32, vp],
         "ukv_pool_error_flags": [vp, vp, P(ctypes.c_uint32)],
+        "ukv_translate_loc": [vp, i32, vp, i64, vp, i64, vp, vp],
+        "ukv_move_pages": [vp, i32, vp, vp, i64, vp],
+        "ukv_remap_pages": [vp, i32, vp, i64, vp, vp, i64, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -414,6 +417,49 @@ def ukv_move_kv(pool: Pool, sub: int, dst: torch.Tensor, src: torch.Tensor, laye
                             int(layer_end), _stream_handle(stream)))
 
 
+def ukv_translate_loc(pool: Pool, sub: int, slots: torch.Tensor, v2p: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """int64 token slots -> int32 internal physical slot ids (-1: tombstone / unmapped)."""
+    d = pool.device
+    _dev_ptr(slots, "slots", d, torch.int64)
+    if not slots.is_contiguous():
+        raise ValueError("slots must be contiguous")
+    if out is None:
+        out = torch.empty(slots.shape, dtype=torch.int32, device=d)
+    _dev_ptr(out, "out", d, torch.int32)
+    if out.numel() != slots.numel() or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 tensor of slots' size")
+    vp = _dev_ptr(v2p, "v2p", d, torch.int32)
+    _check(_lib.ukv_translate_loc(pool.handle, sub, slots.data_ptr(), slots.numel(), vp,
+                                  0 if v2p is None else v2p.numel(), out.data_ptr(), _stream_handle(stream)))
+    return out
+
+
+def ukv_move_pages(pool: Pool, sub: int, dst_pages: torch.Tensor, src_pages: torch.Tensor, stream=None) -> None:
+    """Relocate whole physical pages (every layer, K and V): page src[i] -> page dst[i]."""
+    d = pool.device
+    _dev_ptr(dst_pages, "dst_pages", d, torch.int32)
+    _dev_ptr(src_pages, "src_pages", d, torch.int32)
+    if dst_pages.numel() != src_pages.numel() or not (dst_pages.is_contiguous() and src_pages.is_contiguous()):
+        raise ValueError("dst_pages and src_pages must be contiguous and of one size")
+    _check(_lib.ukv_move_pages(pool.handle, sub, dst_pages.data_ptr(), src_pages.data_ptr(), dst_pages.numel(),
+                               _stream_handle(stream)))
+
+
+def ukv_remap_pages(pool: Pool, sub: int, v2p: torch.Tensor, virt_pages: torch.Tensor, phys_pages: torch.Tensor,
+                    stream=None) -> None:
+    """v2p[virt[i]] = phys[i] on the device (in place)."""
+    d = pool.device
+    for name, t in (("v2p", v2p), ("virt_pages", virt_pages), ("phys_pages", phys_pages)):
+        _dev_ptr(t, name, d, torch.int32)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if virt_pages.numel() != phys_pages.numel():
+        raise ValueError("virt_pages and phys_pages differ in size")
+    _check(_lib.ukv_remap_pages(pool.handle, sub, v2p.data_ptr(), v2p.numel(), virt_pages.data_ptr(),
+                                phys_pages.data_ptr(), virt_pages.numel(), _stream_handle(stream)))
+
+
 def ukv_pool_error_flags(pool: Pool, stream=None) -> frozenset:
     """Read and clear the pool's sticky flags (synchronises the stream)."""
     out = ctypes.c_uint32(0)
@@ -426,5 +472,5 @@ __all__ = [
     "plan_status", "ukv_pool_create", "allocate_pool", "ukv_pool_destroy", "ukv_pool_view", "ukv_plan_view", "dense_view",
     "ukv_translate_loc_for_kernel", "ukv_translate_pages_for_kernel", "ukv_store_kv", "ukv_store_kv_layers",
     "ukv_gather_kv", "ukv_gather_kv_layers", "ukv_move_kv", "ukv_pool_error_flags", "ukv_last_error", "EXPORTS",
-    "STATUS", "FLAGS",
+    "STATUS", "FLAGS", "ukv_translate_loc", "ukv_move_pages", "ukv_remap_pages",
 ]

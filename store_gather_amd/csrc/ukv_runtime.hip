@@ -112,6 +112,7 @@ struct TranslateArgs {
     int64_t page_stride;  // ps * blocks_per_page
     int64_t bpp;
     int64_t num_pages;
+    int32_t internal;  // 1: physical slot ids (translate_kv_loc), tombstones stay -1
 };
 
 // slot t -> id: tombstone (t < 0) -> 0; page = t / ps, offset = t % ps;
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kBlock) void translate_slots_kernel(TranslateArgs a
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i >= a.n) return;
     const int64_t t = a.slots[i];
-    int32_t id = 0;
+    int32_t id = a.internal ? -1 : 0;
     bool out_of_range = false;
     if (t >= 0) {
         const int64_t page = t / a.ps;
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(kBlock) void translate_slots_kernel(TranslateArgs a
         if (phys >= a.num_pages) {
             out_of_range = true;
         } else if (phys >= 0) {
-            id = (int32_t)(phys * a.page_stride + offset);
+            id = (int32_t)(phys * (a.internal ? a.ps : a.page_stride) + offset);
         }
     }
     a.out[i] = id;
@@ -479,6 +480,70 @@ __global__ __launch_bounds__(kBlock) void move_kernel(MoveArgs a) {
     if (bad) atomicOr(a.flags, UKV_FLAG_BAD_ID);
 }
 
+// ----------------------------------------------------------------------------
+// page relocation and table rewrite (compaction: DKV alloc excerpt and 关键文件)
+// ----------------------------------------------------------------------------
+struct PageMoveArgs {
+    uint8_t *pool;
+    uint64_t anchor;
+    uint64_t page_bytes;
+    const int32_t *dst;
+    const int32_t *src;
+    int64_t n;
+    int64_t num_pages;
+    int64_t vecs;       // page_bytes / sizeof(V)
+    int64_t segs;       // segments per page
+    uint32_t *flags;
+};
+
+// A page's rows on every layer, K and V, are one contiguous envelope, so a
+// page relocation is a straight copy of page_bytes.  One wave per
+// (pair, 64 * TPL-chunk segment); the pair index is wave-uniform.
+template <typename V, int TPL>
+__global__ __launch_bounds__(kBlock) void move_pages_kernel(PageMoveArgs a) {
+    const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int64_t pair = w / a.segs;
+    if (pair >= a.n) return;
+    const int64_t seg = w - pair * a.segs;
+    const int lane = lane_id();
+    const int32_t d = a.dst[pair];
+    const int32_t s = a.src[pair];
+    if (d < 0 || d >= a.num_pages || s < 0 || s >= a.num_pages) {
+        if (lane == 0 && seg == 0) atomicOr(a.flags, UKV_FLAG_BAD_ID);
+        return;
+    }
+    const V *src = reinterpret_cast<const V *>(a.pool + a.anchor + (uint64_t)s * a.page_bytes);
+    V *dst = reinterpret_cast<V *>(a.pool + a.anchor + (uint64_t)d * a.page_bytes);
+    const int64_t c0 = seg * (int64_t)(kWave * TPL) + lane;
+    V buf[TPL];
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) {
+        const int64_t c = c0 + (int64_t)j * kWave;
+        if (c < a.vecs) buf[j] = src[c];
+    }
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) {
+        const int64_t c = c0 + (int64_t)j * kWave;
+        if (c < a.vecs) put<true>(&dst[c], buf[j]);
+    }
+}
+
+// v2p[virt[i]] = phys[i]; virt past the table or phys outside [-1, num_pages)
+// skip the entry and raise UKV_FLAG_SLOT_RANGE.
+__global__ __launch_bounds__(kBlock) void remap_pages_kernel(int32_t *v2p, int64_t v2p_len, const int32_t *virt,
+                                                            const int32_t *phys, int64_t n, int64_t num_pages,
+                                                            uint32_t *flags) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= n) return;
+    const int32_t v = virt[i];
+    const int32_t p = phys[i];
+    if (v < 0 || v >= v2p_len || p < -1 || p >= num_pages) {
+        atomicOr(flags, UKV_FLAG_SLOT_RANGE);
+        return;
+    }
+    v2p[v] = p;
+}
+
 __global__ void flags_fetch_clear_kernel(uint32_t *f) {
     if (threadIdx.x == 0) f[1] = atomicExch(&f[0], 0u);
 }
@@ -654,7 +719,7 @@ int ukv_plan_view(const ukv_plan *plan, const ukv_subpool_spec *specs, int32_t s
 
 static int translate_common(const ukv_pool *pool, int32_t sub, const void *in, uint64_t in_elem, int64_t n,
                             const int32_t *v2p, int64_t v2p_len, int32_t *out, hipStream_t stream, bool pages,
-                            const char *who) {
+                            const char *who, bool internal = false) {
     int rc = check_pool_call(pool, sub, who);
     if (rc != UKV_OK) return rc;
     if (n < 0 || n > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n=%lld outside [0, 2^31)", who, (long long)n);
@@ -679,6 +744,7 @@ static int translate_common(const ukv_pool *pool, int32_t sub, const void *in, u
     a.bpp = q.blocks_per_page;
     a.page_stride = pool->plan.page_size * q.blocks_per_page;
     a.num_pages = s.num_pages;
+    a.internal = internal ? 1 : 0;
     const unsigned grid = (unsigned)((n + kBlock - 1) / kBlock);
     if (pages)
         hipLaunchKernelGGL(translate_pages_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
@@ -691,6 +757,12 @@ int ukv_translate_loc_for_kernel(const ukv_pool *pool, int32_t sub, const int64_
                                  const int32_t *v2p_dev, int64_t v2p_len, int32_t *out_dev, hipStream_t stream) {
     return translate_common(pool, sub, slots_dev, sizeof(int64_t), n, v2p_dev, v2p_len, out_dev, stream, false,
                             "ukv_translate_loc_for_kernel");
+}
+
+int ukv_translate_loc(const ukv_pool *pool, int32_t sub, const int64_t *slots_dev, int64_t n, const int32_t *v2p_dev,
+                      int64_t v2p_len, int32_t *out_dev, hipStream_t stream) {
+    return translate_common(pool, sub, slots_dev, sizeof(int64_t), n, v2p_dev, v2p_len, out_dev, stream, false,
+                            "ukv_translate_loc", true);
 }
 
 int ukv_translate_pages_for_kernel(const ukv_pool *pool, int32_t sub, const int32_t *pages_dev, int64_t n,
@@ -921,6 +993,61 @@ int ukv_move_kv(const ukv_pool *pool, int32_t sub, const int32_t *dst_dev, const
         return check_launch(who);
     };
     return dispatch_vec<2>(vb, launch);
+}
+
+int ukv_move_pages(const ukv_pool *pool, int32_t sub, const int32_t *dst_pages_dev, const int32_t *src_pages_dev,
+                   int64_t n, hipStream_t stream) {
+    const char *who = "ukv_move_pages";
+    int rc = check_pool_call(pool, sub, who);
+    if (rc != UKV_OK) return rc;
+    if (n < 0 || n > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n=%lld outside [0, 2^31)", who, (long long)n);
+    if (n == 0) return UKV_OK;
+    if (dst_pages_dev == nullptr || src_pages_dev == nullptr)
+        return fail(UKV_ERR_INVALID_ARG, "%s: null dst or src", who);
+    const ukv_subpool_plan &q = pool->plan.sub[sub];
+    PageMoveArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.pool = pool->raw;
+    a.anchor = q.anchor_bytes;
+    a.page_bytes = q.page_bytes;
+    a.dst = dst_pages_dev;
+    a.src = src_pages_dev;
+    a.n = n;
+    a.num_pages = pool->spec[sub].num_pages;
+    a.flags = pool->flags_dev;
+    const int vb = vec_bytes_for({q.page_bytes, q.anchor_bytes, (uint64_t)(uintptr_t)pool->raw});
+    constexpr int kTpl = 8;
+    a.vecs = (int64_t)(q.page_bytes / (uint64_t)vb);
+    a.segs = (a.vecs + kWave * kTpl - 1) / (kWave * kTpl);
+    const int64_t waves = n * a.segs;
+    const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n pages too large for one launch", who);
+    auto launch = [&](auto *tag) {
+        using V = std::remove_pointer_t<decltype(tag)>;
+        hipLaunchKernelGGL((move_pages_kernel<V, kTpl>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        return check_launch(who);
+    };
+    return dispatch_vec<1>(vb, launch);
+}
+
+int ukv_remap_pages(const ukv_pool *pool, int32_t sub, int32_t *v2p_dev, int64_t v2p_len,
+                    const int32_t *virt_pages_dev, const int32_t *phys_pages_dev, int64_t n, hipStream_t stream) {
+    const char *who = "ukv_remap_pages";
+    int rc = check_pool_call(pool, sub, who);
+    if (rc != UKV_OK) return rc;
+    if (n < 0 || n > kMaxGrid || v2p_len < 0)
+        return fail(UKV_ERR_INVALID_ARG, "%s: n=%lld or v2p_len=%lld out of range", who, (long long)n,
+                    (long long)v2p_len);
+    if (n == 0) return UKV_OK;
+    if (v2p_dev == nullptr || virt_pages_dev == nullptr || phys_pages_dev == nullptr)
+        return fail(UKV_ERR_INVALID_ARG, "%s: null table or pages", who);
+    if (ranges_overlap(v2p_dev, (uint64_t)v2p_len * 4, virt_pages_dev, (uint64_t)n * 4) ||
+        ranges_overlap(v2p_dev, (uint64_t)v2p_len * 4, phys_pages_dev, (uint64_t)n * 4))
+        return fail(UKV_ERR_INVALID_ARG, "%s: the table overlaps the page lists", who);
+    const unsigned grid = (unsigned)((n + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL(remap_pages_kernel, dim3(grid), dim3(kBlock), 0, stream, v2p_dev, v2p_len, virt_pages_dev,
+                       phys_pages_dev, n, (int64_t)pool->spec[sub].num_pages, pool->flags_dev);
+    return check_launch(who);
 }
 
 int ukv_pool_error_flags(ukv_pool *pool, hipStream_t stream, uint32_t *out_and_clear) {

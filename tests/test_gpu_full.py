@@ -245,3 +245,51 @@ def test_full_bound_rejected_without_allocation():
     assert U.plan_status([W.mha(80, 8, 128, 838861)], 16) == "UKV_ERR_KERNEL_ID_BOUND"
     assert U.plan_status([W.mha(80, 8, 128, 838860)], 16) == "UKV_OK"
     assert torch.cuda.memory_allocated() == before
+
+
+def test_full_compaction_prefill_8b():
+    """32 GiB pool; the 16 requests' pages (scattered over 16,383) are relocated below the
+    watermark (whole page envelopes, all 32 layers, K and V) and the table rewritten; every
+    gathered row is the same before and after, and only destination pages change."""
+    w = W.prefill_8b(move_rows=0)
+    pool, orc = _make(w)
+    P, ps = w.shapes[0].num_pages, w.page_size
+    used = np.unique(np.concatenate(w.req_pages[0]))
+    v2p = used.astype(np.int32).copy()
+    vpages = [np.searchsorted(used, p).astype(np.int32) for p in w.req_pages[0]]
+    lens = w.req_lens[0]
+    v2p_d = _dev(v2p)
+    table = W.padded_table(vpages)
+    cu = W.out_offsets(lens)
+    rows = int(cu[-1])
+    anchor, env, rb = _sub_geom(pool, 0)
+
+    def read():
+        bt = U.ukv_translate_pages_for_kernel(pool, 0, _dev(table), v2p=v2p_d)
+        ko = torch.empty((32, rows, rb), dtype=torch.uint8, device="cuda")
+        vo = torch.empty_like(ko)
+        U.ukv_gather_kv_layers(pool, 0, 0, 32, bt, _dev(lens), _dev(cu), 0, ko, vo)
+        return ko, vo
+
+    before = read()
+    src, dst = W.compaction_plan(used, P)
+    log(f"  relocating {src.size} pages ({src.size * pool.plan.sub[0].page_bytes / 1e9:.2f} GB)")
+    snap = pool.raw.clone()
+    U.ukv_move_pages(pool, 0, _dev(dst), _dev(src))
+    U.ukv_remap_pages(pool, 0, v2p_d, _dev(np.searchsorted(used, src).astype(np.int32)), _dev(dst))
+    after = read()
+    assert torch.equal(before[0], after[0]) and torch.equal(before[1], after[1])
+    pb = int(pool.plan.sub[0].page_bytes)
+    pages_now = pool.raw[anchor: anchor + env].view(P, pb)
+    pages_then = snap[anchor: anchor + env].view(P, pb)
+    d_t, s_t = _dev(dst.astype(np.int64)), _dev(src.astype(np.int64))
+    assert torch.equal(pages_now.index_select(0, d_t), pages_then.index_select(0, s_t))
+    changed = (pages_now != pages_then).any(dim=1).nonzero().flatten()
+    allowed = torch.zeros(P, dtype=torch.bool, device="cuda")
+    allowed[d_t] = True
+    assert_rows_subset(changed, allowed, "page move")
+    v2p_exp = v2p.copy()
+    orc.remap_pages(0, v2p_exp, np.searchsorted(used, src).astype(np.int32), dst)
+    assert np.array_equal(v2p_d.cpu().numpy(), v2p_exp)
+    assert U.ukv_pool_error_flags(pool) == frozenset()
+    del snap

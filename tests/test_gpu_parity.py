@@ -473,3 +473,86 @@ def test_fused_layers_mla_and_argument_errors():
     with pytest.raises(U.UkvError):
         U.ukv_store_kv_layers(pair.gpu, 1, 20, 5, ids_d, to_dev(lat[:5]))
     assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+
+
+# ---------------------------------------------------------------------------
+# virtual-to-physical indirection and compaction
+# ---------------------------------------------------------------------------
+
+def test_translate_loc_parity():
+    pair = Pair([W.mha(4, 2, 8, 30)], 8)
+    g = np.random.default_rng(12)
+    slots = g.integers(-3, 40 * 8, size=2000).astype(np.int64)
+    v2p = g.integers(-2, 33, size=37).astype(np.int32)
+    for table in (None, v2p):
+        got = U.ukv_translate_loc(pair.gpu, 0, to_dev(slots), v2p=None if table is None else to_dev(table))
+        exp, ef = pair.orc.translate_loc(0, slots, table)
+        assert np.array_equal(got.cpu().numpy(), exp)
+        assert U.ukv_pool_error_flags(pair.gpu) == ef
+
+
+def test_move_pages_and_remap_parity():
+    pair = Pair([W.mha(3, 2, 16, 12), W.mla(5, 9, latent_dim=24)], 4)
+    for sub, (dst, src) in ((0, ([1, 2, 11], [7, 4, 5])), (1, ([3, 8], [1, 6]))):
+        U.ukv_move_pages(pair.gpu, sub, to_dev(np.array(dst, np.int32)), to_dev(np.array(src, np.int32)))
+        assert pair.orc.move_pages(sub, dst, src) == frozenset()
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    pair.assert_pools_equal()
+    U.ukv_move_pages(pair.gpu, 0, to_dev(np.array([12, 3], np.int32)), to_dev(np.array([2, 3], np.int32)))
+    assert pair.orc.move_pages(0, [12, 3], [2, 3]) == {"bad_id"}
+    assert U.ukv_pool_error_flags(pair.gpu) == {"bad_id"}
+    pair.assert_pools_equal()
+    v2p = np.arange(20, dtype=np.int32)
+    vd = to_dev(v2p)
+    virt = np.array([3, 19, 25, 0, 7], np.int32)
+    phys = np.array([11, -1, 2, 12, -2], np.int32)
+    U.ukv_remap_pages(pair.gpu, 0, vd, to_dev(virt), to_dev(phys))
+    assert pair.orc.remap_pages(0, v2p, virt, phys) == {"slot_range"}
+    assert U.ukv_pool_error_flags(pair.gpu) == {"slot_range"}
+    assert np.array_equal(vd.cpu().numpy(), v2p)
+
+
+def test_compaction_end_to_end():
+    """Requests written through a virtual-to-physical table; the pages above the watermark are
+    relocated below it and the table rewritten; every request reads the same K/V after."""
+    w = W.prefill_8b(num_pages=160, tokens=1500, num_reqs=6, move_rows=0, layer_num=6)
+    pair = Pair(w.shapes, w.page_size)
+    P, ps, rb = w.shapes[0].num_pages, w.page_size, pair.rb(0)
+    used = np.unique(np.concatenate(w.req_pages[0]))
+    v2p = used.astype(np.int32).copy()
+    vpages = [np.searchsorted(used, p).astype(np.int32) for p in w.req_pages[0]]
+    lens = w.req_lens[0]
+    vslots = W.slots_of_requests(vpages, lens, ps)
+    v2p_d = to_dev(v2p)
+    ids_d = U.ukv_translate_loc_for_kernel(pair.gpu, 0, to_dev(vslots), v2p=v2p_d)
+    ids, _ = pair.orc.translate(0, vslots, v2p)
+    assert np.array_equal(ids_d.cpu().numpy(), ids)
+    internal = U.ukv_translate_loc(pair.gpu, 0, to_dev(vslots), v2p=v2p_d)
+    assert np.array_equal(internal.cpu().numpy(), W.slots_of_requests(w.req_pages[0], lens, ps))
+    for layer in range(6):
+        k = bf16_rows(300 + layer, vslots.size, rb)
+        v = bf16_rows(400 + layer, vslots.size, rb)
+        U.ukv_store_kv(pair.gpu, 0, layer, ids_d, rows_dev(k), rows_dev(v))
+        pair.orc.store(0, layer, ids, k, v)
+    table = W.padded_table(vpages)
+    cu = W.out_offsets(lens)
+
+    def read(vt):
+        bt = U.ukv_translate_pages_for_kernel(pair.gpu, 0, to_dev(table), v2p=vt)
+        ko = torch.empty((6, int(cu[-1]), rb), dtype=torch.uint8, device="cuda")
+        vo = torch.empty_like(ko)
+        U.ukv_gather_kv_layers(pair.gpu, 0, 0, 6, bt, to_dev(lens), to_dev(cu), 0, ko, vo)
+        return ko.cpu().numpy(), vo.cpu().numpy()
+
+    before = read(v2p_d)
+    src, dst = W.compaction_plan(used, P)
+    assert src.size > 10
+    U.ukv_move_pages(pair.gpu, 0, to_dev(dst), to_dev(src))
+    U.ukv_remap_pages(pair.gpu, 0, v2p_d, to_dev(np.searchsorted(used, src).astype(np.int32)), to_dev(dst))
+    pair.orc.move_pages(0, dst, src)
+    pair.orc.remap_pages(0, v2p, np.searchsorted(used, src).astype(np.int32), dst)
+    assert np.array_equal(v2p_d.cpu().numpy(), v2p) and v2p.max() <= used.size
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    pair.assert_pools_equal()
+    after = read(v2p_d)
+    assert np.array_equal(before[0], after[0]) and np.array_equal(before[1], after[1])

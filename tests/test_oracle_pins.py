@@ -481,3 +481,81 @@ def test_address_maps_match_strided_reference_and_need_no_buffer():
                     assert d_off[at] == ref.row_address(layer, kv, *divmod(int(mv[5 + i]), w.page_size))
                     at += 1
         assert at == d_off.size
+
+
+# ---------------------------------------------------------------------------
+# virtual-to-physical indirection and compaction
+# ---------------------------------------------------------------------------
+
+def test_translate_loc_is_the_physical_slot_behind_every_kernel_id():
+    ps, L, P = 4, 3, 9
+    pool = oracle.OraclePool([make_spec(MHA, L, P, 2, 8, 2)], ps)
+    bpp = 2 * L
+    v2p = np.array([5, -1, 2, 8, 0, 11], dtype=np.int32)  # 11 is past the pool
+    slots = np.arange(-2, 6 * ps + 3, dtype=np.int64)
+    internal, f_int = pool.translate_loc(0, slots, v2p)
+    kernel, f_ker = pool.translate(0, slots, v2p)
+    assert f_int == f_ker == {"slot_range"}
+    for t, i, k in zip(slots, internal, kernel):
+        if i >= 0:
+            assert oracle.kernel_id(int(i), ps, bpp) == k
+        else:
+            assert k == 0  # tombstone, unmapped or out of range: the kernel id is the sink
+    assert internal[slots == -1][0] == -1
+    ident, _ = pool.translate_loc(0, np.arange(P * ps))
+    assert ident.tolist() == list(range(P * ps))
+
+
+def test_page_move_copies_whole_envelopes():
+    """A page's rows on every layer, K and V, are one contiguous envelope (the walk):
+    moving page s to d copies exactly those bytes and nothing else."""
+    shapes = [W.mha(3, 2, 8, 7), W.mla(2, 5, latent_dim=16)]
+    pool, raw = _filled_pool(shapes, 4)
+    orig = raw.copy()
+    for sub in (0, 1):
+        sp = pool.plan.subs[sub]
+        assert pool.move_pages(sub, [1, 6 if sub == 0 else 4], [3, 2]) == frozenset()
+        for d, s in ((1, 3), (6 if sub == 0 else 4, 2)):
+            a_d = sp.anchor_bytes + d * sp.page_bytes
+            a_s = sp.anchor_bytes + s * sp.page_bytes
+            assert np.array_equal(raw[a_d:a_d + sp.page_bytes], orig[a_s:a_s + sp.page_bytes])
+            orig[a_d:a_d + sp.page_bytes] = orig[a_s:a_s + sp.page_bytes]
+    assert np.array_equal(raw, orig)
+    assert pool.move_pages(0, [7], [1]) == {"bad_id"}
+    assert np.array_equal(raw, orig)
+
+
+def test_compaction_preserves_what_requests_read():
+    """Relocate the pages above a watermark into free pages below it, rewrite the table:
+    every request gathers the same rows through the new table as through the old."""
+    w = W.prefill_8b(num_pages=40, tokens=300, num_reqs=3, move_rows=0, layer_num=2)
+    pool, raw = _filled_pool(w.shapes, w.page_size)
+    P = w.shapes[0].num_pages
+    pages = w.req_pages[0]
+    lens = w.req_lens[0]
+    used = np.unique(np.concatenate(pages))
+    # virtual page v of the batch = its index in `used`; the table maps it to its physical page
+    v2p = used.astype(np.int32).copy()
+    vpages = [np.searchsorted(used, p).astype(np.int32) for p in pages]
+    table = W.padded_table(vpages)
+    cu = W.out_offsets(lens)
+
+    def read_all():
+        bt, _ = pool.translate_pages(0, table, v2p)
+        out = []
+        for layer in range(2):
+            ko = np.zeros((int(cu[-1]), pool.row_bytes(0)), np.uint8)
+            vo = np.zeros_like(ko)
+            assert pool.gather(0, layer, bt, lens, cu, 0, ko, vo) == frozenset()
+            out += [ko, vo]
+        return out
+
+    before = read_all()
+    plan = W.compaction_plan(used, P)
+    assert len(plan[0]) > 0
+    assert pool.move_pages(0, plan[1], plan[0]) == frozenset()
+    virt = np.searchsorted(used, plan[0]).astype(np.int32)
+    assert pool.remap_pages(0, v2p, virt, plan[1]) == frozenset()
+    assert v2p.max() < len(used) + 1  # every live page now sits below the watermark
+    after = read_all()
+    assert all(np.array_equal(a, b) for a, b in zip(before, after))

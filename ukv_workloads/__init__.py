@@ -215,6 +215,18 @@ def out_offsets(lens: Sequence[int], window: int = 0) -> np.ndarray:
     return np.concatenate([[0], np.cumsum(kept)]).astype(np.int64)
 
 
+def compaction_plan(live_pages, num_pages: int):
+    """An allocator's compaction choice: live pages above the watermark (the live count,
+    counting the sink page 0) move into the free pages below it, lowest first.
+    Returns (src_pages, dst_pages) as int32 arrays."""
+    live = np.unique(np.asarray(live_pages, dtype=np.int64))
+    mark = live.size + 1  # pages [1, mark) can hold every live page
+    src = live[live >= mark]
+    free_low = np.setdiff1d(np.arange(1, mark), live)
+    assert free_low.size >= src.size
+    return src.astype(np.int32), free_low[: src.size].astype(np.int32)
+
+
 # ----------------------------------------------------------------------------
 # The five workloads
 # ----------------------------------------------------------------------------
@@ -378,5 +390,5 @@ __all__ = [
     "splitmix64", "fill_pattern_host", "fill_pattern_device", "f32_to_bf16_bits", "normal_bf16_host",
     "normal_bf16_device", "SubPoolShape", "mha", "mla", "rng", "live_slots", "page_permutation",
     "slots_of_requests", "padded_table", "out_offsets", "Workload", "tiny_mha", "decode_8b",
-    "dirichlet_lengths", "prefill_8b", "hybrid", "move_70b", "MHA", "MLA",
+    "dirichlet_lengths", "prefill_8b", "hybrid", "move_70b", "compaction_plan", "MHA", "MLA",
 ]
