@@ -42,7 +42,8 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "KV store/gather/move HBM GB/s and % of peak, Llama-3-8B-shape pool"
 KERNEL_SRC = os.path.join(ROOT, "store_gather_amd", "csrc", "ukv_runtime.hip")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-WORKLOADS = ("decode_8b", "prefill_8b", "hybrid", "move_70b", "tiny", "decode_8b_fused", "prefill_8b_fused")
+WORKLOADS = ("decode_8b", "prefill_8b", "hybrid", "move_70b", "tiny", "decode_8b_fused", "prefill_8b_fused",
+             "compact_8b")
 
 
 def log(msg):
@@ -133,12 +134,18 @@ DESCRIPTIONS = {
                        "launch (ukv_store_kv_layers), then the per-layer gathers",
     "prefill_8b_fused": "prefill_8b_fused: the prefill_8b batch with all 32 layers stored in one launch and gathered "
                         "back in one launch (ukv_store_kv_layers / ukv_gather_kv_layers), then the move",
+    "compact_8b": "compact_8b: the prefill_8b pool (16,384 pages of 2 MiB) with its 16 requests addressed through a "
+                  "virtual-to-physical table; per step: internal ids of the batch (translate_loc), relocation of every "
+                  "live page above the watermark into the free pages below it (whole page envelopes, all 32 layers, "
+                  "K and V), the table rewrite, and the block table through the new table",
 }
 
 
 def build_script(name: str, W, reduced: bool = False) -> Script:
     """The step of workload `name`.  `reduced` shrinks the pools (same row and page geometry,
     envelopes of at most ~8 GiB) for the CPU-oracle sample."""
+    if name == "compact_8b":
+        return compaction_script(W, reduced)
     if name.endswith("_fused"):
         return fuse_layers(build_script(name[: -len("_fused")], W, reduced), name,
                            gathers=name.startswith("prefill"))
@@ -249,6 +256,36 @@ def build_script(name: str, W, reduced: bool = False) -> Script:
     return Script(name, DESCRIPTIONS[name], list(w.shapes), ps, arrays, buffers, ops, roof[0], roof[1], counts)
 
 
+def compaction_script(W, reduced: bool) -> Script:
+    w = W.prefill_8b(num_pages=4096, move_rows=0) if reduced else W.prefill_8b(move_rows=0)
+    ps = w.page_size
+    shape = w.shapes[0]
+    P = shape.num_pages
+    used = np.unique(np.concatenate(w.req_pages[0]))
+    vpages = [np.searchsorted(used, p).astype(np.int32) for p in w.req_pages[0]]
+    src, dst = W.compaction_plan(used, P)
+    arrays = {
+        "vslots0": W.slots_of_requests(vpages, w.req_lens[0], ps).astype(np.int64),
+        "v2p0": used.astype(np.int32),
+        "psrc0": src,
+        "pdst0": dst,
+        "pvirt0": np.searchsorted(used, src).astype(np.int32),
+        "table0": W.padded_table(vpages),
+    }
+    page_bytes = ps * 2 * shape.layer_num * shape.row_bytes
+    n, m, t = arrays["vslots0"].size, src.size, arrays["table0"].size
+    ops = [
+        Op("translate_loc", 0, "translate_loc sub0", {"inp": "vslots0", "out": "int0", "v2p": "v2p0"}, n * 16),
+        Op("move_pages", 0, "move_pages sub0", {}, m * 2 * page_bytes + m * 8),
+        Op("remap_pages", 0, "remap_pages sub0", {}, m * 12),
+        Op("translate_pages", 0, "translate_pages sub0", {"inp": "table0", "out": "bt0", "v2p": "v2p0"}, t * 12),
+    ]
+    counts = {"layers": shape.layer_num, "relocated_pages": int(m), "live_pages": int(used.size),
+              "page_bytes": int(page_bytes)}
+    return Script("compact_8b", DESCRIPTIONS["compact_8b"], list(w.shapes), ps, arrays, {}, ops,
+                  lambda op: op.kind == "move_pages", "move_pages", counts)
+
+
 def fuse_layers(s: Script, name: str, gathers: bool) -> Script:
     """The same step with each sub-pool's per-layer stores (and, if asked, its per-layer
     gathers, when they share one window) replaced by one launch over all layers."""
@@ -288,9 +325,6 @@ def fuse_layers(s: Script, name: str, gathers: bool) -> Script:
                   lambda op: op.kind == top, top.split("_")[0], dict(s.counts))
 
 
-_OUT_OF = {"slots": "ids", "msrc": "msrcid", "mdst": "mdstid", "table": "bt"}
-
-
 class GpuRunner:
     """Runs a script through libukv on the current device and stream."""
 
@@ -304,10 +338,10 @@ class GpuRunner:
         if fill:
             W.fill_pattern_device(self.pool.raw, 1)
         self.t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device) for k, v in script.arrays.items()}
-        for k, v in script.arrays.items():
-            stem = re.match(r"[a-z]+", k).group(0)
-            if stem in _OUT_OF:
-                self.t[_OUT_OF[stem] + k[len(stem):]] = torch.empty(v.shape, dtype=torch.int32, device=device)
+        for op in script.ops:  # int32 outputs of the translations, shaped like their inputs
+            if "out" in op.args and op.args["out"] not in self.t:
+                self.t[op.args["out"]] = torch.empty(script.arrays[op.args["inp"]].shape, dtype=torch.int32,
+                                                     device=device)
         for i, (k, (rows, rb)) in enumerate(script.buffers.items()):
             if k.startswith("src"):
                 self.t[k] = W.normal_bf16_device((rows, rb // 2), 100 + i, device).view(torch.uint8)
@@ -322,7 +356,14 @@ class GpuRunner:
         if op.kind == "translate":
             U.ukv_translate_loc_for_kernel(self.pool, sub, t[a["inp"]], out=t[a["out"]])
         elif op.kind == "translate_pages":
-            U.ukv_translate_pages_for_kernel(self.pool, sub, t[a["inp"]], out=t[a["out"]])
+            U.ukv_translate_pages_for_kernel(self.pool, sub, t[a["inp"]], out=t[a["out"]],
+                                             v2p=t[a["v2p"]] if "v2p" in a else None)
+        elif op.kind == "translate_loc":
+            U.ukv_translate_loc(self.pool, sub, t[a["inp"]], v2p=t[a["v2p"]], out=t[a["out"]])
+        elif op.kind == "move_pages":
+            U.ukv_move_pages(self.pool, sub, t[f"pdst{sub}"], t[f"psrc{sub}"])
+        elif op.kind == "remap_pages":
+            U.ukv_remap_pages(self.pool, sub, t[f"v2p{sub}"], t[f"pvirt{sub}"], t[f"pdst{sub}"])
         elif op.kind == "store":
             r0, n = a["row0"], a["n"]
             k = t[f"src{sub}_0"][r0: r0 + n]
@@ -372,7 +413,14 @@ def cpu_baseline(name: str, W, budget_s: float = 12.0) -> dict:
         if op.kind == "translate":
             h[a["out"]], _ = pool.translate(sub, h[a["inp"]])
         elif op.kind == "translate_pages":
-            h[a["out"]], _ = pool.translate_pages(sub, h[a["inp"]])
+            h[a["out"]], _ = pool.translate_pages(sub, h[a["inp"]], h[a["v2p"]] if "v2p" in a else None)
+        elif op.kind == "translate_loc":
+            h[a["out"]], _ = pool.translate_loc(sub, h[a["inp"]], h[a["v2p"]])
+        elif op.kind == "move_pages":
+            pool.move_pages(sub, h[f"pdst{sub}"], h[f"psrc{sub}"])
+        elif op.kind == "remap_pages":
+            h[f"v2p{sub}"] = h[f"v2p{sub}"].copy()
+            pool.remap_pages(sub, h[f"v2p{sub}"], h[f"pvirt{sub}"], h[f"pdst{sub}"])
         elif op.kind == "store":
             r0, n = a["row0"], a["n"]
             pool.store(sub, a["layer"], h[a["ids"]], bufs[f"src{sub}_0"][r0: r0 + n],
@@ -397,12 +445,12 @@ def cpu_baseline(name: str, W, budget_s: float = 12.0) -> dict:
                             bufs[f"out{sub}_1"][i * rows:(i + 1) * rows] if nkv == 2 else None)
         done_bytes += op.nbytes
         done_ops += 1
-        if time.perf_counter() - t0 > budget_s and op.kind not in ("translate", "translate_pages"):
+        if time.perf_counter() - t0 > budget_s and not op.kind.startswith("translate"):
             break
     dt = time.perf_counter() - t0
     envelope = sum(p.envelope_bytes for p in pool.plan.subs)
     shrunk = " (same row and page geometry, fewer pages)" if name.split("_fused")[0] in (
-        "prefill_8b", "hybrid", "move_70b") else ""
+        "prefill_8b", "hybrid", "move_70b", "compact_8b") else ""
     return {
         "value": round(done_bytes / dt / 1e9, 3),
         "unit": "GB/s",

@@ -498,7 +498,8 @@ struct PageMoveArgs {
 
 // A page's rows on every layer, K and V, are one contiguous envelope, so a
 // page relocation is a straight copy of page_bytes.  One wave per
-// (pair, 64 * TPL-chunk segment); the pair index is wave-uniform.
+// (pair, 64 * TPL-chunk segment); the pair index is wave-uniform, so the
+// page lookups are scalar loads.
 template <typename V, int TPL>
 __global__ __launch_bounds__(kBlock) void move_pages_kernel(PageMoveArgs a) {
     const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
@@ -1016,7 +1017,10 @@ int ukv_move_pages(const ukv_pool *pool, int32_t sub, const int32_t *dst_pages_d
     a.num_pages = pool->spec[sub].num_pages;
     a.flags = pool->flags_dev;
     const int vb = vec_bytes_for({q.page_bytes, q.anchor_bytes, (uint64_t)(uintptr_t)pool->raw});
-    constexpr int kTpl = 8;
+    // one 16-byte chunk per lane (1 KiB per wave of 16-byte vectors): measured on
+    // MI355X at 5.9 TB/s for 2 MiB pages, against 5.6 at 2-4 chunks per lane and
+    // 4.0 at 8 (8 KiB per wave)
+    constexpr int kTpl = 1;
     a.vecs = (int64_t)(q.page_bytes / (uint64_t)vb);
     a.segs = (a.vecs + kWave * kTpl - 1) / (kWave * kTpl);
     const int64_t waves = n * a.segs;
