@@ -43,7 +43,7 @@ METRIC = "KV store/gather/move HBM GB/s and % of peak, Llama-3-8B-shape pool"
 KERNEL_SRC = os.path.join(ROOT, "store_gather_amd", "csrc", "ukv_runtime.hip")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 WORKLOADS = ("decode_8b", "prefill_8b", "hybrid", "move_70b", "tiny", "decode_8b_fused", "prefill_8b_fused",
-             "compact_8b")
+             "compact_8b", "swa_decode")
 
 
 def log(msg):
@@ -134,6 +134,12 @@ DESCRIPTIONS = {
                        "launch (ukv_store_kv_layers), then the per-layer gathers",
     "prefill_8b_fused": "prefill_8b_fused: the prefill_8b batch with all 32 layers stored in one launch and gathered "
                         "back in one launch (ukv_store_kv_layers / ukv_gather_kv_layers), then the move",
+    "swa_decode": "swa_decode: a 24-layer hybrid model (8 KV heads x 64, bf16, page 64) whose 12 full-attention "
+                  "layers use a full sub-pool (16,540 pages) and whose 12 sliding-window-128 layers use their own "
+                  "sub-pool (638 pages) reached through a full-to-SWA page mapping; 128 requests of U[256, 16384] "
+                  "tokens get one new token each; per step: translate (the window layers through the mapping), "
+                  "per layer store the new rows and gather every request (full, or its last 128 positions), then "
+                  "evict the pages that left the window",
     "compact_8b": "compact_8b: the prefill_8b pool (16,384 pages of 2 MiB) with its 16 requests addressed through a "
                   "virtual-to-physical table; per step: internal ids of the batch (translate_loc), relocation of every "
                   "live page above the watermark into the free pages below it (whole page envelopes, all 32 layers, "
@@ -146,6 +152,8 @@ def build_script(name: str, W, reduced: bool = False) -> Script:
     envelopes of at most ~8 GiB) for the CPU-oracle sample."""
     if name == "compact_8b":
         return compaction_script(W, reduced)
+    if name == "swa_decode":
+        return swa_script(W, reduced)
     if name.endswith("_fused"):
         return fuse_layers(build_script(name[: -len("_fused")], W, reduced), name,
                            gathers=name.startswith("prefill"))
@@ -286,6 +294,45 @@ def compaction_script(W, reduced: bool) -> Script:
                   lambda op: op.kind == "move_pages", "move_pages", counts)
 
 
+def swa_script(W, reduced: bool) -> Script:
+    w = W.swa_decode(num_reqs=24 if reduced else 128)
+    ps = w.page_size
+    full, swa = w.shapes
+    lens = w.req_lens[0]
+    table = W.padded_table(w.req_pages[0])
+    arrays = {"slots0": w.store_slots[0], "slots1": w.store_slots[0].copy(), "map1": w.swa_mapping.copy(),
+              "table0": table, "table1": table.copy(), "ptable": W.padded_table(w.req_pages[0], pad=-1),
+              "lens0": lens, "lens1": lens, "cu0_0": W.out_offsets(lens), "cu1_win": W.out_offsets(lens, w.window)}
+    n, R, rb = lens.size, lens.size, full.row_bytes
+    ops = [Op("translate", 0, "translate sub0", {"inp": "slots0", "out": "ids0"}, n * 12),
+           Op("translate", 1, "translate swa sub1", {"inp": "slots1", "out": "ids1", "v2p": "map1"}, n * 16),
+           Op("translate_pages", 0, "translate_pages sub0", {"inp": "table0", "out": "bt0"}, table.size * 8),
+           Op("translate_pages", 1, "translate_pages swa sub1", {"inp": "table1", "out": "bt1", "v2p": "map1"},
+              table.size * 12)]
+    rows_full = int(arrays["cu0_0"][-1])
+    rows_win = int(arrays["cu1_win"][-1])
+    pr_full = _pages_read(w.req_pages[0], lens, 0, ps)
+    pr_win = _pages_read(w.req_pages[0], lens, w.window, ps)
+    for layer in range(full.layer_num):
+        for sub in (0, 1):
+            ops.append(Op("store", sub, f"store {'swa ' if sub else ''}sub{sub}",
+                          {"layer": layer, "ids": f"ids{sub}", "row0": layer * n, "n": n}, n * (4 * rb + 4)))
+        ops.append(Op("gather", 0, "gather sub0", {"layer": layer, "window": 0, "cu": "cu0_0", "rows": rows_full},
+                      rows_full * 4 * rb + pr_full * 4 + R * 12 + 8))
+        ops.append(Op("gather", 1, "gather swa sub1",
+                      {"layer": layer, "window": w.window, "cu": "cu1_win", "rows": rows_win},
+                      rows_win * 4 * rb + pr_win * 4 + R * 12 + 8))
+    ops.append(Op("evict", 1, "evict_window sub1", {"window": w.window}, table.size * 4 + n * 4))
+    buffers = {"src0_0": (full.layer_num * n, rb), "src0_1": (full.layer_num * n, rb),
+               "src1_0": (swa.layer_num * n, rb), "src1_1": (swa.layer_num * n, rb),
+               "out0_0": (rows_full, rb), "out0_1": (rows_full, rb), "out1_0": (rows_win, rb), "out1_1": (rows_win, rb)}
+    counts = {"layers": 2 * full.layer_num, "requests": int(n), "gathered_rows_full_layer": rows_full,
+              "gathered_rows_window_layer": rows_win, "full_pages": int(full.num_pages),
+              "swa_pages": int(swa.num_pages)}
+    return Script("swa_decode", DESCRIPTIONS["swa_decode"], list(w.shapes), ps, arrays, buffers, ops,
+                  lambda op: op.kind == "gather" and op.sub == 0, "gather", counts)
+
+
 def fuse_layers(s: Script, name: str, gathers: bool) -> Script:
     """The same step with each sub-pool's per-layer stores (and, if asked, its per-layer
     gathers, when they share one window) replaced by one launch over all layers."""
@@ -354,7 +401,10 @@ class GpuRunner:
         U, t, a, sub = self.U, self.t, op.args, op.sub
         nkv = 2 if self.s.shapes[sub].kind == 0 else 1
         if op.kind == "translate":
-            U.ukv_translate_loc_for_kernel(self.pool, sub, t[a["inp"]], out=t[a["out"]])
+            U.ukv_translate_loc_for_kernel(self.pool, sub, t[a["inp"]], out=t[a["out"]],
+                                           v2p=t[a["v2p"]] if "v2p" in a else None)
+        elif op.kind == "evict":
+            U.ukv_evict_window(self.pool, t[f"map{sub}"], t["ptable"], t["lens0"], a["window"])
         elif op.kind == "translate_pages":
             U.ukv_translate_pages_for_kernel(self.pool, sub, t[a["inp"]], out=t[a["out"]],
                                              v2p=t[a["v2p"]] if "v2p" in a else None)
@@ -411,7 +461,10 @@ def cpu_baseline(name: str, W, budget_s: float = 12.0) -> dict:
         a, sub = op.args, op.sub
         nkv = 2 if s.shapes[sub].kind == 0 else 1
         if op.kind == "translate":
-            h[a["out"]], _ = pool.translate(sub, h[a["inp"]])
+            h[a["out"]], _ = pool.translate(sub, h[a["inp"]], h[a["v2p"]] if "v2p" in a else None)
+        elif op.kind == "evict":
+            h[f"map{sub}"] = h[f"map{sub}"].copy()
+            pool.evict_window(h[f"map{sub}"], h["ptable"], h["lens0"], a["window"])
         elif op.kind == "translate_pages":
             h[a["out"]], _ = pool.translate_pages(sub, h[a["inp"]], h[a["v2p"]] if "v2p" in a else None)
         elif op.kind == "translate_loc":
@@ -450,7 +503,7 @@ def cpu_baseline(name: str, W, budget_s: float = 12.0) -> dict:
     dt = time.perf_counter() - t0
     envelope = sum(p.envelope_bytes for p in pool.plan.subs)
     shrunk = " (same row and page geometry, fewer pages)" if name.split("_fused")[0] in (
-        "prefill_8b", "hybrid", "move_70b", "compact_8b") else ""
+        "prefill_8b", "hybrid", "move_70b", "compact_8b", "swa_decode") else ""
     return {
         "value": round(done_bytes / dt / 1e9, 3),
         "unit": "GB/s",

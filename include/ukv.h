@@ -304,6 +304,23 @@ int ukv_remap_pages(const ukv_pool *pool, int32_t sub, int32_t *v2p_dev, int64_t
                     const int32_t *virt_pages_dev, const int32_t *phys_pages_dev, int64_t n, hipStream_t stream);
 
 /*
+ * Sliding-window eviction (DKV 功能与动机 and 关联脉络: SWA layers live in a
+ * sub-pool of their own, and the tombstone fix clears the full-to-SWA
+ * mapping of tokens that left the window).  mapping_dev: the caller's
+ * int32[map_len] full virtual page -> SWA physical page table (-1 = not
+ * resident), which is also the v2p argument of the translations on the SWA
+ * sub-pool, so a write through an evicted page goes to the sink row.  For
+ * each request r and page i of its block table (int32[num_reqs * bt_stride],
+ * full virtual pages) with (i + 1) * ps <= seq_lens[r] - window:
+ * mapping[table[r][i]] = -1.  A page past the mapping raises
+ * UKV_FLAG_SLOT_RANGE; negative entries are skipped; window <= 0 is a no-op.
+ * Pages must not be shared between requests.  The page size is the pool's.
+ */
+int ukv_evict_window(const ukv_pool *pool, int32_t *mapping_dev, int64_t map_len, const int32_t *table_dev,
+                     int64_t bt_stride, const int32_t *seq_lens_dev, int32_t num_reqs, int32_t window,
+                     hipStream_t stream);
+
+/*
  * Reads and clears the pool's sticky flags (UKV_FLAG_*): enqueued on
  * `stream` after the work already there, then synchronises that stream.
  */

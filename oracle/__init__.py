@@ -131,6 +131,8 @@ def lib() -> ctypes.CDLL:
         L.orc_move_pages.restype = ctypes.c_int
         L.orc_remap_pages.argtypes = [vp, i64, vp, vp, i64, i64, ctypes.POINTER(ctypes.c_uint32)]
         L.orc_remap_pages.restype = None
+        L.orc_evict_window.argtypes = [vp, i64, vp, i64, vp, i32, i32, i64, ctypes.POINTER(ctypes.c_uint32)]
+        L.orc_evict_window.restype = None
         for fn in ("orc_sizeof_pool", "orc_sizeof_sub_plan", "orc_sizeof_spec"):
             getattr(L, fn).restype = ctypes.c_int
         assert L.orc_sizeof_pool() == ctypes.sizeof(_Pool)
@@ -308,6 +310,18 @@ class OraclePool:
         flags = ctypes.c_uint32(0)
         lib().orc_remap_pages(_ptr(v2p), v2p.size, _ptr(virt), _ptr(phys), virt.size, self.specs[sub].num_pages,
                               ctypes.byref(flags))
+        return flag_names(flags.value)
+
+    def evict_window(self, mapping: np.ndarray, table, seq_lens, window: int):
+        """In place on the int32 full-to-SWA page mapping."""
+        assert mapping.dtype == np.int32 and mapping.flags.c_contiguous
+        bt = np.ascontiguousarray(table, dtype=np.int32)
+        if bt.ndim == 1:
+            bt = bt.reshape(len(seq_lens), -1)
+        lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        flags = ctypes.c_uint32(0)
+        lib().orc_evict_window(_ptr(mapping), mapping.size, _ptr(bt), bt.shape[1], _ptr(lens), lens.size, window,
+                               self.page_size, ctypes.byref(flags))
         return flag_names(flags.value)
 
     def store(self, sub: int, layer: int, ids, k: np.ndarray, v: Optional[np.ndarray]):

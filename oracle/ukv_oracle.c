@@ -593,3 +593,36 @@ void orc_remap_pages(int32_t *v2p, int64_t v2p_len, const int32_t *virt, const i
         v2p[virt[i]] = phys[i];
     }
 }
+
+/*
+ * Sliding-window eviction (DKV 功能与动机 and 关联脉络: the unified pool holds
+ * SWA layers in their own sub-pool; the tombstone fix clears the full-to-SWA
+ * mapping of tokens that left the window).  READING: the mapping is per page
+ * (full virtual page -> SWA physical page, -1 = not resident); page i of
+ * request r (positions [i*ps, (i+1)*ps)) is evicted when it lies wholly
+ * before the window, (i+1)*ps <= len - window: mapping[table[r][i]] = -1.
+ * A table entry past the mapping raises ORC_F_SLOT_RANGE; negative entries
+ * are skipped.  window <= 0 evicts nothing.  Requests do not share pages.
+ */
+void orc_evict_window(int32_t *mapping, int64_t map_len, const int32_t *table, int64_t bt_stride,
+                      const int32_t *seq_lens, int32_t num_reqs, int32_t window, int64_t page_size, uint32_t *flags)
+{
+    if (window <= 0)
+        return;
+    for (int32_t r = 0; r < num_reqs; r++) {
+        int64_t len = seq_lens[r];
+        if (len <= window)
+            continue;
+        int64_t start = len - window;
+        for (int64_t i = 0; i < bt_stride && (i + 1) * page_size <= start; i++) {
+            int64_t page = table[(int64_t)r * bt_stride + i];
+            if (page < 0)
+                continue;
+            if (page >= map_len) {
+                *flags |= ORC_F_SLOT_RANGE;
+                continue;
+            }
+            mapping[page] = -1;
+        }
+    }
+}

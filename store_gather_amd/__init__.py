@@ -41,7 +41,7 @@ EXPORTS = (
     "ukv_pool_plan", "ukv_pool_create", "ukv_pool_destroy", "ukv_pool_get_plan", "ukv_pool_view", "ukv_plan_view",
     "ukv_translate_loc_for_kernel", "ukv_translate_pages_for_kernel", "ukv_store_kv", "ukv_store_kv_layers",
     "ukv_gather_kv", "ukv_gather_kv_layers", "ukv_move_kv", "ukv_pool_error_flags", "ukv_last_error",
-    "ukv_status_name", "ukv_translate_loc", "ukv_move_pages", "ukv_remap_pages",
+    "ukv_status_name", "ukv_translate_loc", "ukv_move_pages", "ukv_remap_pages", "ukv_evict_window",
 )
 
 
@@ -110,6 +110,7 @@ def _load() -> ctypes.CDLL:
         "ukv_translate_loc": [vp, i32, vp, i64, vp, i64, vp, vp],
         "ukv_move_pages": [vp, i32, vp, vp, i64, vp],
         "ukv_remap_pages": [vp, i32, vp, i64, vp, vp, i64, vp],
+        "ukv_evict_window": [vp, vp, i64, vp, i64, vp, i32, i32, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -460,6 +461,21 @@ def ukv_remap_pages(pool: Pool, sub: int, v2p: torch.Tensor, virt_pages: torch.T
                                 phys_pages.data_ptr(), virt_pages.numel(), _stream_handle(stream)))
 
 
+def ukv_evict_window(pool: Pool, mapping: torch.Tensor, table: torch.Tensor, seq_lens: torch.Tensor, window: int,
+                     stream=None) -> None:
+    """Clear the full-to-SWA page mapping of pages wholly before each request's window (in place)."""
+    d = pool.device
+    _dev_ptr(mapping, "mapping", d, torch.int32)
+    _dev_ptr(table, "table", d, torch.int32)
+    _dev_ptr(seq_lens, "seq_lens", d, torch.int32)
+    if table.dim() != 2 or not table.is_contiguous() or table.shape[0] != seq_lens.numel():
+        raise ValueError("table must be a contiguous [num_reqs, width] tensor")
+    if not (mapping.is_contiguous() and seq_lens.is_contiguous()):
+        raise ValueError("mapping and seq_lens must be contiguous")
+    _check(_lib.ukv_evict_window(pool.handle, mapping.data_ptr(), mapping.numel(), table.data_ptr(), table.shape[1],
+                                 seq_lens.data_ptr(), seq_lens.numel(), int(window), _stream_handle(stream)))
+
+
 def ukv_pool_error_flags(pool: Pool, stream=None) -> frozenset:
     """Read and clear the pool's sticky flags (synchronises the stream)."""
     out = ctypes.c_uint32(0)
@@ -472,5 +488,5 @@ __all__ = [
     "plan_status", "ukv_pool_create", "allocate_pool", "ukv_pool_destroy", "ukv_pool_view", "ukv_plan_view", "dense_view",
     "ukv_translate_loc_for_kernel", "ukv_translate_pages_for_kernel", "ukv_store_kv", "ukv_store_kv_layers",
     "ukv_gather_kv", "ukv_gather_kv_layers", "ukv_move_kv", "ukv_pool_error_flags", "ukv_last_error", "EXPORTS",
-    "STATUS", "FLAGS", "ukv_translate_loc", "ukv_move_pages", "ukv_remap_pages",
+    "STATUS", "FLAGS", "ukv_translate_loc", "ukv_move_pages", "ukv_remap_pages", "ukv_evict_window",
 ]

@@ -545,6 +545,27 @@ __global__ __launch_bounds__(kBlock) void remap_pages_kernel(int32_t *v2p, int64
     v2p[v] = p;
 }
 
+// Sliding-window eviction: thread per block-table entry (r, i); page i of
+// request r is evicted when it lies wholly before the window.
+__global__ __launch_bounds__(kBlock) void evict_window_kernel(int32_t *mapping, int64_t map_len, const int32_t *table,
+                                                             int64_t bt_stride, const int32_t *seq_lens,
+                                                             int32_t num_reqs, int32_t window, int64_t ps,
+                                                             uint32_t *flags) {
+    const int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (e >= (int64_t)num_reqs * bt_stride) return;
+    const int64_t r = e / bt_stride;
+    const int64_t i = e - r * bt_stride;
+    const int64_t len = seq_lens[r];
+    if (len <= window || (i + 1) * ps > len - window) return;
+    const int32_t page = table[e];
+    if (page < 0) return;
+    if (page >= map_len) {
+        atomicOr(flags, UKV_FLAG_SLOT_RANGE);
+        return;
+    }
+    mapping[page] = -1;
+}
+
 __global__ void flags_fetch_clear_kernel(uint32_t *f) {
     if (threadIdx.x == 0) f[1] = atomicExch(&f[0], 0u);
 }
@@ -1051,6 +1072,28 @@ int ukv_remap_pages(const ukv_pool *pool, int32_t sub, int32_t *v2p_dev, int64_t
     const unsigned grid = (unsigned)((n + kBlock - 1) / kBlock);
     hipLaunchKernelGGL(remap_pages_kernel, dim3(grid), dim3(kBlock), 0, stream, v2p_dev, v2p_len, virt_pages_dev,
                        phys_pages_dev, n, (int64_t)pool->spec[sub].num_pages, pool->flags_dev);
+    return check_launch(who);
+}
+
+int ukv_evict_window(const ukv_pool *pool, int32_t *mapping_dev, int64_t map_len, const int32_t *table_dev,
+                     int64_t bt_stride, const int32_t *seq_lens_dev, int32_t num_reqs, int32_t window,
+                     hipStream_t stream) {
+    const char *who = "ukv_evict_window";
+    int rc = check_pool_call(pool, 0, who);
+    if (rc != UKV_OK) return rc;
+    if (num_reqs < 0 || map_len < 0 || bt_stride < 0)
+        return fail(UKV_ERR_INVALID_ARG, "%s: negative size", who);
+    if (window <= 0 || num_reqs == 0 || bt_stride == 0) return UKV_OK;
+    if (mapping_dev == nullptr || table_dev == nullptr || seq_lens_dev == nullptr)
+        return fail(UKV_ERR_INVALID_ARG, "%s: null mapping, table or seq_lens", who);
+    const int64_t entries = (int64_t)num_reqs * bt_stride;
+    if (ranges_overlap(mapping_dev, (uint64_t)map_len * 4, table_dev, (uint64_t)entries * 4))
+        return fail(UKV_ERR_INVALID_ARG, "%s: the mapping overlaps the table", who);
+    const int64_t grid = (entries + kBlock - 1) / kBlock;
+    if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: table too large for one launch", who);
+    hipLaunchKernelGGL(evict_window_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream, mapping_dev, map_len,
+                       table_dev, bt_stride, seq_lens_dev, num_reqs, window, (int64_t)pool->plan.page_size,
+                       pool->flags_dev);
     return check_launch(who);
 }
 

@@ -556,3 +556,52 @@ def test_compaction_end_to_end():
     pair.assert_pools_equal()
     after = read(v2p_d)
     assert np.array_equal(before[0], after[0]) and np.array_equal(before[1], after[1])
+
+
+# ---------------------------------------------------------------------------
+# sliding-window layers in a sub-pool of their own
+# ---------------------------------------------------------------------------
+
+def test_swa_subpool_store_gather_and_eviction():
+    w = W.swa_decode(num_reqs=7, len_lo=40, len_hi=900, layer_num=6, window=100)
+    pair = Pair(w.shapes, w.page_size)
+    ps = w.page_size
+    mapping = w.swa_mapping.copy()
+    map_d = to_dev(mapping)
+    slots = w.store_slots[0]
+    lens = w.req_lens[0]
+    # the new token of every request: full layers directly, window layers through the mapping
+    for sub, v2p in ((0, None), (1, mapping)):
+        ids_d = U.ukv_translate_loc_for_kernel(pair.gpu, sub, to_dev(slots), v2p=None if v2p is None else map_d)
+        ids, _ = pair.orc.translate(sub, slots, v2p)
+        assert np.array_equal(ids_d.cpu().numpy(), ids)
+        rb = pair.rb(sub)
+        for layer in range(3):
+            k = bf16_rows(500 + 10 * sub + layer, slots.size, rb)
+            v = bf16_rows(600 + 10 * sub + layer, slots.size, rb)
+            U.ukv_store_kv(pair.gpu, sub, layer, ids_d, rows_dev(k), rows_dev(v))
+            pair.orc.store(sub, layer, ids, k, v)
+            pair.record_store(sub, layer, ids, k, v)
+    pair.assert_pools_equal()
+    table = W.padded_table(w.req_pages[0])
+    for sub, win in ((0, 0), (1, w.window)):
+        bt_d = U.ukv_translate_pages_for_kernel(pair.gpu, sub, to_dev(table), v2p=None if sub == 0 else map_d)
+        bt, _ = pair.orc.translate_pages(sub, table, None if sub == 0 else mapping)
+        assert np.array_equal(bt_d.cpu().numpy(), bt)
+        cu = W.out_offsets(lens, win)
+        rb = pair.rb(sub)
+        ko = torch.empty((3, int(cu[-1]), rb), dtype=torch.uint8, device="cuda")
+        vo = torch.empty_like(ko)
+        U.ukv_gather_kv_layers(pair.gpu, sub, 0, 3, bt_d, to_dev(lens), to_dev(cu), win, ko, vo)
+        for layer in range(3):
+            eko = np.zeros((int(cu[-1]), rb), np.uint8)
+            evo = np.zeros_like(eko)
+            assert pair.orc.gather(sub, layer, bt, lens, cu, win, eko, evo) == frozenset()
+            assert np.array_equal(ko[layer].cpu().numpy(), eko) and np.array_equal(vo[layer].cpu().numpy(), evo)
+    # eviction clears exactly the oracle's entries; window reads are unchanged
+    padded = W.padded_table(w.req_pages[0], pad=-1)
+    U.ukv_evict_window(pair.gpu, map_d, to_dev(padded), to_dev(lens), w.window)
+    assert pair.orc.evict_window(mapping, padded, lens, w.window) == frozenset()
+    assert np.array_equal(map_d.cpu().numpy(), mapping)
+    assert (mapping != w.swa_mapping).sum() > 0
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()

@@ -559,3 +559,40 @@ def test_compaction_preserves_what_requests_read():
     assert v2p.max() < len(used) + 1  # every live page now sits below the watermark
     after = read_all()
     assert all(np.array_equal(a, b) for a, b in zip(before, after))
+
+
+def test_window_eviction_brute_force_and_window_reads_unchanged():
+    w = W.swa_decode(num_reqs=5, len_lo=20, len_hi=700, layer_num=4, window=70)
+    ps = w.page_size
+    mapping = w.swa_mapping.copy()
+    pool, raw = _filled_pool(w.shapes, ps)
+    table = W.padded_table(w.req_pages[0], pad=-1)
+    lens = w.req_lens[0]
+    win = w.window
+    bt_before, _ = pool.translate_pages(1, W.padded_table(w.req_pages[0]), mapping)
+    cu = W.out_offsets(lens, win)
+    rb = pool.row_bytes(1)
+
+    def read(bt):
+        ko = np.zeros((int(cu[-1]), rb), np.uint8)
+        vo = np.zeros_like(ko)
+        assert pool.gather(1, 1, bt, lens, cu, win, ko, vo) == frozenset()
+        return ko, vo
+
+    before = read(bt_before)
+    exp = mapping.copy()
+    for r, pages in enumerate(w.req_pages[0]):
+        for i, page in enumerate(pages):
+            positions = range(i * ps, (i + 1) * ps)
+            if all(p < lens[r] - win for p in positions):
+                exp[page] = -1
+    assert (exp != mapping).sum() > 0
+    assert pool.evict_window(mapping, table, lens, win) == frozenset()
+    assert np.array_equal(mapping, exp)
+    after = read(pool.translate_pages(1, W.padded_table(w.req_pages[0]), mapping)[0])
+    assert np.array_equal(before[0], after[0]) and np.array_equal(before[1], after[1])
+    # a slot on an evicted page now translates to the sink
+    evicted = np.nonzero((exp == -1) & (w.swa_mapping >= 0))[0]
+    ids, _ = pool.translate(1, [int(evicted[0]) * ps + 3], mapping)
+    assert ids.tolist() == [0]
+    assert pool.evict_window(mapping, np.array([[len(mapping)]], np.int32), np.array([1000], np.int32), 10) == {"slot_range"}

@@ -375,6 +375,52 @@ def hybrid(num_reqs: int = 128, len_lo: int = 256, len_hi: int = 16384, layer_nu
     return w
 
 
+def swa_decode(num_reqs: int = 128, len_lo: int = 256, len_hi: int = 16384, layer_num: int = 24, window: int = 128,
+               seed: int = 0) -> Workload:
+    """Hybrid decode step with the sliding-window layers in a sub-pool of their own.
+
+    Sub-pool 0 holds the full-attention layers (even layers of a 24-layer model,
+    8 KV heads of dim 64, bf16, page 64), sub-pool 1 the sliding-window ones (odd
+    layers, window 128).  ``num_reqs`` requests of U[len_lo, len_hi] tokens get
+    one new token each.  Full pages come from a seeded permutation (room for the
+    new token included); every full page that overlaps a request's window after
+    the new token, and ``stale`` older pages, are mapped to SWA pages from their
+    own permutation (``mapping``: full page -> SWA page, -1 = not resident).
+    """
+    ps = 64
+    g = rng(seed, SUB_LENS)
+    lens = g.integers(len_lo, len_hi, endpoint=True, size=num_reqs).astype(np.int32)
+    new_len = lens.astype(np.int64) + 1
+    npages = (new_len + ps - 1) // ps
+    P_full = int(1 + npages.sum())
+    first = np.maximum(new_len - window, 0) // ps  # first page overlapping the window
+    stale = np.minimum(first, 2)  # two pages that left the window still mapped
+    n_swa = int((npages - first + stale).sum())
+    P_swa = 1 + n_swa
+    half = layer_num // 2
+    w = Workload("swa_decode", ps, [mha(half, 8, 64, P_full), mha(half, 8, 64, P_swa)], seed)
+    perm = page_permutation(seed, P_full)
+    start = np.concatenate([[0], np.cumsum(npages)])
+    pages = [perm[start[r]: start[r + 1]] for r in range(num_reqs)]
+    w.req_pages[0] = pages
+    w.req_lens[0] = new_len.astype(np.int32)
+    w.windows[0] = [0] * half
+    w.windows[1] = [window] * half
+    mapping = np.full(P_full, -1, dtype=np.int32)
+    swa_perm = page_permutation(seed, P_swa, sub=SUB_PAGES + 10)
+    at = 0
+    for r in range(num_reqs):
+        for i in range(int(first[r] - stale[r]), int(npages[r])):
+            mapping[pages[r][i]] = swa_perm[at]
+            at += 1
+    w.store_slots[0] = np.array([pages[r][lens[r] // ps] * ps + lens[r] % ps for r in range(num_reqs)],
+                                dtype=np.int64)
+    w.notes = "mapping"
+    w.swa_mapping = mapping
+    w.window = window
+    return w
+
+
 def move_70b(num_pages: int = 32768, rows: int = 65536, layer_num: int = 80, seed: int = 0) -> Workload:
     """Llama-3-70B-shape pool: 80 layers, 8 KV heads of dim 128, bf16, page size 16;
     32,768 pages (160 GiB of envelopes).  Move ``rows`` live rows to ``rows`` other
@@ -390,5 +436,5 @@ __all__ = [
     "splitmix64", "fill_pattern_host", "fill_pattern_device", "f32_to_bf16_bits", "normal_bf16_host",
     "normal_bf16_device", "SubPoolShape", "mha", "mla", "rng", "live_slots", "page_permutation",
     "slots_of_requests", "padded_table", "out_offsets", "Workload", "tiny_mha", "decode_8b",
-    "dirichlet_lengths", "prefill_8b", "hybrid", "move_70b", "compaction_plan", "MHA", "MLA",
+    "dirichlet_lengths", "prefill_8b", "hybrid", "move_70b", "compaction_plan", "swa_decode", "MHA", "MLA",
 ]
