@@ -133,6 +133,8 @@ def lib() -> ctypes.CDLL:
         L.orc_remap_pages.restype = None
         L.orc_evict_window.argtypes = [vp, i64, vp, i64, vp, i32, i32, i64, ctypes.POINTER(ctypes.c_uint32)]
         L.orc_evict_window.restype = None
+        L.orc_build_page_table.argtypes = [vp, i64, vp, i32, i64, i64, i64, vp, i64, vp, ctypes.POINTER(ctypes.c_uint32)]
+        L.orc_build_page_table.restype = None
         for fn in ("orc_sizeof_pool", "orc_sizeof_sub_plan", "orc_sizeof_spec"):
             getattr(L, fn).restype = ctypes.c_int
         assert L.orc_sizeof_pool() == ctypes.sizeof(_Pool)
@@ -311,6 +313,19 @@ class OraclePool:
         lib().orc_remap_pages(_ptr(v2p), v2p.size, _ptr(virt), _ptr(phys), virt.size, self.specs[sub].num_pages,
                               ctypes.byref(flags))
         return flag_names(flags.value)
+
+    def build_page_table(self, sub: int, req_pages, prefix_lens, v2p=None):
+        """Prefix-only kernel-facing page table [num_reqs, width] (int32), plus flags."""
+        t = np.ascontiguousarray(req_pages, dtype=np.int32)
+        lens = np.ascontiguousarray(prefix_lens, dtype=np.int32)
+        out = np.empty(t.shape, dtype=np.int32)
+        flags = ctypes.c_uint32(0)
+        v = None if v2p is None else np.ascontiguousarray(v2p, dtype=np.int32)
+        sp = self.plan.subs[sub]
+        lib().orc_build_page_table(_ptr(t), t.shape[1], _ptr(lens), lens.size, self.page_size, sp.blocks_per_page,
+                                   self.specs[sub].num_pages, _ptr(v), 0 if v is None else v.size, _ptr(out),
+                                   ctypes.byref(flags))
+        return out, flag_names(flags.value)
 
     def evict_window(self, mapping: np.ndarray, table, seq_lens, window: int):
         """In place on the int32 full-to-SWA page mapping."""

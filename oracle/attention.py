@@ -1,0 +1,127 @@
+"""Reference decode attention read straight from the dense per-layer views (fp64, CPU).
+
+TEST INFRASTRUCTURE ONLY: like the rest of oracle/, only the tests, the
+package smoke check and the benchmark's CPU-baseline leg may import this.
+
+Source: the report page "PR #34602: feat(unified-memory): dense KV views for
+uniform-row MHA/SWA models", section 功能与动机 (motivation): once every layer
+of the pool is a dense (n_rows, head_num, head_dim) view, an attention
+backend reads a layer through that one tensor and one block table shared by
+all layers; section 关联脉络 (related work) places the kernel-facing,
+prefix-only page-table build (#35247) on that read path.  The pages print
+no attention kernel.  READING: the attention is the textbook scaled
+dot-product decode attention with grouped KV heads, written out in float64.
+For request r with length len (positions j0 <= j < len, j0 = len - window
+for a sliding-window layer longer than its window, else 0), query head g
+(KV head h = g // G, G = q_heads / head_num):
+
+    s_j = scale * sum_d q[r, g, d] * K_j[h, d]
+    p_j = exp(s_j - max_j s_j) / sum_j exp(s_j - max_j s_j)
+    out[r, g, d] = sum_j p_j * V_j[h, d]
+
+K_j / V_j are the rows of the layer's K / V views at row
+bt[r][j // ps] * ps + j % ps (block-table entries are kernel-facing page
+indices, phys * blocks_per_page), decoded from their bf16 bits.
+
+Conditions (the same readings as the block-table gather): a request with
+len <= 0 attends to nothing and its output is zero; a request longer than
+the caller's bound max_seq_len raises LAYOUT; one whose positions need a
+table column past the table width, or a negative / non-kernel-facing /
+out-of-pool entry, raises BAD_BLOCK.  Such a request's output is all zeros.
+
+Pinned in tests/test_oracle_pins.py: against torch's scaled_dot_product_attention
+in float64 over rows fetched by the independent strided builder, against
+the closed forms of uniform keys and of a single position, and on the
+error conditions above.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 (exact: every bf16 value is a float32 value)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """One request: q [Hq, D], k [n, Hkv, D], v [n, Hkv, Dv] (float64) -> [Hq, Dv].
+
+    Query head g reads KV head g // (Hq // Hkv).  n == 0 gives zeros.
+    """
+    hq = q.shape[0]
+    n, hkv = k.shape[0], k.shape[1]
+    group = hq // hkv
+    out = np.zeros((hq, v.shape[2]))
+    if n == 0:
+        return out
+    for g in range(hq):
+        h = g // group
+        s = scale * (k[:, h, :] @ q[g])
+        e = np.exp(s - s.max())
+        out[g] = (e / e.sum()) @ v[:, h, :]
+    return out
+
+
+def decode_attention(pool, sub: int, layer: int, q_bits: np.ndarray, block_table, seq_lens, window: int,
+                     scale: float, max_seq_len: int | None = None, read=None, requests=None):
+    """Decode attention of every request over its positions in the pool's dense views.
+
+    q_bits: [R, Hq, D] bf16 bits (uint16); block_table: [R, width] int32
+    kernel-facing page indices; seq_lens: [R].  ``read(offset, nbytes)``
+    returns the uint16 words at a byte offset of the pool (default: the
+    pool's own buffer), so that an addresses-only pool can be served from
+    values generated on demand.  ``requests`` limits the work to some
+    requests (the others stay zero).  Returns (out float64 [R, Hq, Dv], set
+    of condition names raised).
+    """
+    if read is None:
+        def read(off, nbytes):
+            return pool.raw[off: off + nbytes].view(np.uint16)
+    spec = pool.specs[sub]
+    assert spec.kind == 0, "decode attention reads an MHA sub-pool"
+    hkv, d, dv = spec.head_num, spec.head_dim, spec.v_head_dim
+    ps = pool.page_size
+    bpp = pool.plan.subs[sub].blocks_per_page
+    bt = np.asarray(block_table, dtype=np.int64)
+    width = bt.shape[1] if bt.ndim == 2 else 0
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    R, hq = q_bits.shape[0], q_bits.shape[1]
+    assert hq % hkv == 0
+    k_base, v_base = pool.view_base(sub, layer, 0), pool.view_base(sub, layer, 1)
+    k_row_bytes, v_row_bytes = hkv * d * spec.elem_bytes, hkv * dv * spec.elem_bytes
+    out = np.zeros((R, hq, dv))
+    flags = set()
+    for r in (range(R) if requests is None else requests):
+        n = int(lens[r])
+        if n <= 0:
+            continue
+        if max_seq_len is not None and n > max_seq_len:
+            flags.add("layout")
+            continue
+        j0 = n - window if (window > 0 and n > window) else 0
+        positions = range(j0, n)
+        rows = []
+        for j in positions:
+            col = j // ps
+            entry = int(bt[r, col]) if col < width else -1
+            if entry < 0 or entry % bpp != 0 or entry // bpp >= spec.num_pages:
+                rows = None
+                break
+            rows.append(entry * ps + j % ps)
+        if rows is None:
+            flags.add("bad_block")
+            continue
+        k = np.stack([read(k_base + row * k_row_bytes, k_row_bytes) for row in rows])
+        v = np.stack([read(v_base + row * v_row_bytes, v_row_bytes) for row in rows])
+        out[r] = attend(bf16_bits_to_f64(q_bits[r]), bf16_bits_to_f64(k).reshape(-1, hkv, d),
+                        bf16_bits_to_f64(v).reshape(-1, hkv, dv), scale)
+    return out, frozenset(flags)
+
+
+def default_scale(head_dim: int) -> float:
+    """The usual softmax scale, 1 / sqrt(head_dim)."""
+    return 1.0 / math.sqrt(head_dim)

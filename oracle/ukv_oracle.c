@@ -626,3 +626,35 @@ void orc_evict_window(int32_t *mapping, int64_t map_len, const int32_t *table, i
         }
     }
 }
+
+/*
+ * Prefix-only page-table build for the read path (DKV 关联脉络: the stacked
+ * change #35247 builds the kernel-facing page table of the attention
+ * backends by translating the prefix only).  READING: row r of req_pages
+ * lists the request's allocator pages in position order; entry i holds
+ * positions [i*ps, (i+1)*ps), so it is translated (as orc_translate_pages,
+ * through v2p when given) exactly when i < ceil(prefix_len[r] / ps); every
+ * other entry is written as page 0 (the sink page) and is never read, so it
+ * raises nothing.  A prefix needing more than bt_stride entries raises
+ * ORC_F_LAYOUT (the covered entries are still translated); range conditions
+ * of translated entries raise ORC_F_SLOT_RANGE as in orc_translate_pages.
+ */
+void orc_build_page_table(const int32_t *req_pages, int64_t bt_stride, const int32_t *prefix_lens, int32_t num_reqs,
+                          int64_t page_size, int64_t blocks_per_page, int64_t num_pages, const int32_t *v2p,
+                          int64_t v2p_len, int32_t *out, uint32_t *flags)
+{
+    for (int32_t r = 0; r < num_reqs; r++) {
+        int64_t len = prefix_lens[r] > 0 ? prefix_lens[r] : 0;
+        int64_t used = (len + page_size - 1) / page_size;
+        if (used > bt_stride)
+            *flags |= ORC_F_LAYOUT;
+        for (int64_t i = 0; i < bt_stride; i++) {
+            int64_t at = (int64_t)r * bt_stride + i;
+            if (i < used)
+                orc_translate_pages(&req_pages[at], 1, page_size, blocks_per_page, num_pages, v2p, v2p_len, &out[at],
+                                    flags);
+            else
+                out[at] = 0;
+        }
+    }
+}

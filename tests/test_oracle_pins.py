@@ -596,3 +596,171 @@ def test_window_eviction_brute_force_and_window_reads_unchanged():
     ids, _ = pool.translate(1, [int(evicted[0]) * ps + 3], mapping)
     assert ids.tolist() == [0]
     assert pool.evict_window(mapping, np.array([[len(mapping)]], np.int32), np.array([1000], np.int32), 10) == {"slot_range"}
+
+
+# ---------------------------------------------------------------------------
+# read path: prefix-only page table and decode attention over the dense views
+# ---------------------------------------------------------------------------
+
+from oracle import attention as A  # noqa: E402
+
+
+def _gauss_pool(shapes, ps, seed=11):
+    """A pool whose every byte pair is a finite bf16 value (attention reads whole rows)."""
+    specs = [Spec(s.kind, s.layer_num, s.head_num, s.head_dim, s.v_head_dim, s.elem_bytes, s.num_pages) for s in shapes]
+    req = oracle.plan(specs, ps).required_bytes
+    raw = W.irwin_hall_bf16_host(seed, 0, (req + 7) // 8 * 8).view(np.uint8).copy()
+    return oracle.OraclePool(specs, ps, raw), raw
+
+
+def _requests(seed, P, ps, lens):
+    """Per-request physical page lists drawn from pages 1..P-1, pages not shared."""
+    perm = W.page_permutation(seed, P)
+    perm = perm[perm != 0]
+    out, at = [], 0
+    for n in lens:
+        k = (int(n) + ps - 1) // ps
+        out.append(perm[at: at + k])
+        at += k
+    assert at <= perm.size
+    return out
+
+
+def _sdpa_reference(ref, layer, pages, lens, window, q_bits, hkv, d, scale):
+    """torch's scaled_dot_product_attention in float64, rows fetched by the strided builder."""
+    import torch
+
+    out = np.zeros((len(lens), q_bits.shape[1], d))
+    group = q_bits.shape[1] // hkv
+    for r, (pg, n) in enumerate(zip(pages, lens)):
+        if n <= 0:
+            continue
+        k, v = ref.gather_pages(layer, [pg], [n], window)
+        kt = torch.from_numpy(A.bf16_bits_to_f64(k.view(np.uint16)).reshape(-1, hkv, d)).transpose(0, 1)
+        vt = torch.from_numpy(A.bf16_bits_to_f64(v.view(np.uint16)).reshape(-1, hkv, d)).transpose(0, 1)
+        kt = kt.repeat_interleave(group, dim=0).unsqueeze(0)  # [1, Hq, n, d]: q head g reads KV head g // G
+        vt = vt.repeat_interleave(group, dim=0).unsqueeze(0)
+        q = torch.from_numpy(A.bf16_bits_to_f64(q_bits[r])).unsqueeze(0).unsqueeze(2)  # [1, Hq, 1, d]
+        o = torch.nn.functional.scaled_dot_product_attention(q, kt.contiguous(), vt.contiguous(), scale=scale)
+        out[r] = o[0, :, 0, :].numpy()
+    return out
+
+
+@pytest.mark.parametrize("hkv,group,d,window", [(2, 2, 16, 0), (2, 2, 16, 6), (1, 4, 8, 0), (3, 1, 8, 9)])
+def test_decode_attention_matches_torch_sdpa(hkv, group, d, window):
+    ps, P, L = 4, 24, 2
+    lens = np.array([1, 5, 13, 4, 22, 0], dtype=np.int32)
+    pool, raw = _gauss_pool([W.mha(L, hkv, d, P)], ps)
+    pages = _requests(3, P, ps, lens)
+    bt, flags = pool.translate_pages(0, W.padded_table(pages))
+    assert flags == frozenset()
+    q = W.irwin_hall_bf16_host(5, 0, 2 * lens.size * hkv * group * d).reshape(lens.size, hkv * group, d)
+    scale = A.default_scale(d)
+    ref = _strided(pool, 0)
+    for layer in range(L):
+        out, fl = A.decode_attention(pool, 0, layer, q, bt, lens, window, scale)
+        assert fl == frozenset()
+        exp = _sdpa_reference(ref, layer, pages, lens, window, q, hkv, d, scale)
+        assert np.abs(out - exp).max() < 1e-12
+        assert not np.allclose(out[1:5], 0)
+
+
+def test_decode_attention_closed_forms():
+    ps, P, hkv, group, d = 4, 12, 2, 2, 8
+    lens = np.array([7, 1], dtype=np.int32)
+    pool, raw = _gauss_pool([W.mha(1, hkv, d, P)], ps)
+    ref = _strided(pool, 0)
+    pages = _requests(8, P, ps, lens)
+    bt, _ = pool.translate_pages(0, W.padded_table(pages))
+    q = W.irwin_hall_bf16_host(9, 0, 2 * 2 * hkv * group * d).reshape(2, hkv * group, d)
+    # request 0: every K row the same -> uniform weights -> the mean of its V rows
+    k0 = ref.row(0, 0, int(pages[0][0]), 0).copy()
+    for j in range(7):
+        ref.env[int(pages[0][j // ps]), 0, 0, j % ps] = k0
+    out, fl = A.decode_attention(pool, 0, 0, q, bt, lens, 0, 0.3)
+    assert fl == frozenset()
+    _, v = ref.gather_pages(0, [pages[0]], [7], 0)
+    vmean = A.bf16_bits_to_f64(v.view(np.uint16)).reshape(7, hkv, d).mean(axis=0)
+    for g in range(hkv * group):
+        assert np.allclose(out[0, g], vmean[g // group], rtol=0, atol=1e-14)
+    # request 1: a single position -> exactly its V row, whatever q and the scale
+    _, v1 = ref.gather_pages(0, [pages[1]], [1], 0)
+    v1 = A.bf16_bits_to_f64(v1.view(np.uint16)).reshape(hkv, d)
+    for g in range(hkv * group):
+        assert np.array_equal(out[1, g], v1[g // group])
+    # scale 0 -> uniform weights for any keys
+    out0, _ = A.decode_attention(pool, 0, 0, q, bt, lens, 3, 0.0)
+    _, v3 = ref.gather_pages(0, [pages[0]], [7], 3)
+    v3 = A.bf16_bits_to_f64(v3.view(np.uint16)).reshape(3, hkv, d).mean(axis=0)
+    assert np.allclose(out0[0, 1], v3[0], rtol=0, atol=1e-14)
+
+
+def test_decode_attention_conditions_zero_the_request():
+    ps, P, hkv, d = 4, 12, 2, 8
+    lens = np.array([6, 6, 6, 0, 9], dtype=np.int32)
+    pool, raw = _gauss_pool([W.mha(1, hkv, d, P)], ps)
+    pages = _requests(4, P, ps, lens)
+    bt, _ = pool.translate_pages(0, W.padded_table(pages))
+    q = W.irwin_hall_bf16_host(2, 0, 2 * lens.size * hkv * d).reshape(lens.size, hkv, d)
+    good, fl = A.decode_attention(pool, 0, 0, q, bt, lens, 0, 0.5)
+    assert fl == frozenset() and np.allclose(good[3], 0) and not np.allclose(good[0], 0)
+    bpp = pool.plan.subs[0].blocks_per_page
+    for bad in (-1, 1, P * bpp, bt[1, 0] + 1):
+        b = bt.copy()
+        b[1, 1] = bad
+        out, fl = A.decode_attention(pool, 0, 0, q, b, lens, 0, 0.5)
+        assert fl == {"bad_block"}
+        assert np.allclose(out[1], 0) and np.array_equal(np.delete(out, 1, 0), np.delete(good, 1, 0))
+    # a bad entry outside the window is never read
+    b = bt.copy()
+    b[4, 0] = -1
+    out, fl = A.decode_attention(pool, 0, 0, q, b, lens, 4, 0.5)
+    assert fl == frozenset()
+    # a table too narrow for the length, and a length past the caller's bound
+    out, fl = A.decode_attention(pool, 0, 0, q, bt[:, :2], lens, 0, 0.5)
+    assert fl == {"bad_block"} and np.allclose(out[4], 0) and np.array_equal(out[:4], good[:4])
+    out, fl = A.decode_attention(pool, 0, 0, q, bt, lens, 0, 0.5, max_seq_len=8)
+    assert fl == {"layout"} and np.allclose(out[4], 0) and np.array_equal(out[:4], good[:4])
+
+
+def test_build_page_table_is_prefix_only():
+    ps, P = 4, 16
+    pool, raw = _filled_pool([W.mha(2, 2, 8, P)], ps)
+    lens = np.array([5, 1, 12, 0], dtype=np.int32)
+    pages = _requests(6, P, ps, lens)
+    width = 5
+    req = np.full((lens.size, width), 10 ** 6, dtype=np.int32)  # entries past the prefix hold garbage
+    for r, pg in enumerate(pages):
+        req[r, :pg.size] = pg
+    out, fl = pool.build_page_table(0, req, lens)
+    assert fl == frozenset()
+    full, _ = pool.translate_pages(0, W.padded_table(pages))
+    for r, pg in enumerate(pages):
+        assert np.array_equal(out[r, :pg.size], full[r, :pg.size])
+        assert (out[r, pg.size:] == 0).all()
+    # the built table reads back, through the block-table gather, what the strided builder holds
+    ref = _strided(pool, 0)
+    cu = W.out_offsets(lens, 0)
+    ko = np.zeros((int(cu[-1]), 32), np.uint8)
+    vo = np.zeros_like(ko)
+    assert pool.gather(0, 1, out, lens, cu, 0, ko, vo) == frozenset()
+    rk, rv = ref.gather_pages(1, pages, lens, 0)
+    assert np.array_equal(ko, rk) and np.array_equal(vo, rv)
+    # through a virtual-to-physical table: entry i is the kernel-facing index of v2p[page]
+    v2p = W.page_permutation(12, P).astype(np.int32)
+    out2, fl = pool.build_page_table(0, req, lens, v2p)
+    assert fl == frozenset()
+    bpp = pool.plan.subs[0].blocks_per_page
+    for r, pg in enumerate(pages):
+        walk_rows, _ = walk(P, 2, MHA, ps, 32)
+        for i, page in enumerate(pg):
+            phys = int(v2p[page])
+            assert pool.view_base(0, 0, 0) + out2[r, i] * ps * 32 == walk_rows[(phys, 0, 0, 0)]
+            assert out2[r, i] % bpp == 0
+    # a prefix wider than the table, and an out-of-range page inside the prefix
+    _, fl = pool.build_page_table(0, req[:, :2], lens)
+    assert fl == {"layout"}
+    bad = req.copy()
+    bad[2, 1] = P
+    out3, fl = pool.build_page_table(0, bad, lens)
+    assert fl == {"slot_range"} and out3[2, 1] == 0

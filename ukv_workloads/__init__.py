@@ -16,6 +16,9 @@ Generators (both published, both re-implemented here from their definitions):
 * SplitMix64 (Steele, Lea, Flood, "Fast splittable pseudorandom number
   generators", OOPSLA 2014; output mix as in Vigna's public-domain reference):
   element w of the stream seeded with s is mix(s + (w + 1) * 0x9E3779B97F4A7C15).
+* Irwin-Hall (1927): the sum of n independent uniforms; with n = 4 it stands
+  in for N(0, 1) where the values must be generated bit-identically on the
+  device and on the host (pools of many GiB that attention reads).
 * Box-Muller (1958): z0 = sqrt(-2 ln u1) cos(2 pi u2), z1 = sqrt(-2 ln u1) sin(2 pi u2),
   with u1, u2 in (0, 1] from 53-bit SplitMix64 draws; z is rounded to float32
   and then to bfloat16 with round-to-nearest-even on the bit pattern.
@@ -133,6 +136,64 @@ def normal_bf16_device(shape, seed: int, device):
     g.manual_seed(seed)
     x = torch.randn(*shape, generator=g, dtype=torch.float32, device=device)
     return x.to(torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------
+# Counter-based bf16 values with an approximately N(0, 1) distribution
+# ----------------------------------------------------------------------------
+
+# Irwin-Hall sum of four uniform 16-bit integers: mean 4 * 65535 / 2 and
+# variance 4 * (65536^2 - 1) / 12; scaled to unit variance.
+IH_MEAN = 2 * 65535
+IH_SCALE = 1.0 / float(np.sqrt(4.0 * (65536.0 * 65536.0 - 1.0) / 12.0))
+
+
+def irwin_hall_bf16_host(seed: int, byte_start: int, nbytes: int) -> np.ndarray:
+    """bf16 values (as uint16 bit patterns) for bytes [byte_start, byte_start+nbytes) of a buffer.
+
+    The bf16 element at byte 2e is drawn from SplitMix64 element e of the
+    stream seeded with ``seed``: the four 16-bit fields of that output are
+    summed exactly, centred and scaled in float64 (one rounding), rounded to
+    float32 and then to bf16 with round-to-nearest-even on the bits.  The
+    result has mean 0, variance 1 and range about +-3.46, and is bit-identical
+    to :func:`irwin_hall_bf16_device` (every step is an exact integer step or
+    one correctly rounded IEEE operation).
+    """
+    assert byte_start % 2 == 0 and nbytes % 2 == 0
+    z = splitmix64(seed, byte_start // 2, nbytes // 2)
+    m = np.uint64(0xFFFF)
+    s = ((z & m) + ((z >> np.uint64(16)) & m) + ((z >> np.uint64(32)) & m) + (z >> np.uint64(48))).astype(np.int64)
+    x = (s - IH_MEAN).astype(np.float64) * IH_SCALE
+    return f32_to_bf16_bits(x.astype(np.float32))
+
+
+def irwin_hall_fill_device(t, seed: int, byte_start: int = 0, chunk_elems: int = 1 << 27):
+    """Write :func:`irwin_hall_bf16_host`'s values for bytes [byte_start, ...) into device uint8 ``t``."""
+    import torch
+
+    assert t.dtype == torch.uint8 and t.is_contiguous()
+    assert byte_start % 2 == 0 and t.numel() % 2 == 0
+    out = t.view(torch.int16)
+    n = out.numel()
+    e0 = byte_start // 2
+    for a in range(0, n, chunk_elems):
+        b = min(n, a + chunk_elems)
+        z = torch.arange(e0 + a + 1, e0 + b + 1, dtype=torch.int64, device=t.device)
+        z.mul_(_i64(GAMMA)).add_(_i64(seed & MASK64))
+        z ^= (z >> 30) & ((1 << 34) - 1)
+        z.mul_(_i64(M1))
+        z ^= (z >> 27) & ((1 << 37) - 1)
+        z.mul_(_i64(M2))
+        z ^= (z >> 31) & ((1 << 33) - 1)
+        s = (z & 0xFFFF) + ((z >> 16) & 0xFFFF) + ((z >> 32) & 0xFFFF) + ((z >> 48) & 0xFFFF)
+        del z
+        x = (s - IH_MEAN).to(torch.float64).mul_(IH_SCALE).to(torch.float32)
+        del s
+        u = x.view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+        del x
+        bits = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+        out[a:b].copy_(bits.to(torch.int16))
+        del u, bits
 
 
 # ----------------------------------------------------------------------------
