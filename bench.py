@@ -41,9 +41,10 @@ if ROOT not in sys.path:
 PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "KV store/gather/move HBM GB/s and % of peak, Llama-3-8B-shape pool"
 KERNEL_SRC = os.path.join(ROOT, "store_gather_amd", "csrc", "ukv_runtime.hip")
+ATTN_SRC = os.path.join(ROOT, "store_gather_amd", "csrc", "ukv_attention.hip")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 WORKLOADS = ("decode_8b", "prefill_8b", "hybrid", "move_70b", "tiny", "decode_8b_fused", "prefill_8b_fused",
-             "compact_8b", "swa_decode")
+             "compact_8b", "swa_decode", "decode_attn_8b")
 
 
 def log(msg):
@@ -55,8 +56,9 @@ def num(x, nd):
     return None if x is None or x != x else round(float(x), nd)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(kernel: str = "") -> str:
+    """First 16 hex digits of the SHA-256 of the source file that holds `kernel`."""
+    with open(ATTN_SRC if kernel.startswith("attn") else KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -69,7 +71,7 @@ def traffic_from_profile(workload: str, kernel: str):
     text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(kernel):
         return None
     return int(m_bytes.group(1))
 
@@ -99,6 +101,7 @@ class Script:
     roofline: Callable[[Op], bool]
     roofline_kernel: str
     counts: dict = field(default_factory=dict)
+    dtype: str = "u8"  # what the path computes in: bytes moved as integers
 
 
 def _pages_read(pages_per_req, lens, window, ps):
@@ -140,6 +143,11 @@ DESCRIPTIONS = {
                   "tokens get one new token each; per step: translate (the window layers through the mapping), "
                   "per layer store the new rows and gather every request (full, or its last 128 positions), then "
                   "evict the pages that left the window",
+    "decode_attn_8b": "decode_attn_8b: the decode_8b batch on the read path: a Llama-3-8B-shape pool (32 layers, "
+                      "8 KV heads x 128, bf16, page 16, 4,096 pages, 8 GiB) of Irwin-Hall bf16 values, 256 requests "
+                      "of U[1024, 8192] positions with 32 query heads each (GQA 4); per step: translate the 256 new "
+                      "slots and build the prefix-only page table once, then per layer store the 256 new K/V rows "
+                      "and run decode attention over every request straight from the dense views (fp32 output)",
     "compact_8b": "compact_8b: the prefill_8b pool (16,384 pages of 2 MiB) with its 16 requests addressed through a "
                   "virtual-to-physical table; per step: internal ids of the batch (translate_loc), relocation of every "
                   "live page above the watermark into the free pages below it (whole page envelopes, all 32 layers, "
@@ -154,6 +162,8 @@ def build_script(name: str, W, reduced: bool = False) -> Script:
         return compaction_script(W, reduced)
     if name == "swa_decode":
         return swa_script(W, reduced)
+    if name == "decode_attn_8b":
+        return attention_script(W, reduced)
     if name.endswith("_fused"):
         return fuse_layers(build_script(name[: -len("_fused")], W, reduced), name,
                            gathers=name.startswith("prefill"))
@@ -333,6 +343,39 @@ def swa_script(W, reduced: bool) -> Script:
                   lambda op: op.kind == "gather" and op.sub == 0, "gather", counts)
 
 
+ATTN_Q_HEADS = 32  # Llama-3-8B: 32 query heads on 8 KV heads
+ATTN_SCALE = 128 ** -0.5
+
+
+def attention_script(W, reduced: bool) -> Script:
+    """The decode step of the read path: page table, then per layer store + decode attention."""
+    w = W.decode_8b(num_pages=1024, num_reqs=16) if reduced else W.decode_8b()
+    ps = w.page_size
+    shape = w.shapes[0]
+    lens = w.req_lens[0].astype(np.int32)
+    R, d, hq = lens.size, shape.head_dim, ATTN_Q_HEADS
+    rb = shape.row_bytes
+    slots = w.store_slots[0].astype(np.int64)
+    n = slots.size
+    req = W.padded_table(w.req_pages[0])
+    arrays = {"slots0": slots, "req0": req, "lens0": lens,
+              "q0": W.irwin_hall_bf16_host(41, 0, 2 * R * hq * d).view(np.int16).reshape(R, hq, d)}
+    pages_read = _pages_read(w.req_pages[0], lens, 0, ps)
+    attn_bytes = int(lens.astype(np.int64).sum()) * 2 * rb + R * hq * d * (2 + 4) + pages_read * 4 + R * 4
+    ops = [Op("translate", 0, "translate sub0", {"inp": "slots0", "out": "ids0"}, n * 12),
+           Op("build_table", 0, "build_page_table sub0", {"inp": "req0", "out": "bt0"}, req.size * 8 + R * 4)]
+    for layer in range(shape.layer_num):
+        ops.append(Op("store", 0, "store mha sub0", {"layer": layer, "ids": "ids0", "row0": layer * n, "n": n},
+                      n * (4 * rb + 4)))
+        ops.append(Op("attention", 0, "attention sub0", {"layer": layer, "max_len": int(lens.max())}, attn_bytes))
+    buffers = {"src0_0": (shape.layer_num * n, rb), "src0_1": (shape.layer_num * n, rb)}
+    counts = {"layers": shape.layer_num, "requests": int(R), "q_heads": hq,
+              "attended_positions_per_layer": int(lens.astype(np.int64).sum()),
+              "attention_flops_per_layer": int(4 * lens.astype(np.int64).sum() * hq * d)}
+    return Script("decode_attn_8b", DESCRIPTIONS["decode_attn_8b"], list(w.shapes), ps, arrays, buffers, ops,
+                  lambda op: op.kind == "attention", "attn_chunk", counts, dtype="bf16")
+
+
 def fuse_layers(s: Script, name: str, gathers: bool) -> Script:
     """The same step with each sub-pool's per-layer stores (and, if asked, its per-layer
     gathers, when they share one window) replaced by one launch over all layers."""
@@ -382,9 +425,19 @@ class GpuRunner:
         n = (int(plan.required_bytes) + 7) // 8 * 8
         self.pool = U.allocate_pool(script.shapes, script.page_size, device=device,
                                     extra_bytes=n - int(plan.required_bytes))
-        if fill:
+        attn = any(op.kind == "attention" for op in script.ops)
+        if fill and attn:
+            W.irwin_hall_fill_device(self.pool.raw, 1)  # attention reads whole rows: finite bf16 values
+        elif fill:
             W.fill_pattern_device(self.pool.raw, 1)
         self.t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device) for k, v in script.arrays.items()}
+        if attn:
+            q = self.t["q0"].view(torch.bfloat16)
+            self.t["q0"] = q
+            mx = max(op.args["max_len"] for op in script.ops if op.kind == "attention")
+            self.t["attn_out"] = torch.empty(q.shape, dtype=torch.float32, device=device)
+            need = U.ukv_decode_attention_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], mx, 0)
+            self.t["attn_ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
         for op in script.ops:  # int32 outputs of the translations, shaped like their inputs
             if "out" in op.args and op.args["out"] not in self.t:
                 self.t[op.args["out"]] = torch.empty(script.arrays[op.args["inp"]].shape, dtype=torch.int32,
@@ -410,6 +463,11 @@ class GpuRunner:
                                              v2p=t[a["v2p"]] if "v2p" in a else None)
         elif op.kind == "translate_loc":
             U.ukv_translate_loc(self.pool, sub, t[a["inp"]], v2p=t[a["v2p"]], out=t[a["out"]])
+        elif op.kind == "build_table":
+            U.ukv_build_page_table(self.pool, sub, t[a["inp"]], t[f"lens{sub}"], out=t[a["out"]])
+        elif op.kind == "attention":
+            U.ukv_decode_attention(self.pool, sub, a["layer"], t["q0"], t[f"bt{sub}"], t[f"lens{sub}"], a["max_len"],
+                                   0, ATTN_SCALE, out=t["attn_out"], workspace=t["attn_ws"])
         elif op.kind == "move_pages":
             U.ukv_move_pages(self.pool, sub, t[f"pdst{sub}"], t[f"psrc{sub}"])
         elif op.kind == "remap_pages":
@@ -451,7 +509,9 @@ def cpu_baseline(name: str, W, budget_s: float = 12.0) -> dict:
     specs = [oracle.Spec(x.kind, x.layer_num, x.head_num, x.head_dim, x.v_head_dim, x.elem_bytes, x.num_pages)
              for x in s.shapes]
     req = oracle.plan(specs, s.page_size).required_bytes
-    pool = oracle.OraclePool(specs, s.page_size, np.full(req, 0x5A, dtype=np.uint8))  # pages touched up front
+    # pages touched up front; 0x3F3F is the finite bf16 value 0.746 for the attention reads
+    pool = oracle.OraclePool(specs, s.page_size, np.full(req, 0x3F if name == "decode_attn_8b" else 0x5A,
+                                                         dtype=np.uint8))
     h = dict(s.arrays)
     bufs = {k: np.full((rows, rb), 7, dtype=np.uint8) for k, (rows, rb) in s.buffers.items()}
     done_bytes = 0
@@ -469,6 +529,15 @@ def cpu_baseline(name: str, W, budget_s: float = 12.0) -> dict:
             h[a["out"]], _ = pool.translate_pages(sub, h[a["inp"]], h[a["v2p"]] if "v2p" in a else None)
         elif op.kind == "translate_loc":
             h[a["out"]], _ = pool.translate_loc(sub, h[a["inp"]], h[a["v2p"]])
+        elif op.kind == "build_table":
+            h[a["out"]], _ = pool.build_page_table(sub, h[a["inp"]], h[f"lens{sub}"])
+        elif op.kind == "attention":
+            from threadpoolctl import threadpool_limits
+
+            from oracle import attention as oracle_attention
+            with threadpool_limits(limits=1):  # numpy's BLAS on one thread, like the C oracle
+                oracle_attention.decode_attention(pool, sub, a["layer"], h["q0"].view(np.uint16), h[f"bt{sub}"],
+                                                  h[f"lens{sub}"], 0, ATTN_SCALE, a["max_len"])
         elif op.kind == "move_pages":
             pool.move_pages(sub, h[f"pdst{sub}"], h[f"psrc{sub}"])
         elif op.kind == "remap_pages":
@@ -504,6 +573,9 @@ def cpu_baseline(name: str, W, budget_s: float = 12.0) -> dict:
     envelope = sum(p.envelope_bytes for p in pool.plan.subs)
     shrunk = " (same row and page geometry, fewer pages)" if name.split("_fused")[0] in (
         "prefill_8b", "hybrid", "move_70b", "compact_8b", "swa_decode") else ""
+    if name == "decode_attn_8b":
+        shrunk = (" (16 of the 256 requests on 1,024 pages of the same geometry; fp64 numpy attention, one "
+                  "BLAS thread, over rows the C oracle addresses)")
     return {
         "value": round(done_bytes / dt / 1e9, 3),
         "unit": "GB/s",
@@ -613,7 +685,7 @@ def run_workload(name, args, torch, U, W, device) -> dict:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u8",
+        "dtype": script.dtype,
         "data": "synthetic",
         "config": dict({"workload": script.description, "kv_dtype": "bf16", "parallelism": "single GPU",
                         "step_bytes": step_bytes, "launches_per_step": len(script.ops)}, **script.counts),

@@ -10,8 +10,9 @@
  *     kernel_id(t) = (t / ps) * (ps * blocks_per_page) + t % ps,
  *
  * with blocks_per_page = 2L for MHA and L for MLA.  On that pool this library
- * runs four HIP kernels: id translation, the per-layer K/V scatter-store, the
- * block-table gather and the row move.
+ * runs HIP kernels for id translation, the per-layer K/V scatter-store, the
+ * block-table gather, the row and page moves, and, on the read path, the
+ * prefix-only page-table build and a decode attention over the views.
  *
  * Source for the method: the report page "PR #34602: feat(unified-memory):
  * dense KV views for uniform-row MHA/SWA models" (sgl-project/sglang), cited
@@ -319,6 +320,64 @@ int ukv_remap_pages(const ukv_pool *pool, int32_t sub, int32_t *v2p_dev, int64_t
 int ukv_evict_window(const ukv_pool *pool, int32_t *mapping_dev, int64_t map_len, const int32_t *table_dev,
                      int64_t bt_stride, const int32_t *seq_lens_dev, int32_t num_reqs, int32_t window,
                      hipStream_t stream);
+
+/*
+ * Kernel-facing page table for the read path, built from the prefix only
+ * (DKV 关联脉络: the stacked change #35247 translates, for the attention
+ * backends, only the pages that hold a request's prefix).
+ * req_pages_dev: int32[num_reqs * bt_stride], row r = request r's allocator
+ *   pages in position order (entry i holds positions [i*ps, (i+1)*ps));
+ * prefix_lens_dev: int32[num_reqs];
+ * out_dev: int32[num_reqs * bt_stride], the same buffer as req_pages_dev or
+ *   not overlapping it (nor the lengths or v2p).
+ * Entry i of row r is translated exactly when i < ceil(prefix_lens[r] / ps),
+ * as ukv_translate_pages_for_kernel (through v2p_dev when not NULL): the
+ * result is phys * blocks_per_page, 0 for a negative or unmapped page, and
+ * 0 plus UKV_FLAG_SLOT_RANGE past the v2p table or the pool.  Every other
+ * entry is written 0 and its input is never read for translation.  A prefix
+ * needing more than bt_stride entries raises UKV_FLAG_LAYOUT.
+ */
+int ukv_build_page_table(const ukv_pool *pool, int32_t sub, const int32_t *req_pages_dev, int64_t bt_stride,
+                         const int32_t *prefix_lens_dev, int32_t num_reqs, const int32_t *v2p_dev, int64_t v2p_len,
+                         int32_t *out_dev, hipStream_t stream);
+
+/*
+ * Decode attention straight from the dense views (DKV 功能与动机: a backend
+ * reads each layer through one dense tensor plus one block table shared by
+ * all layers).  The pages print no attention kernel; this is the textbook
+ * scaled dot-product attention of one query token per request with grouped
+ * KV heads.  For request r with len = seq_lens[r] > 0, positions
+ * j0 <= j < len (j0 = len - window when 0 < window < len, else 0), query
+ * head g reading KV head h = g / G (G = q_heads / head_num):
+ *     out[r][g] = sum_j softmax_j(scale * q[r][g] . K_j[h]) * V_j[h],
+ * K_j / V_j being row block_table[r][j / ps] * ps + j % ps of the layer's
+ * K / V views.
+ * Sub-pool: MHA, bf16, head_dim 64, 128 or 256; G in {1, 2, 4, 8}.
+ * q_dev: bf16 [num_reqs, q_heads, head_dim], contiguous, 16-byte aligned.
+ * block_table_dev: int32[num_reqs * bt_stride] kernel-facing page indices
+ *   (ukv_build_page_table / ukv_translate_pages_for_kernel).
+ * seq_lens_dev: int32[num_reqs]; max_seq_len: a host bound on them that
+ *   sizes the launch.
+ * out_dev: fp32 [num_reqs, q_heads, head_dim], 16-byte aligned, overlapping
+ *   neither q, the workspace nor the pool.
+ * workspace_dev: at least ukv_decode_attention_workspace_bytes(...) bytes,
+ *   16-byte aligned, owned by the caller (partial results per chunk of
+ *   positions; its contents on entry do not matter).
+ * Arithmetic: scores on the matrix cores from bf16 inputs with fp32
+ * accumulation, softmax and the weighted sum of V in fp32.
+ * Conditions: a request with len <= 0 gives zeros; len > max_seq_len gives
+ * zeros and UKV_FLAG_LAYOUT; a position whose table column is past
+ * bt_stride, or whose entry is negative, not a multiple of blocks_per_page
+ * or past the pool, gives zeros for the whole request and UKV_FLAG_BAD_BLOCK.
+ */
+int ukv_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const void *q_dev, int32_t q_heads,
+                         const int32_t *block_table_dev, int64_t bt_stride, const int32_t *seq_lens_dev,
+                         int32_t num_reqs, int32_t max_seq_len, int32_t window, float scale, float *out_dev,
+                         void *workspace_dev, uint64_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes ukv_decode_attention needs for these sizes (0 when none). */
+uint64_t ukv_decode_attention_workspace_bytes(int32_t num_reqs, int32_t q_heads, int32_t head_dim,
+                                              int32_t max_seq_len, int32_t window);
 
 /*
  * Reads and clears the pool's sticky flags (UKV_FLAG_*): enqueued on

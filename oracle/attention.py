@@ -66,8 +66,45 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndar
     return out
 
 
+U32 = 2.0 ** -24  # unit roundoff of float32
+
+
+def gamma(n: int) -> float:
+    """n u / (1 - n u): the bound on the relative error of an n-term float32 sum."""
+    return n * U32 / (1.0 - n * U32)
+
+
+def fp32_error_bound(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, sum_terms: int) -> np.ndarray:
+    """Bound on |out_fp32 - out| per query head for an fp32 evaluation of `attend`.
+
+    q [Hq, D], k [n, Hkv, D], v [n, Hkv, Dv] as in `attend`.  An fp32
+    evaluation computes each score from exact products (bf16 x bf16 fits in
+    float32) with a D-term fp32 sum, so |ds_j| <= scale * gamma(D) *
+    sum_d |q_d k_jd| (A); scaling and the exponential add a few units of
+    roundoff relative to the argument (4 u (|scale s_j| log2 e + 1)).  Weights
+    perturbed by at most delta relative change the weighted mean by at most
+    4 delta max|v|, and the numerator / denominator sums of at most
+    `sum_terms` terms add 2 gamma(sum_terms) max|v|.
+    """
+    hq, d = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    bound = np.zeros(hq)
+    if k.shape[0] == 0:
+        return bound
+    for g in range(hq):
+        h = g // group
+        a = (np.abs(k[:, h, :]) @ np.abs(q[g])).max()
+        s_max = np.abs(scale * (k[:, h, :] @ q[g])).max() * 1.4426950408889634
+        delta = scale * gamma(d) * a + 4 * U32 * (s_max + 1.0)
+        vmax = np.abs(v[:, h, :]).max()
+        bound[g] = 4 * delta * vmax + 2 * gamma(sum_terms) * vmax
+    return bound
+
+
 def decode_attention(pool, sub: int, layer: int, q_bits: np.ndarray, block_table, seq_lens, window: int,
-                     scale: float, max_seq_len: int | None = None, read=None, requests=None):
+                     scale: float, max_seq_len: int | None = None, read=None, requests=None,
+                     bound_terms: int | None = None):
     """Decode attention of every request over its positions in the pool's dense views.
 
     q_bits: [R, Hq, D] bf16 bits (uint16); block_table: [R, width] int32
@@ -76,7 +113,8 @@ def decode_attention(pool, sub: int, layer: int, q_bits: np.ndarray, block_table
     pool's own buffer), so that an addresses-only pool can be served from
     values generated on demand.  ``requests`` limits the work to some
     requests (the others stay zero).  Returns (out float64 [R, Hq, Dv], set
-    of condition names raised).
+    of condition names raised), and with ``bound_terms`` also the
+    fp32_error_bound [R, Hq] of every request (0 where nothing is read).
     """
     if read is None:
         def read(off, nbytes):
@@ -94,6 +132,7 @@ def decode_attention(pool, sub: int, layer: int, q_bits: np.ndarray, block_table
     k_base, v_base = pool.view_base(sub, layer, 0), pool.view_base(sub, layer, 1)
     k_row_bytes, v_row_bytes = hkv * d * spec.elem_bytes, hkv * dv * spec.elem_bytes
     out = np.zeros((R, hq, dv))
+    bound = np.zeros((R, hq))
     flags = set()
     for r in (range(R) if requests is None else requests):
         n = int(lens[r])
@@ -117,8 +156,13 @@ def decode_attention(pool, sub: int, layer: int, q_bits: np.ndarray, block_table
             continue
         k = np.stack([read(k_base + row * k_row_bytes, k_row_bytes) for row in rows])
         v = np.stack([read(v_base + row * v_row_bytes, v_row_bytes) for row in rows])
-        out[r] = attend(bf16_bits_to_f64(q_bits[r]), bf16_bits_to_f64(k).reshape(-1, hkv, d),
-                        bf16_bits_to_f64(v).reshape(-1, hkv, dv), scale)
+        qf, kf, vf = (bf16_bits_to_f64(q_bits[r]), bf16_bits_to_f64(k).reshape(-1, hkv, d),
+                      bf16_bits_to_f64(v).reshape(-1, hkv, dv))
+        out[r] = attend(qf, kf, vf, scale)
+        if bound_terms is not None:
+            bound[r] = fp32_error_bound(qf, kf, vf, scale, bound_terms)
+    if bound_terms is not None:
+        return out, frozenset(flags), bound
     return out, frozenset(flags)
 
 

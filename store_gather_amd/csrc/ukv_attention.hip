@@ -1,0 +1,560 @@
+// libukv read path for gfx950 (MI355X): the kernel-facing, prefix-only
+// page-table build and a paged decode attention that reads the dense
+// per-layer K / V views through that table.
+//
+// Source: report page "PR #34602: feat(unified-memory): dense KV views for
+// uniform-row MHA/SWA models": 功能与动机 (motivation: a backend reads each
+// layer through one dense tensor and one block table shared by all layers)
+// and 关联脉络 (related work: the stacked change #35247 builds the backends'
+// kernel-facing page table by translating the prefix only).  The pages print
+// no attention kernel; the attention is the textbook scaled dot-product
+// decode attention with grouped KV heads (G query heads per KV head).
+//
+// Design (decode: one query token per request, G <= 8 query heads per KV
+// head, bf16 K / V / Q, fp32 accumulation and output):
+//
+//  - split-K over positions ("flash decoding"): one 64-lane wave owns
+//    (request, KV head, chunk of kChunk positions) and writes an unnormalised
+//    partial (running max, row sum, G x D sums) to a workspace; a second,
+//    small kernel merges the chunks of each (request, KV head).  Tens of
+//    thousands of waves for a decode batch, whatever the length mix.
+//  - per tile of 16 positions: S^T = K Q^T on the matrix cores
+//    (v_mfma_f32_16x16x32_bf16, D / 32 steps).  K is the A operand straight
+//    from HBM: lane l loads 16 bytes of position l % 16, so every load is a
+//    plain 16-byte vector load of the dense view.  Q is the B operand, its G
+//    heads repeated over the 16 columns, so lane l ends with the scores of
+//    positions 4 (l / 16) + i (i < 4) for query head (l % 16) % G.
+//  - online softmax in base 2 with a lazy rescale: the running max moves
+//    only when a tile's max exceeds it by more than 8 (weights stay <= 2^8,
+//    no overflow), so the G x D / 4 accumulators are rescaled a handful of
+//    times per chunk instead of every tile.
+//  - P V on the vector ALUs in fp32: lane l accumulates position group
+//    l / 16 and dims [(l % 16) D / 16, +D / 16) of every query head; V is
+//    read as 16-byte loads of D / 16 elements, 4 positions per wave load.
+//    (P V reduces over positions, which are strided in the dense view, so
+//    the matrix cores would need a transpose through LDS; the vector work is
+//    a small share of the HBM time at decode's arithmetic intensity.)
+//  - K and V of the next tile are loaded before the current tile is
+//    computed; the block-table lookups of a tile are done by its 16
+//    position lanes and broadcast with ds_bpermute.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "ukv_internal.h"
+
+using ukv::check_launch;
+using ukv::check_pool_call;
+using ukv::fail;
+using ukv::ranges_overlap;
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int64_t kMaxGrid = 0x7fffffff;
+constexpr int kTile = 16;        // positions per MFMA tile
+constexpr int kChunk = 256;      // positions per wave (split-K unit)
+constexpr float kRescaleGap = 8.0f;  // log2 headroom before the running max moves
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ----------------------------------------------------------------------------
+// prefix-only page-table build (关联脉络: #35247)
+// ----------------------------------------------------------------------------
+struct TableArgs {
+    const int32_t *req_pages;  // [num_reqs, width] allocator pages in position order
+    const int32_t *prefix_lens;
+    const int32_t *v2p;
+    int32_t *out;  // [num_reqs, width] kernel-facing page indices
+    uint32_t *flags;
+    int64_t width;
+    int64_t entries;
+    int64_t v2p_len;
+    int64_t ps;
+    int64_t bpp;
+    int64_t num_pages;
+};
+
+// Entry i of request r is translated when it holds a prefix position
+// (i < ceil(len / ps)), through v2p when given: negative or unmapped -> 0,
+// past the table or the pool -> 0 plus UKV_FLAG_SLOT_RANGE, else
+// phys * blocks_per_page.  Entries past the prefix are written 0 and never
+// read.  A prefix needing more than `width` entries raises UKV_FLAG_LAYOUT.
+__global__ __launch_bounds__(kBlock) void build_page_table_kernel(TableArgs a) {
+    const int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (e >= a.entries) return;
+    const int64_t r = e / a.width;
+    const int64_t i = e - r * a.width;
+    const int64_t len = a.prefix_lens[r];
+    const int64_t used = len > 0 ? (len + a.ps - 1) / a.ps : 0;
+    if (i == 0 && used > a.width) atomicOr(a.flags, UKV_FLAG_LAYOUT);
+    int32_t kp = 0;
+    bool out_of_range = false;
+    if (i < used) {
+        const int64_t q = a.req_pages[e];
+        if (q >= 0) {
+            int64_t phys = q;
+            if (a.v2p != nullptr) {
+                if (q >= a.v2p_len) {
+                    out_of_range = true;
+                    phys = -1;
+                } else {
+                    phys = a.v2p[q];
+                }
+            }
+            if (phys >= a.num_pages)
+                out_of_range = true;
+            else if (phys >= 0)
+                kp = (int32_t)(phys * a.bpp);
+        }
+    }
+    a.out[e] = kp;
+    if (out_of_range) atomicOr(a.flags, UKV_FLAG_SLOT_RANGE);
+}
+
+// ----------------------------------------------------------------------------
+// decode attention
+// ----------------------------------------------------------------------------
+struct AttnArgs {
+    const uint8_t *pool;
+    uint64_t k_base;     // byte offset of the layer's K view (row 0)
+    uint64_t v_base;     // byte offset of the layer's V view
+    uint32_t row_bytes;  // head_num * head_dim * 2
+    uint32_t ps;
+    uint32_t bpp;
+    uint32_t num_pages;
+    const uint16_t *q;  // [num_reqs, head_num * G, D] bf16
+    const int32_t *bt;  // [num_reqs, bt_stride] kernel-facing page indices
+    int64_t bt_stride;
+    const int32_t *seq_lens;
+    int32_t num_reqs;
+    int32_t heads;  // KV heads
+    int32_t window;
+    int32_t max_seq_len;
+    int32_t max_chunks;
+    float scale_log2;  // softmax scale * log2(e)
+    float *part_o;     // [num_reqs, max_chunks, heads, G, D]
+    float *part_ml;    // [num_reqs, max_chunks, heads, G, 2]: running max (log2 units), row sum; sum < 0 marks a bad chunk
+    float *out;        // [num_reqs, heads * G, D] fp32
+    uint32_t *flags;
+};
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// Positions [j0, len) of a request: the last `window` ones for a windowed layer.
+__device__ __forceinline__ int32_t first_position(int32_t len, int32_t window) {
+    return (window > 0 && len > window) ? len - window : 0;
+}
+
+// Dense-view row of position j of request r, or -1 (with *bad set) when its
+// table column is past the table or its entry is not a kernel-facing page.
+__device__ __forceinline__ int32_t row_of(const AttnArgs &a, int32_t r, int32_t j, bool *bad) {
+    const uint32_t col = (uint32_t)j / a.ps;
+    if ((int64_t)col >= a.bt_stride) {
+        *bad = true;
+        return -1;
+    }
+    const int32_t kp = a.bt[(int64_t)r * a.bt_stride + col];
+    if (kp < 0 || (uint32_t)kp % a.bpp != 0 || (uint32_t)kp / a.bpp >= a.num_pages) {
+        *bad = true;
+        return -1;
+    }
+    return (int32_t)((uint32_t)kp * a.ps + ((uint32_t)j - col * a.ps));  // < n_rows < 2^31
+}
+
+__device__ __forceinline__ u32x4 load16(const uint8_t *p) { return *(const u32x4 *)p; }
+
+// bf16 pair in one 32-bit word -> two floats (exact).
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int G, int D>
+__global__ __launch_bounds__(kBlock) void attn_chunk_kernel(AttnArgs a) {
+    static_assert(D % 32 == 0 && D >= 64 && D <= 256, "head_dim");
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group");
+    constexpr int KS = D / 32;   // MFMA k-steps per tile
+    constexpr int DL = D / 16;   // V elements per lane per position
+    constexpr int VL = DL / 8;   // 16-byte V loads per lane per position (D >= 128)
+    constexpr int VH = DL < 8 ? 1 : VL;
+    const int lane = lane_id();
+    const int grp = lane >> 4;   // position group of this lane (0..3)
+    const int col = lane & 15;   // MFMA column: position (K operand) and query head (Q operand)
+
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int64_t per_req = (int64_t)a.max_chunks * a.heads;
+    const int32_t r = (int32_t)(wave / per_req);
+    if (r >= a.num_reqs) return;
+    const int32_t rem = (int32_t)(wave - (int64_t)r * per_req);
+    const int32_t c = rem / a.heads;
+    const int32_t h = rem - c * a.heads;
+    const int32_t len = a.seq_lens[r];
+    if (len <= 0 || len > a.max_seq_len) return;
+    const int32_t j0 = first_position(len, a.window);
+    const int32_t pbeg = j0 + c * kChunk;
+    if (pbeg >= len) return;
+    const int32_t pend = min(len, pbeg + kChunk);
+    const int32_t tiles = (pend - pbeg + kTile - 1) / kTile;
+
+    // Q as the B operand: column col holds query head (col % G) of KV head h;
+    // lane group grp holds dims [8 (4 s + grp), +8) at k-step s.
+    const int qhead = h * G + (col % G);
+    const uint16_t *qrow = a.q + ((int64_t)r * a.heads * G + qhead) * D;
+    bf16x8 qb[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * s + grp)));
+
+    const uint8_t *kview = a.pool + a.k_base + (uint64_t)h * D * 2;
+    const uint8_t *vview = a.pool + a.v_base + (uint64_t)h * D * 2 + (uint64_t)col * DL * 2;
+
+    // Tile t: lane resolves the row of position pbeg + 16 t + col (its K
+    // position); -1 past the chunk.
+    bool bad = false;
+    auto lookup = [&](int t) -> int32_t {
+        const int32_t j = pbeg + t * kTile + col;
+        return j < pend ? row_of(a, r, j, &bad) : -1;
+    };
+    u32x4 kreg[KS];
+    u32x4 vreg[4][VH] = {};
+    uint64_t vlo[4] = {};  // D = 64: 8 bytes per lane
+    auto load_tile = [&](int32_t krow) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            kreg[s] = krow >= 0 ? load16(kview + (uint64_t)(uint32_t)krow * a.row_bytes + 16 * (4 * s + grp))
+                                : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int32_t vrow = __shfl(krow, 4 * grp + t);
+            const uint8_t *p = vview + (uint64_t)(uint32_t)(vrow < 0 ? 0 : vrow) * a.row_bytes;
+            if constexpr (DL >= 8) {
+#pragma unroll
+                for (int v = 0; v < VH; ++v) vreg[t][v] = vrow >= 0 ? load16(p + 16 * v) : u32x4{0, 0, 0, 0};
+            } else {
+                vlo[t] = vrow >= 0 ? *(const uint64_t *)p : 0ull;
+            }
+        }
+    };
+
+    float acc[G][DL];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int d = 0; d < DL; ++d) acc[g][d] = 0.0f;
+    float m_run = -INFINITY;  // running max of this lane's query head, log2 units
+    float l_run = 0.0f;       // row sum over this lane's positions
+
+    int32_t krow = lookup(0);
+    if (__any(bad)) {
+        atomicOr(a.flags, UKV_FLAG_BAD_BLOCK);
+        if (lane < G) a.part_ml[((((int64_t)r * a.max_chunks + c) * a.heads + h) * G + lane) * 2 + 1] = -1.0f;
+        return;
+    }
+    load_tile(krow);
+    for (int t = 0; t < tiles; ++t) {
+        // scores of this tile
+        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[s]), qb[s], sacc, 0, 0, 0);
+        u32x4 vcur[4][VH] = {};
+        uint64_t vcur_lo[4] = {};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (DL >= 8) {
+#pragma unroll
+                for (int v = 0; v < VH; ++v) vcur[i][v] = vreg[i][v];
+            } else {
+                vcur_lo[i] = vlo[i];
+            }
+        }
+        // next tile's rows and loads go out before this tile's arithmetic
+        if (t + 1 < tiles) {
+            krow = lookup(t + 1);
+            if (__any(bad)) {
+                atomicOr(a.flags, UKV_FLAG_BAD_BLOCK);
+                if (lane < G)
+                    a.part_ml[((((int64_t)r * a.max_chunks + c) * a.heads + h) * G + lane) * 2 + 1] = -1.0f;
+                return;
+            }
+            load_tile(krow);
+        }
+        const int32_t tile0 = pbeg + t * kTile + 4 * grp;
+        float x[4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = tile0 + i < pend ? sacc[i] * a.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, x[i]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const bool need = tmax > m_run + kRescaleGap;
+        if (__any(need)) {
+            const float alpha = need ? exp2f(m_run - tmax) : 1.0f;
+            if (need) m_run = tmax;
+            l_run *= alpha;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float ag = __shfl(alpha, g);
+#pragma unroll
+                for (int d = 0; d < DL; ++d) acc[g][d] *= ag;
+            }
+        }
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = exp2f(x[i] - m_run);
+            l_run += p[i];
+        }
+        // P V: position 4 grp + i of the tile, dims [col * DL, +DL) of every head
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float vf[DL];
+            if constexpr (DL >= 8) {
+#pragma unroll
+                for (int v = 0; v < VH; ++v)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        vf[8 * v + 2 * w] = lo_bf16(vcur[i][v][w]);
+                        vf[8 * v + 2 * w + 1] = hi_bf16(vcur[i][v][w]);
+                    }
+            } else {
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const uint32_t word = (uint32_t)(vcur_lo[i] >> (32 * w));
+                    vf[2 * w] = lo_bf16(word);
+                    vf[2 * w + 1] = hi_bf16(word);
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float pg = __shfl(p[i], 16 * grp + g);
+#pragma unroll
+                for (int d = 0; d < DL; ++d) acc[g][d] = fmaf(pg, vf[d], acc[g][d]);
+            }
+        }
+    }
+    // sum the four position groups
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int d = 0; d < DL; ++d) {
+            acc[g][d] += __shfl_xor(acc[g][d], 16);
+            acc[g][d] += __shfl_xor(acc[g][d], 32);
+        }
+    const int64_t unit = ((int64_t)r * a.max_chunks + c) * a.heads + h;
+    if (lane < 16) {
+        float *po = a.part_o + unit * G * D + col * DL;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int d = 0; d < DL; d += 4)
+                *(f32x4 *)(po + g * D + d) = f32x4{acc[g][d], acc[g][d + 1], acc[g][d + 2], acc[g][d + 3]};
+    }
+    if (lane < G) {
+        a.part_ml[(unit * G + lane) * 2] = m_run;
+        a.part_ml[(unit * G + lane) * 2 + 1] = l_run;
+    }
+}
+
+// Merge the chunks of (request, KV head): out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+// A bad chunk, a request past max_seq_len (UKV_FLAG_LAYOUT) or an empty one
+// gives zeros.
+template <int G, int D>
+__global__ __launch_bounds__(kWave) void attn_combine_kernel(AttnArgs a) {
+    const int lane = lane_id();
+    const int32_t r = (int32_t)(blockIdx.x / (uint32_t)a.heads);
+    const int32_t h = (int32_t)(blockIdx.x - (uint32_t)r * a.heads);
+    float *o = a.out + ((int64_t)r * a.heads + h) * G * D;
+    const int32_t len = a.seq_lens[r];
+    int32_t chunks = 0;
+    if (len > a.max_seq_len) {
+        if (h == 0 && lane == 0) atomicOr(a.flags, UKV_FLAG_LAYOUT);
+    } else if (len > 0) {
+        const int32_t n = len - first_position(len, a.window);
+        chunks = (n + kChunk - 1) / kChunk;
+    }
+    const int64_t unit0 = (int64_t)r * a.max_chunks * a.heads + h;  // chunk c: unit0 + c * heads
+    bool bad = false;
+    for (int c = 0; c < chunks; ++c)
+        for (int g = 0; g < G; ++g) bad |= a.part_ml[((unit0 + (int64_t)c * a.heads) * G + g) * 2 + 1] < 0.0f;
+    for (int e = lane; e < G * D; e += kWave) {
+        const int g = e / D;
+        float res = 0.0f;
+        if (chunks > 0 && !bad) {
+            float mx = -INFINITY;
+            for (int c = 0; c < chunks; ++c)
+                mx = fmaxf(mx, a.part_ml[((unit0 + (int64_t)c * a.heads) * G + g) * 2]);
+            float num = 0.0f, den = 0.0f;
+            for (int c = 0; c < chunks; ++c) {
+                const int64_t u = unit0 + (int64_t)c * a.heads;
+                const float w = exp2f(a.part_ml[(u * G + g) * 2] - mx);
+                den = fmaf(w, a.part_ml[(u * G + g) * 2 + 1], den);
+                num = fmaf(w, a.part_o[u * G * D + e], num);
+            }
+            res = num / den;
+        }
+        o[e] = res;
+    }
+}
+
+int64_t max_chunks_for(int32_t max_seq_len, int32_t window) {
+    const int64_t n = (window > 0 && window < max_seq_len) ? window : max_seq_len;
+    return n > 0 ? (n + kChunk - 1) / kChunk : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ukv_build_page_table(const ukv_pool *pool, int32_t sub, const int32_t *req_pages_dev, int64_t bt_stride,
+                         const int32_t *prefix_lens_dev, int32_t num_reqs, const int32_t *v2p_dev, int64_t v2p_len,
+                         int32_t *out_dev, hipStream_t stream) {
+    const char *who = "ukv_build_page_table";
+    int rc = check_pool_call(pool, sub, who);
+    if (rc != UKV_OK) return rc;
+    if (num_reqs < 0 || bt_stride < 0) return fail(UKV_ERR_INVALID_ARG, "%s: negative size", who);
+    if (v2p_dev != nullptr && v2p_len < 0) return fail(UKV_ERR_INVALID_ARG, "%s: v2p_len < 0", who);
+    const int64_t entries = (int64_t)num_reqs * bt_stride;
+    if (entries == 0) return UKV_OK;
+    if (req_pages_dev == nullptr || prefix_lens_dev == nullptr || out_dev == nullptr)
+        return fail(UKV_ERR_INVALID_ARG, "%s: null page lists, lengths or output", who);
+    const uint64_t bytes = (uint64_t)entries * sizeof(int32_t);
+    if ((const void *)out_dev != (const void *)req_pages_dev && ranges_overlap(out_dev, bytes, req_pages_dev, bytes))
+        return fail(UKV_ERR_INVALID_ARG, "%s: output overlaps the page lists (same buffer or disjoint)", who);
+    if (ranges_overlap(out_dev, bytes, prefix_lens_dev, (uint64_t)num_reqs * 4) ||
+        (v2p_dev != nullptr && ranges_overlap(out_dev, bytes, v2p_dev, (uint64_t)v2p_len * 4)))
+        return fail(UKV_ERR_INVALID_ARG, "%s: output overlaps the lengths or the v2p table", who);
+    const int64_t grid = (entries + kBlock - 1) / kBlock;
+    if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: table too large for one launch", who);
+    TableArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.req_pages = req_pages_dev;
+    a.prefix_lens = prefix_lens_dev;
+    a.v2p = v2p_dev;
+    a.out = out_dev;
+    a.flags = pool->flags_dev;
+    a.width = bt_stride;
+    a.entries = entries;
+    a.v2p_len = v2p_dev == nullptr ? 0 : v2p_len;
+    a.ps = pool->plan.page_size;
+    a.bpp = pool->plan.sub[sub].blocks_per_page;
+    a.num_pages = pool->spec[sub].num_pages;
+    hipLaunchKernelGGL(build_page_table_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+    return check_launch(who);
+}
+
+uint64_t ukv_decode_attention_workspace_bytes(int32_t num_reqs, int32_t q_heads, int32_t head_dim,
+                                              int32_t max_seq_len, int32_t window) {
+    if (num_reqs <= 0 || q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) return 0;
+    return (uint64_t)num_reqs * (uint64_t)max_chunks_for(max_seq_len, window < 0 ? 0 : window) * (uint64_t)q_heads *
+           ((uint64_t)head_dim + 2) * sizeof(float);
+}
+
+int ukv_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const void *q_dev, int32_t q_heads,
+                         const int32_t *block_table_dev, int64_t bt_stride, const int32_t *seq_lens_dev,
+                         int32_t num_reqs, int32_t max_seq_len, int32_t window, float scale, float *out_dev,
+                         void *workspace_dev, uint64_t workspace_bytes, hipStream_t stream) {
+    const char *who = "ukv_decode_attention";
+    int rc = check_pool_call(pool, sub, who);
+    if (rc != UKV_OK) return rc;
+    const ukv_subpool_spec &s = pool->spec[sub];
+    const ukv_subpool_plan &p = pool->plan.sub[sub];
+    if (s.kind != UKV_MHA) return fail(UKV_ERR_INVALID_ARG, "%s: sub-pool %d is not MHA", who, sub);
+    if (s.elem_bytes != 2) return fail(UKV_ERR_INVALID_ARG, "%s: K / V must be bf16 (itemsize %d)", who, s.elem_bytes);
+    if (layer < 0 || layer >= s.layer_num)
+        return fail(UKV_ERR_INVALID_ARG, "%s: layer %d outside [0, %d)", who, layer, s.layer_num);
+    const int D = s.head_dim;
+    if (D != 64 && D != 128 && D != 256) return fail(UKV_ERR_INVALID_ARG, "%s: head_dim %d not 64, 128 or 256", who, D);
+    if (q_heads <= 0 || q_heads % s.head_num != 0)
+        return fail(UKV_ERR_INVALID_ARG, "%s: q_heads %d is not a multiple of head_num %d", who, q_heads, s.head_num);
+    const int G = q_heads / s.head_num;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(UKV_ERR_INVALID_ARG, "%s: %d query heads per KV head (supported: 1, 2, 4, 8)", who, G);
+    if (num_reqs < 0 || window < 0 || max_seq_len < 0 || bt_stride < 0)
+        return fail(UKV_ERR_INVALID_ARG, "%s: negative size", who);
+    if (!std::isfinite(scale)) return fail(UKV_ERR_INVALID_ARG, "%s: scale is not finite", who);
+    if (num_reqs == 0) return UKV_OK;
+    if (q_dev == nullptr || seq_lens_dev == nullptr || out_dev == nullptr)
+        return fail(UKV_ERR_INVALID_ARG, "%s: null q, seq_lens or output", who);
+    if (((uintptr_t)q_dev % 16) != 0 || ((uintptr_t)out_dev % 16) != 0)
+        return fail(UKV_ERR_ALIGNMENT, "%s: q and out must be 16-byte aligned", who);
+    ukv_view vk, vv;
+    ukv::view_of(pool->plan, s, sub, layer, 0, &vk);
+    ukv::view_of(pool->plan, s, sub, layer, 1, &vv);
+    if (((uintptr_t)pool->raw + vk.byte_offset) % 16 != 0 || ((uintptr_t)pool->raw + vv.byte_offset) % 16 != 0)
+        return fail(UKV_ERR_ALIGNMENT, "%s: the layer's views are not 16-byte aligned", who);
+    const int64_t chunks = max_chunks_for(max_seq_len, window);
+    const uint64_t need = ukv_decode_attention_workspace_bytes(num_reqs, q_heads, D, max_seq_len, window);
+    if (chunks > 0) {
+        if (block_table_dev == nullptr || bt_stride < 1)
+            return fail(UKV_ERR_INVALID_ARG, "%s: null block table or bt_stride < 1", who);
+        if (workspace_dev == nullptr || workspace_bytes < need)
+            return fail(UKV_ERR_INVALID_ARG, "%s: workspace of %llu bytes, %llu needed", who,
+                        (unsigned long long)workspace_bytes, (unsigned long long)need);
+        if (((uintptr_t)workspace_dev % 16) != 0)
+            return fail(UKV_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", who);
+    }
+    const uint64_t out_bytes = (uint64_t)num_reqs * q_heads * D * sizeof(float);
+    if (ranges_overlap(out_dev, out_bytes, q_dev, (uint64_t)num_reqs * q_heads * D * 2) ||
+        ranges_overlap(out_dev, out_bytes, workspace_dev, need) ||
+        ranges_overlap(out_dev, out_bytes, pool->raw, pool->raw_bytes))
+        return fail(UKV_ERR_INVALID_ARG, "%s: output overlaps q, the workspace or the pool", who);
+    const int64_t waves = (int64_t)num_reqs * chunks * s.head_num;
+    const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (grid > kMaxGrid || (int64_t)num_reqs * s.head_num > kMaxGrid)
+        return fail(UKV_ERR_INVALID_ARG, "%s: batch too large for one launch", who);
+    AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.pool = pool->raw;
+    a.k_base = vk.byte_offset;
+    a.v_base = vv.byte_offset;
+    a.row_bytes = (uint32_t)p.row_bytes;
+    a.ps = (uint32_t)pool->plan.page_size;
+    a.bpp = (uint32_t)p.blocks_per_page;
+    a.num_pages = (uint32_t)s.num_pages;
+    a.q = (const uint16_t *)q_dev;
+    a.bt = block_table_dev;
+    a.bt_stride = bt_stride;
+    a.seq_lens = seq_lens_dev;
+    a.num_reqs = num_reqs;
+    a.heads = s.head_num;
+    a.window = window;
+    a.max_seq_len = max_seq_len;
+    a.max_chunks = (int32_t)chunks;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    float *ws = (float *)workspace_dev;
+    a.part_o = ws;
+    a.part_ml = ws == nullptr ? nullptr : ws + (uint64_t)num_reqs * chunks * q_heads * D;
+    a.out = out_dev;
+    a.flags = pool->flags_dev;
+    auto launch = [&](auto gtag, auto dtag) {
+        constexpr int GG = decltype(gtag)::value;
+        constexpr int DD = decltype(dtag)::value;
+        if (grid > 0) hipLaunchKernelGGL((attn_chunk_kernel<GG, DD>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        hipLaunchKernelGGL((attn_combine_kernel<GG, DD>), dim3((unsigned)(num_reqs * s.head_num)), dim3(kWave), 0,
+                           stream, a);
+        return check_launch(who);
+    };
+    auto by_dim = [&](auto gtag) {
+        switch (D) {
+            case 64: return launch(gtag, std::integral_constant<int, 64>());
+            case 128: return launch(gtag, std::integral_constant<int, 128>());
+            default: return launch(gtag, std::integral_constant<int, 256>());
+        }
+    };
+    switch (G) {
+        case 1: return by_dim(std::integral_constant<int, 1>());
+        case 2: return by_dim(std::integral_constant<int, 2>());
+        case 4: return by_dim(std::integral_constant<int, 4>());
+        default: return by_dim(std::integral_constant<int, 8>());
+    }
+}
+
+}  // extern "C"

@@ -6,12 +6,19 @@
 
 #include <cstdint>
 
+struct ukv_pool;
+
 namespace ukv {
 
 // Records a thread-local message for ukv_last_error() and returns `code`.
 int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 const char *last_error();
+
+// Host-side checks shared by the entry points.
+int check_pool_call(const ukv_pool *pool, int32_t sub, const char *who);  // pool, sub-pool, current device
+int check_launch(const char *who);                                       // hipGetLastError after a launch
+bool ranges_overlap(const void *a, uint64_t na, const void *b, uint64_t nb);
 
 int plan_pool(const ukv_subpool_spec *specs, int32_t n_specs, int64_t page_size, ukv_plan *out);
 int view_of(const ukv_plan &p, const ukv_subpool_spec &s, int32_t sub, int32_t layer, int32_t kv, ukv_view *out);

@@ -57,9 +57,33 @@ void clear_error() { g_last_error[0] = '\0'; }
 
 const char *last_error() { return g_last_error; }
 
+int check_pool_call(const ukv_pool *pool, int32_t sub, const char *who) {
+    if (pool == nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: null pool", who);
+    if (sub < 0 || sub >= pool->plan.n_sub)
+        return fail(UKV_ERR_INVALID_ARG, "%s: sub-pool %d outside [0, %d)", who, sub, pool->plan.n_sub);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != pool->device)
+        return fail(UKV_ERR_INVALID_ARG, "%s: current device %d is not the pool's device %d", who, dev, pool->device);
+    return UKV_OK;
+}
+
+int check_launch(const char *who) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(UKV_ERR_HIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
+    return UKV_OK;
+}
+
+bool ranges_overlap(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na != 0 && nb != 0 && x < y + nb && y < x + na;
+}
+
 }  // namespace ukv
 
+using ukv::check_launch;
+using ukv::check_pool_call;
 using ukv::fail;
+using ukv::ranges_overlap;
 
 namespace {
 
@@ -582,27 +606,6 @@ int vec_bytes_for(std::initializer_list<uint64_t> values) {
         while (acc > 1 && (v % acc) != 0) acc >>= 1;
     }
     return (int)acc;
-}
-
-int check_pool_call(const ukv_pool *pool, int32_t sub, const char *who) {
-    if (pool == nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: null pool", who);
-    if (sub < 0 || sub >= pool->plan.n_sub)
-        return fail(UKV_ERR_INVALID_ARG, "%s: sub-pool %d outside [0, %d)", who, sub, pool->plan.n_sub);
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev != pool->device)
-        return fail(UKV_ERR_INVALID_ARG, "%s: current device %d is not the pool's device %d", who, dev, pool->device);
-    return UKV_OK;
-}
-
-int check_launch(const char *who) {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(UKV_ERR_HIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
-    return UKV_OK;
-}
-
-bool ranges_overlap(const void *a, uint64_t na, const void *b, uint64_t nb) {
-    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-    return na != 0 && nb != 0 && x < y + nb && y < x + na;
 }
 
 template <int NKV, typename F>
