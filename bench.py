@@ -436,7 +436,7 @@ class GpuRunner:
             self.t["q0"] = q
             mx = max(op.args["max_len"] for op in script.ops if op.kind == "attention")
             self.t["attn_out"] = torch.empty(q.shape, dtype=torch.float32, device=device)
-            need = U.ukv_decode_attention_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], mx, 0)
+            need = U.ukv_decode_attention_workspace_bytes(self.pool, 0, q.shape[0], q.shape[1], mx, 0)
             self.t["attn_ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
         for op in script.ops:  # int32 outputs of the translations, shaped like their inputs
             if "out" in op.args and op.args["out"] not in self.t:

@@ -375,8 +375,13 @@ int ukv_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const
                          int32_t num_reqs, int32_t max_seq_len, int32_t window, float scale, float *out_dev,
                          void *workspace_dev, uint64_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes ukv_decode_attention needs for these sizes (0 when none). */
-uint64_t ukv_decode_attention_workspace_bytes(int32_t num_reqs, int32_t q_heads, int32_t head_dim,
+/*
+ * Workspace bytes ukv_decode_attention needs on this sub-pool for these
+ * sizes (0 when none, or for a bad pool / sub-pool).  The call splits each
+ * request into units of up to 1,024 positions, fewer when the batch is small,
+ * so the size depends on num_reqs, max_seq_len and window together.
+ */
+uint64_t ukv_decode_attention_workspace_bytes(const ukv_pool *pool, int32_t sub, int32_t num_reqs, int32_t q_heads,
                                               int32_t max_seq_len, int32_t window);
 
 /*

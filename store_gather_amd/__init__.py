@@ -119,7 +119,7 @@ def _load() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
-    L.ukv_decode_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.ukv_decode_attention_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32]
     L.ukv_decode_attention_workspace_bytes.restype = u64
     L.ukv_last_error.argtypes = []
     L.ukv_last_error.restype = ctypes.c_char_p
@@ -506,9 +506,9 @@ def ukv_build_page_table(pool: Pool, sub: int, req_pages: torch.Tensor, prefix_l
     return out
 
 
-def ukv_decode_attention_workspace_bytes(num_reqs: int, q_heads: int, head_dim: int, max_seq_len: int,
+def ukv_decode_attention_workspace_bytes(pool: Pool, sub: int, num_reqs: int, q_heads: int, max_seq_len: int,
                                          window: int = 0) -> int:
-    return int(_lib.ukv_decode_attention_workspace_bytes(num_reqs, q_heads, head_dim, max_seq_len, window))
+    return int(_lib.ukv_decode_attention_workspace_bytes(pool.handle, sub, num_reqs, q_heads, max_seq_len, window))
 
 
 def ukv_decode_attention(pool: Pool, sub: int, layer: int, q: torch.Tensor, block_table: torch.Tensor,
@@ -535,7 +535,7 @@ def ukv_decode_attention(pool: Pool, sub: int, layer: int, q: torch.Tensor, bloc
     _dev_ptr(out, "out", d, torch.float32)
     if tuple(out.shape) != (num_reqs, q_heads, head_dim) or not out.is_contiguous():
         raise ValueError("out must be a contiguous fp32 tensor shaped like q")
-    need = ukv_decode_attention_workspace_bytes(num_reqs, q_heads, head_dim, max_seq_len, window)
+    need = ukv_decode_attention_workspace_bytes(pool, sub, num_reqs, q_heads, max_seq_len, window)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=d)
     _dev_ptr(workspace, "workspace", d)

@@ -14,7 +14,7 @@
 // head, bf16 K / V / Q, fp32 accumulation and output):
 //
 //  - split-K over positions ("flash decoding"): one 64-lane wave owns
-//    (request, KV head, chunk of kChunk positions) and writes an unnormalised
+//    (request, KV head, chunk of up to 1,024 positions) and writes an unnormalised
 //    partial (running max, row sum, G x D sums) to a workspace; a second,
 //    small kernel merges the chunks of each (request, KV head).  Tens of
 //    thousands of waves for a decode batch, whatever the length mix.
@@ -53,10 +53,11 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
-constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int64_t kMaxGrid = 0x7fffffff;
 constexpr int kTile = 16;        // positions per MFMA tile
-constexpr int kChunk = 256;      // positions per wave (split-K unit)
+constexpr int kMaxChunk = 1024;  // positions per wave (split-K unit), at most
+constexpr int kMinChunk = 128;
+constexpr int64_t kBusyWaves = 4096;  // about 1.3 x the waves MI355X holds at this kernel's occupancy
 constexpr float kRescaleGap = 8.0f;  // log2 headroom before the running max moves
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -137,7 +138,9 @@ struct AttnArgs {
     int32_t window;
     int32_t max_seq_len;
     int32_t max_chunks;
+    int32_t chunk;     // positions per split-K unit, a multiple of 16
     float scale_log2;  // softmax scale * log2(e)
+    double inv_bpp;    // 1 / blocks_per_page
     float *part_o;     // [num_reqs, max_chunks, heads, G, D]
     float *part_ml;    // [num_reqs, max_chunks, heads, G, 2]: running max (log2 units), row sum; sum < 0 marks a bad chunk
     float *out;        // [num_reqs, heads * G, D] fp32
@@ -151,54 +154,71 @@ __device__ __forceinline__ int32_t first_position(int32_t len, int32_t window) {
     return (window > 0 && len > window) ? len - window : 0;
 }
 
-// Dense-view row of position j of request r, or -1 (with *bad set) when its
-// table column is past the table or its entry is not a kernel-facing page.
-__device__ __forceinline__ int32_t row_of(const AttnArgs &a, int32_t r, int32_t j, bool *bad) {
-    const uint32_t col = (uint32_t)j / a.ps;
-    if ((int64_t)col >= a.bt_stride) {
-        *bad = true;
-        return -1;
-    }
-    const int32_t kp = a.bt[(int64_t)r * a.bt_stride + col];
-    if (kp < 0 || (uint32_t)kp % a.bpp != 0 || (uint32_t)kp / a.bpp >= a.num_pages) {
-        *bad = true;
-        return -1;
-    }
-    return (int32_t)((uint32_t)kp * a.ps + ((uint32_t)j - col * a.ps));  // < n_rows < 2^31
-}
-
 __device__ __forceinline__ u32x4 load16(const uint8_t *p) { return *(const u32x4 *)p; }
 
 // bf16 pair in one 32-bit word -> two floats (exact).
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
+}
+
+// e is a multiple of bpp: floor(e * (1 / bpp)) in double is off by at most one
+// for e < 2^31, fixed by one correction step; no integer division.
+__device__ __forceinline__ bool multiple_of(int32_t e, int32_t bpp, double inv_bpp) {
+    int32_t q = (int32_t)((double)e * inv_bpp);
+    int32_t r = e - q * bpp;
+    if (r < 0) r += bpp;
+    if (r >= bpp) r -= bpp;
+    return r == 0;
+}
+
+template <int G>
+__device__ __forceinline__ float p_of_head(float p, int g) {
+    // p of head g at this lane's position: lane g of the lane's row holds it
+    switch (g) {
+        case 0: return row_bcast<0>(p);
+        case 1: return row_bcast<1>(p);
+        case 2: return row_bcast<2>(p);
+        case 3: return row_bcast<3>(p);
+        case 4: return row_bcast<4>(p);
+        case 5: return row_bcast<5>(p);
+        case 6: return row_bcast<6>(p);
+        default: return row_bcast<7>(p);
+    }
+}
+
 template <int G, int D>
-__global__ __launch_bounds__(kBlock) void attn_chunk_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kWave) void attn_chunk_kernel(AttnArgs a) {
     static_assert(D % 32 == 0 && D >= 64 && D <= 256, "head_dim");
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group");
     constexpr int KS = D / 32;   // MFMA k-steps per tile
     constexpr int DL = D / 16;   // V elements per lane per position
-    constexpr int VL = DL / 8;   // 16-byte V loads per lane per position (D >= 128)
-    constexpr int VH = DL < 8 ? 1 : VL;
+    constexpr int VH = DL < 8 ? 1 : DL / 8;  // 16-byte V loads per lane per position
     const int lane = lane_id();
     const int grp = lane >> 4;   // position group of this lane (0..3)
     const int col = lane & 15;   // MFMA column: position (K operand) and query head (Q operand)
 
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-    const int64_t per_req = (int64_t)a.max_chunks * a.heads;
-    const int32_t r = (int32_t)(wave / per_req);
-    if (r >= a.num_reqs) return;
-    const int32_t rem = (int32_t)(wave - (int64_t)r * per_req);
-    const int32_t c = rem / a.heads;
-    const int32_t h = rem - c * a.heads;
+    // one wave per block; chunk-major order: every request's chunk 0 first,
+    // so the last waves are the late chunks of the longest requests
+    const int64_t wave = blockIdx.x;
+    const int64_t per_chunk = (int64_t)a.num_reqs * a.heads;
+    const int32_t c = (int32_t)(wave / per_chunk);
+    if (c >= a.max_chunks) return;
+    const int32_t rem = (int32_t)(wave - (int64_t)c * per_chunk);
+    const int32_t r = rem / a.heads;
+    const int32_t h = rem - r * a.heads;
     const int32_t len = a.seq_lens[r];
     if (len <= 0 || len > a.max_seq_len) return;
     const int32_t j0 = first_position(len, a.window);
-    const int32_t pbeg = j0 + c * kChunk;
+    const int32_t pbeg = j0 + c * a.chunk;
     if (pbeg >= len) return;
-    const int32_t pend = min(len, pbeg + kChunk);
+    const int32_t pend = min(len, pbeg + a.chunk);
     const int32_t tiles = (pend - pbeg + kTile - 1) / kTile;
+    const int64_t unit = ((int64_t)r * a.max_chunks + c) * a.heads + h;
 
     // Q as the B operand: column col holds query head (col % G) of KV head h;
     // lane group grp holds dims [8 (4 s + grp), +8) at k-step s.
@@ -211,13 +231,44 @@ __global__ __launch_bounds__(kBlock) void attn_chunk_kernel(AttnArgs a) {
     const uint8_t *kview = a.pool + a.k_base + (uint64_t)h * D * 2;
     const uint8_t *vview = a.pool + a.v_base + (uint64_t)h * D * 2 + (uint64_t)col * DL * 2;
 
-    // Tile t: lane resolves the row of position pbeg + 16 t + col (its K
-    // position); -1 past the chunk.
-    bool bad = false;
-    auto lookup = [&](int t) -> int32_t {
-        const int32_t j = pbeg + t * kTile + col;
-        return j < pend ? row_of(a, r, j, &bad) : -1;
+    // The lane's K position in tile t is pbeg + 16 t + col; its table column
+    // and page offset advance by 16 positions per tile without a division.
+    const uint32_t ps = a.ps;
+    const uint32_t q16 = (uint32_t)kTile / ps, r16 = (uint32_t)kTile - q16 * ps;
+    const int32_t *bt_row = a.bt + (int64_t)r * a.bt_stride;
+    const int32_t entry_lim = (int32_t)(a.num_pages * a.bpp);  // num_pages * bpp * ps < 2^31
+    struct Pos {
+        int32_t j;
+        uint32_t col, off;
     };
+    auto advance = [&](Pos p) {
+        p.j += kTile;
+        p.col += q16;
+        p.off += r16;
+        if (p.off >= ps) {
+            p.off -= ps;
+            ++p.col;
+        }
+        return p;
+    };
+    // table entry of a position (a load), -1 past the table; nothing past the chunk
+    auto entry = [&](const Pos &p) -> int32_t {
+        return (p.j < pend && (int64_t)p.col < a.bt_stride) ? bt_row[p.col] : -1;
+    };
+    bool bad = false;
+    auto row_of = [&](const Pos &p, int32_t e) -> int32_t {
+        if (p.j >= pend) return -1;
+        if (e < 0 || e >= entry_lim || !multiple_of(e, (int32_t)a.bpp, a.inv_bpp)) {
+            bad = true;
+            return -1;
+        }
+        return e * (int32_t)ps + (int32_t)p.off;  // < n_rows < 2^31
+    };
+    auto bad_chunk = [&]() {
+        atomicOr(a.flags, UKV_FLAG_BAD_BLOCK);
+        if (lane < G) a.part_ml[(unit * G + lane) * 2 + 1] = -1.0f;
+    };
+
     u32x4 kreg[KS];
     u32x4 vreg[4][VH] = {};
     uint64_t vlo[4] = {};  // D = 64: 8 bytes per lane
@@ -247,12 +298,16 @@ __global__ __launch_bounds__(kBlock) void attn_chunk_kernel(AttnArgs a) {
     float m_run = -INFINITY;  // running max of this lane's query head, log2 units
     float l_run = 0.0f;       // row sum over this lane's positions
 
-    int32_t krow = lookup(0);
-    if (__any(bad)) {
-        atomicOr(a.flags, UKV_FLAG_BAD_BLOCK);
-        if (lane < G) a.part_ml[((((int64_t)r * a.max_chunks + c) * a.heads + h) * G + lane) * 2 + 1] = -1.0f;
-        return;
-    }
+    // prologue: entries of tiles 0 and 1, loads of tile 0
+    Pos p0;
+    p0.j = pbeg + col;
+    p0.col = (uint32_t)p0.j / ps;
+    p0.off = (uint32_t)p0.j - p0.col * ps;
+    const int32_t e0 = entry(p0);
+    Pos p1 = advance(p0);
+    int32_t e1 = entry(p1);
+    int32_t krow = row_of(p0, e0);
+    if (__any(bad)) return bad_chunk();
     load_tile(krow);
     for (int t = 0; t < tiles; ++t) {
         // scores of this tile
@@ -271,16 +326,16 @@ __global__ __launch_bounds__(kBlock) void attn_chunk_kernel(AttnArgs a) {
                 vcur_lo[i] = vlo[i];
             }
         }
-        // next tile's rows and loads go out before this tile's arithmetic
+        // the next tile's loads and the entries of the one after go out
+        // before this tile's arithmetic
         if (t + 1 < tiles) {
-            krow = lookup(t + 1);
-            if (__any(bad)) {
-                atomicOr(a.flags, UKV_FLAG_BAD_BLOCK);
-                if (lane < G)
-                    a.part_ml[((((int64_t)r * a.max_chunks + c) * a.heads + h) * G + lane) * 2 + 1] = -1.0f;
-                return;
-            }
+            const Pos p2 = advance(p1);
+            const int32_t e2 = entry(p2);
+            krow = row_of(p1, e1);
+            if (__any(bad)) return bad_chunk();
             load_tile(krow);
+            p1 = p2;
+            e1 = e2;
         }
         const int32_t tile0 = pbeg + t * kTile + 4 * grp;
         float x[4];
@@ -299,7 +354,7 @@ __global__ __launch_bounds__(kBlock) void attn_chunk_kernel(AttnArgs a) {
             l_run *= alpha;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float ag = __shfl(alpha, g);
+                const float ag = p_of_head<G>(alpha, g);
 #pragma unroll
                 for (int d = 0; d < DL; ++d) acc[g][d] *= ag;
             }
@@ -332,7 +387,7 @@ __global__ __launch_bounds__(kBlock) void attn_chunk_kernel(AttnArgs a) {
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float pg = __shfl(p[i], 16 * grp + g);
+                const float pg = p_of_head<G>(p[i], g);
 #pragma unroll
                 for (int d = 0; d < DL; ++d) acc[g][d] = fmaf(pg, vf[d], acc[g][d]);
             }
@@ -348,7 +403,6 @@ __global__ __launch_bounds__(kBlock) void attn_chunk_kernel(AttnArgs a) {
             acc[g][d] += __shfl_xor(acc[g][d], 16);
             acc[g][d] += __shfl_xor(acc[g][d], 32);
         }
-    const int64_t unit = ((int64_t)r * a.max_chunks + c) * a.heads + h;
     if (lane < 16) {
         float *po = a.part_o + unit * G * D + col * DL;
 #pragma unroll
@@ -378,7 +432,7 @@ __global__ __launch_bounds__(kWave) void attn_combine_kernel(AttnArgs a) {
         if (h == 0 && lane == 0) atomicOr(a.flags, UKV_FLAG_LAYOUT);
     } else if (len > 0) {
         const int32_t n = len - first_position(len, a.window);
-        chunks = (n + kChunk - 1) / kChunk;
+        chunks = (n + a.chunk - 1) / a.chunk;
     }
     const int64_t unit0 = (int64_t)r * a.max_chunks * a.heads + h;  // chunk c: unit0 + c * heads
     bool bad = false;
@@ -404,9 +458,22 @@ __global__ __launch_bounds__(kWave) void attn_combine_kernel(AttnArgs a) {
     }
 }
 
-int64_t max_chunks_for(int32_t max_seq_len, int32_t window) {
+// Positions per split-K unit: the largest of 1024, 768, 512, 384, 256, 128
+// that still gives about kBusyWaves waves for the batch's bound (long units
+// amortise each wave's start and its partial result; enough of them keep
+// every CU busy).  Measured on the decode-shape batch: 1024 (6.5 TB/s) over
+// 512 (6.2 TB/s) in chunk-major order.
+int32_t chunk_for(int32_t num_reqs, int32_t heads, int32_t max_seq_len, int32_t window) {
     const int64_t n = (window > 0 && window < max_seq_len) ? window : max_seq_len;
-    return n > 0 ? (n + kChunk - 1) / kChunk : 0;
+    int32_t chunk = kMaxChunk;
+    while (chunk > kMinChunk && (int64_t)num_reqs * heads * ((n + chunk - 1) / chunk) < kBusyWaves)
+        chunk = chunk > 512 ? chunk - 256 : chunk - 128;
+    return chunk;
+}
+
+int64_t max_chunks_for(int32_t max_seq_len, int32_t window, int32_t chunk) {
+    const int64_t n = (window > 0 && window < max_seq_len) ? window : max_seq_len;
+    return n > 0 ? (n + chunk - 1) / chunk : 0;
 }
 
 }  // namespace
@@ -450,11 +517,15 @@ int ukv_build_page_table(const ukv_pool *pool, int32_t sub, const int32_t *req_p
     return check_launch(who);
 }
 
-uint64_t ukv_decode_attention_workspace_bytes(int32_t num_reqs, int32_t q_heads, int32_t head_dim,
+uint64_t ukv_decode_attention_workspace_bytes(const ukv_pool *pool, int32_t sub, int32_t num_reqs, int32_t q_heads,
                                               int32_t max_seq_len, int32_t window) {
-    if (num_reqs <= 0 || q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) return 0;
-    return (uint64_t)num_reqs * (uint64_t)max_chunks_for(max_seq_len, window < 0 ? 0 : window) * (uint64_t)q_heads *
-           ((uint64_t)head_dim + 2) * sizeof(float);
+    if (pool == nullptr || sub < 0 || sub >= pool->plan.n_sub) return 0;
+    const ukv_subpool_spec &s = pool->spec[sub];
+    if (num_reqs <= 0 || q_heads <= 0 || max_seq_len <= 0 || s.head_num <= 0) return 0;
+    if (window < 0) window = 0;
+    const int32_t chunk = chunk_for(num_reqs, s.head_num, max_seq_len, window);
+    return (uint64_t)num_reqs * (uint64_t)max_chunks_for(max_seq_len, window, chunk) * (uint64_t)q_heads *
+           ((uint64_t)s.head_dim + 2) * sizeof(float);
 }
 
 int ukv_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const void *q_dev, int32_t q_heads,
@@ -490,8 +561,9 @@ int ukv_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const
     ukv::view_of(pool->plan, s, sub, layer, 1, &vv);
     if (((uintptr_t)pool->raw + vk.byte_offset) % 16 != 0 || ((uintptr_t)pool->raw + vv.byte_offset) % 16 != 0)
         return fail(UKV_ERR_ALIGNMENT, "%s: the layer's views are not 16-byte aligned", who);
-    const int64_t chunks = max_chunks_for(max_seq_len, window);
-    const uint64_t need = ukv_decode_attention_workspace_bytes(num_reqs, q_heads, D, max_seq_len, window);
+    const int32_t chunk = chunk_for(num_reqs, s.head_num, max_seq_len, window);
+    const int64_t chunks = max_chunks_for(max_seq_len, window, chunk);
+    const uint64_t need = ukv_decode_attention_workspace_bytes(pool, sub, num_reqs, q_heads, max_seq_len, window);
     if (chunks > 0) {
         if (block_table_dev == nullptr || bt_stride < 1)
             return fail(UKV_ERR_INVALID_ARG, "%s: null block table or bt_stride < 1", who);
@@ -506,8 +578,7 @@ int ukv_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const
         ranges_overlap(out_dev, out_bytes, workspace_dev, need) ||
         ranges_overlap(out_dev, out_bytes, pool->raw, pool->raw_bytes))
         return fail(UKV_ERR_INVALID_ARG, "%s: output overlaps q, the workspace or the pool", who);
-    const int64_t waves = (int64_t)num_reqs * chunks * s.head_num;
-    const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t grid = (int64_t)num_reqs * chunks * s.head_num;  // one wave per block
     if (grid > kMaxGrid || (int64_t)num_reqs * s.head_num > kMaxGrid)
         return fail(UKV_ERR_INVALID_ARG, "%s: batch too large for one launch", who);
     AttnArgs a;
@@ -528,7 +599,9 @@ int ukv_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const
     a.window = window;
     a.max_seq_len = max_seq_len;
     a.max_chunks = (int32_t)chunks;
+    a.chunk = chunk;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    a.inv_bpp = 1.0 / (double)p.blocks_per_page;
     float *ws = (float *)workspace_dev;
     a.part_o = ws;
     a.part_ml = ws == nullptr ? nullptr : ws + (uint64_t)num_reqs * chunks * q_heads * D;
@@ -537,7 +610,7 @@ int ukv_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const
     auto launch = [&](auto gtag, auto dtag) {
         constexpr int GG = decltype(gtag)::value;
         constexpr int DD = decltype(dtag)::value;
-        if (grid > 0) hipLaunchKernelGGL((attn_chunk_kernel<GG, DD>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        if (grid > 0) hipLaunchKernelGGL((attn_chunk_kernel<GG, DD>), dim3((unsigned)grid), dim3(kWave), 0, stream, a);
         hipLaunchKernelGGL((attn_combine_kernel<GG, DD>), dim3((unsigned)(num_reqs * s.head_num)), dim3(kWave), 0,
                            stream, a);
         return check_launch(who);

@@ -19,11 +19,13 @@ from parity_util import log, ospecs, round8, to_dev
 
 pytestmark = pytest.mark.gpu
 
-CHUNK = 256  # positions per split-K unit of the kernel
-# the kernel's longest fp32 sum chain: CHUNK / 4 positions per lane, two lane
-# reductions, the merge over chunks and the division
+MAX_CHUNK, MIN_CHUNK = 1024, 128  # positions per split-K unit of the kernel, by batch size
+
+
 def bound_terms(max_len):
-    return CHUNK // 4 + 2 + (max_len + CHUNK - 1) // CHUNK + 2
+    """The kernel's longest fp32 sum chain: a unit's positions / 4 per lane, two lane
+    reductions, the merge over units and the division (largest units, most units)."""
+    return MAX_CHUNK // 4 + 2 + (max_len + MIN_CHUNK - 1) // MIN_CHUNK + 2
 
 
 @pytest.fixture(autouse=True)
@@ -150,6 +152,27 @@ def test_decode_attention_parity(hkv, group, d, ps, window):
         assert np.array_equal(got[lens == 0], np.zeros_like(got[lens == 0]))
 
 
+@pytest.mark.parametrize("num_reqs,len_hi,window", [(128, 3000, 0), (64, 3000, 0), (256, 2100, 0), (256, 4000, 700),
+                                                    (32, 9000, 0)])
+def test_decode_attention_parity_unit_sizes(num_reqs, len_hi, window):
+    """Batches whose size makes the kernel pick 768-, 384-, 1024-, 512- and 512-position units."""
+    ps, hkv, group, d = 16, 8, 4, 128
+    g = np.random.default_rng(num_reqs + len_hi)
+    lens = g.integers(1, len_hi, size=num_reqs, endpoint=True).astype(np.int32)
+    lens[0] = len_hi
+    P = 2500
+    pair = GaussPair([W.mha(1, hkv, d, P)], ps, seed=num_reqs)
+    pages = requests(4, P, ps, lens, share=True)
+    bt, _ = pair.orc.translate_pages(0, W.padded_table(pages))
+    q = W.irwin_hall_bf16_host(8, 0, 2 * num_reqs * hkv * group * d).reshape(num_reqs, hkv * group, d)
+    scale = A.default_scale(d)
+    got, gf = run_attention(pair, 0, q, bt, lens, window, scale, len_hi)
+    exp, ef, bound = A.decode_attention(pair.orc, 0, 0, q, bt, lens, window, scale, len_hi,
+                                        bound_terms=bound_terms(len_hi))
+    assert gf == ef == frozenset()
+    check_close(got, exp, bound, f"{num_reqs} requests up to {len_hi}")
+
+
 @pytest.mark.parametrize("hkv,group,d", [(2, 4, 128), (1, 2, 64), (2, 8, 256)])
 def test_decode_attention_single_position_is_exact(hkv, group, d):
     """window = 1 keeps only the last position: the output is that V row, exactly, for any length."""
@@ -246,7 +269,7 @@ def test_decode_attention_full_decode_8b_sampled():
     qd = torch.from_numpy(q.view(np.int16)).to("cuda").view(torch.bfloat16)
     scale = A.default_scale(d)
     max_len = int(lens.max())
-    ws = torch.empty(U.ukv_decode_attention_workspace_bytes(R, hq, d, max_len, 0), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(U.ukv_decode_attention_workspace_bytes(pair.gpu, 0, R, hq, max_len, 0), dtype=torch.uint8, device="cuda")
     sample = sorted({0, R - 1, int(np.argmax(lens)), int(np.argmin(lens)), 101, 177})
     for layer in range(32):
         out = U.ukv_decode_attention(pair.gpu, 0, layer, qd, bt_dev, to_dev(lens), max_len, 0, scale, workspace=ws)
