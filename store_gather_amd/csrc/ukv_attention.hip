@@ -417,12 +417,18 @@ __global__ __launch_bounds__(kWave) void attn_chunk_kernel(AttnArgs a) {
     }
 }
 
-// Merge the chunks of (request, KV head): out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
-// A bad chunk, a request past max_seq_len (UKV_FLAG_LAYOUT) or an empty one
-// gives zeros.
+// Merge the units of (request, KV head): out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+// A bad unit, a request past max_seq_len (UKV_FLAG_LAYOUT) or an empty one
+// gives zeros.  One wave: lanes take the (unit, head) pairs in parallel for
+// the maxima and the denominators, the weights go through LDS, and each lane
+// sums G * D / 64 outputs over the units with independent loads.
 template <int G, int D>
 __global__ __launch_bounds__(kWave) void attn_combine_kernel(AttnArgs a) {
+    constexpr int E = G * D / kWave;  // outputs per lane
+    constexpr int kPiece = 4096 / G;  // units whose weights fit the LDS array at once
+    __shared__ float wsh[kPiece * G];
     const int lane = lane_id();
+    const int g_lane = lane % G;  // the head of every (unit, head) pair this lane takes
     const int32_t r = (int32_t)(blockIdx.x / (uint32_t)a.heads);
     const int32_t h = (int32_t)(blockIdx.x - (uint32_t)r * a.heads);
     float *o = a.out + ((int64_t)r * a.heads + h) * G * D;
@@ -434,27 +440,51 @@ __global__ __launch_bounds__(kWave) void attn_combine_kernel(AttnArgs a) {
         const int32_t n = len - first_position(len, a.window);
         chunks = (n + a.chunk - 1) / a.chunk;
     }
-    const int64_t unit0 = (int64_t)r * a.max_chunks * a.heads + h;  // chunk c: unit0 + c * heads
+    const int64_t unit0 = (int64_t)r * a.max_chunks * a.heads + h;  // unit c: unit0 + c * heads
+    auto ml_of = [&](int c) { return *(const float2 *)(a.part_ml + ((unit0 + (int64_t)c * a.heads) * G + g_lane) * 2); };
+    // running max and denominator of head g_lane over this lane's pairs
+    float mx = -INFINITY, den = 0.0f;
     bool bad = false;
-    for (int c = 0; c < chunks; ++c)
-        for (int g = 0; g < G; ++g) bad |= a.part_ml[((unit0 + (int64_t)c * a.heads) * G + g) * 2 + 1] < 0.0f;
-    for (int e = lane; e < G * D; e += kWave) {
-        const int g = e / D;
-        float res = 0.0f;
-        if (chunks > 0 && !bad) {
-            float mx = -INFINITY;
-            for (int c = 0; c < chunks; ++c)
-                mx = fmaxf(mx, a.part_ml[((unit0 + (int64_t)c * a.heads) * G + g) * 2]);
-            float num = 0.0f, den = 0.0f;
-            for (int c = 0; c < chunks; ++c) {
-                const int64_t u = unit0 + (int64_t)c * a.heads;
-                const float w = exp2f(a.part_ml[(u * G + g) * 2] - mx);
-                den = fmaf(w, a.part_ml[(u * G + g) * 2 + 1], den);
-                num = fmaf(w, a.part_o[u * G * D + e], num);
-            }
-            res = num / den;
+    for (int idx = lane; idx < chunks * G; idx += kWave) {
+        const float2 ml = ml_of(idx / G);
+        bad |= ml.y < 0.0f;
+        if (ml.x > mx) {
+            den = den * exp2f(mx - ml.x) + ml.y;
+            mx = ml.x;
+        } else {
+            den += exp2f(ml.x - mx) * ml.y;
         }
-        o[e] = res;
+    }
+    float mh = mx;
+    for (int sh = kWave / 2; sh >= G; sh >>= 1) mh = fmaxf(mh, __shfl_xor(mh, sh));
+    den = mx == -INFINITY ? 0.0f : den * exp2f(mx - mh);
+    for (int sh = kWave / 2; sh >= G; sh >>= 1) den += __shfl_xor(den, sh);
+    const bool any_bad = __any(bad);
+    float acc[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) acc[k] = 0.0f;
+    if (chunks > 0 && !any_bad) {
+        for (int c0 = 0; c0 < chunks; c0 += kPiece) {
+            const int cn = min(kPiece, chunks - c0);
+            for (int idx = lane; idx < cn * G; idx += kWave) wsh[idx] = exp2f(ml_of(c0 + idx / G).x - mh);
+            __syncthreads();
+#pragma unroll 4
+            for (int c = 0; c < cn; ++c) {
+                const float *po = a.part_o + (unit0 + (int64_t)(c0 + c) * a.heads) * G * D;
+#pragma unroll
+                for (int k = 0; k < E; ++k) {
+                    const int e = lane + kWave * k;
+                    acc[k] = fmaf(wsh[c * G + e / D], po[e], acc[k]);
+                }
+            }
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const int e = lane + kWave * k;
+        const float dg = __shfl(den, e / D);  // lane g holds head g's denominator
+        o[e] = (chunks > 0 && !any_bad) ? acc[k] / dg : 0.0f;
     }
 }
 
