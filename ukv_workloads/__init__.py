@@ -498,4 +498,5 @@ __all__ = [
     "normal_bf16_device", "SubPoolShape", "mha", "mla", "rng", "live_slots", "page_permutation",
     "slots_of_requests", "padded_table", "out_offsets", "Workload", "tiny_mha", "decode_8b",
     "dirichlet_lengths", "prefill_8b", "hybrid", "move_70b", "compaction_plan", "swa_decode", "MHA", "MLA",
+    "irwin_hall_bf16_host", "irwin_hall_fill_device",
 ]
