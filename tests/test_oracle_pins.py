@@ -764,3 +764,26 @@ def test_build_page_table_is_prefix_only():
     bad[2, 1] = P
     out3, fl = pool.build_page_table(0, bad, lens)
     assert fl == {"slot_range"} and out3[2, 1] == 0
+
+
+@pytest.mark.parametrize("n,hkv,group,d", [(1, 1, 1, 64), (37, 2, 4, 128), (700, 1, 8, 128), (2500, 2, 2, 64)])
+def test_fp32_error_bound_covers_a_float32_evaluation(n, hkv, group, d):
+    """The derived tolerance is not tighter than the arithmetic: a plain float32
+    evaluation of the same attention stays inside it (sums of up to n terms)."""
+    g = np.random.default_rng(n + d)
+    bits = lambda m: W.irwin_hall_bf16_host(int(g.integers(1 << 30)), 0, 2 * m)
+    q = A.bf16_bits_to_f64(bits(hkv * group * d)).reshape(hkv * group, d)
+    k = A.bf16_bits_to_f64(bits(n * hkv * d)).reshape(n, hkv, d)
+    v = A.bf16_bits_to_f64(bits(n * hkv * d)).reshape(n, hkv, d)
+    scale = A.default_scale(d)
+    exact = A.attend(q, k, v, scale)
+    bound = A.fp32_error_bound(q, k, v, scale, n + 2)
+    out32 = np.zeros_like(exact)
+    for gh in range(hkv * group):
+        h = gh // group
+        s = (k[:, h, :].astype(np.float32) @ q[gh].astype(np.float32)) * np.float32(scale)
+        e = np.exp(s - s.max())
+        out32[gh] = (e @ v[:, h, :].astype(np.float32)) / e.sum(dtype=np.float32)
+    err = np.abs(out32 - exact).max(axis=1)
+    assert (err <= bound).all(), (err, bound)
+    assert (bound < 5e-3).all()
