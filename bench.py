@@ -19,6 +19,9 @@ recorded around each of its launches inside the timed region, on the stream
 the kernels run on.  `ops` gives every launch kind's time per launch, from
 all its launches in step order run back to back (outside the timed region).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+`tokens_per_s` counts token rows (one token's K and V, or its MLA latent, in
+one layer) stored, gathered, moved or attended over the step time; each `ops`
+entry gives its own rows per launch and rate.
 """
 from __future__ import annotations
 
@@ -102,6 +105,29 @@ class Script:
     roofline_kernel: str
     counts: dict = field(default_factory=dict)
     dtype: str = "u8"  # what the path computes in: bytes moved as integers
+
+
+def op_rows(op: Op, s: "Script") -> int:
+    """Token rows one launch moves or reads: one token's K and V (MHA) or latent (MLA) in one
+    layer is one row.  Translations count the slots they translate; table work counts none."""
+    a = op.args
+    if op.kind in ("translate", "translate_loc"):
+        return int(s.arrays[a["inp"]].size)
+    if op.kind == "store":
+        return int(a["n"])
+    if op.kind == "store_layers":
+        return int(a["n"]) * int(a["count"])
+    if op.kind == "gather":
+        return int(a["rows"])
+    if op.kind == "gather_layers":
+        return int(a["rows"]) * int(a["count"])
+    if op.kind == "move":
+        return int(s.arrays[f"msrc{op.sub}"].size) * (int(a["l1"]) - int(a["l0"]))
+    if op.kind == "move_pages":
+        return int(s.arrays[f"psrc{op.sub}"].size) * s.page_size * s.shapes[op.sub].layer_num
+    if op.kind == "attention":
+        return int(s.arrays[f"lens{op.sub}"].astype(np.int64).sum())
+    return 0
 
 
 def _pages_read(pages_per_req, lens, window, ps):
@@ -632,6 +658,7 @@ def run_workload(name, args, torch, U, W, device) -> dict:
 
     step_bytes = sum(op.nbytes for op in script.ops)
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    step_rows = sum(op_rows(op, script) for op in script.ops if not op.kind.startswith("translate"))
     roof_ms = roof_bytes = achieved = None
     if timed:
         roof_ms = float(np.mean([e0.elapsed_time(e1) for _, e0, e1 in timed]))
@@ -661,9 +688,11 @@ def run_workload(name, args, torch, U, W, device) -> dict:
     ops_out = {}
     for k, d in agg.items():
         gbps = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+        rows = sum(op_rows(op, script) for op in kinds[k]) / len(kinds[k])
         ops_out[k] = {"launches_per_step": d["launches"], "ms_per_launch": num(d["ms"], 5),
                       "bytes_per_launch": int(d["bytes"]), "GBps": num(gbps, 1),
-                      "pct_of_peak": num(100 * gbps / PEAK_GBPS, 2)}
+                      "pct_of_peak": num(100 * gbps / PEAK_GBPS, 2), "rows_per_launch": int(rows),
+                      "Mrows_per_s": num(rows / (d["ms"] * 1e-3) / 1e6, 2)}
     flags = U.ukv_pool_error_flags(g.pool)
     assert flags == frozenset(), f"device flags raised: {flags}"
     del g
@@ -688,8 +717,10 @@ def run_workload(name, args, torch, U, W, device) -> dict:
         "dtype": script.dtype,
         "data": "synthetic",
         "config": dict({"workload": script.description, "kv_dtype": "bf16", "parallelism": "single GPU",
-                        "step_bytes": step_bytes, "launches_per_step": len(script.ops)}, **script.counts),
+                        "step_bytes": step_bytes, "token_rows_per_step": step_rows,
+                        "launches_per_step": len(script.ops)}, **script.counts),
         "pct_of_peak": round(100.0 * value / PEAK_GBPS, 2),
+        "tokens_per_s": round(step_rows / (ms_step * 1e-3), 1),
         "roofline": {
             "bound": "hbm",
             "kernel": f"{script.roofline_kernel}_kernel",
