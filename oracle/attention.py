@@ -23,6 +23,15 @@ K_j / V_j are the rows of the layer's K / V views at row
 bt[r][j // ps] * ps + j % ps (block-table entries are kernel-facing page
 indices, phys * blocks_per_page), decoded from their bf16 bits.
 
+MLA sub-pools (one latent row per token per layer, e.g. 576 wide) have one
+dense view per layer and no separate V rows.  READING (the pages print no MLA
+attention either): every query head attends to the single latent "head" —
+the scores use the whole latent row, K_j = c_j, and the values are its
+first v_dim elements, V_j = c_j[:v_dim] (the compressed KV part ahead of the
+rotary part, 512 of 576 in the models with 576-wide latents); the query is
+given in the latent space (its no-position part already absorbed).  That is
+the formula above with one KV head, G = q_heads.
+
 Conditions (the same readings as the block-table gather): a request with
 len <= 0 attends to nothing and its output is zero; a request longer than
 the caller's bound max_seq_len raises LAYOUT; one whose positions need a
@@ -74,7 +83,8 @@ def gamma(n: int) -> float:
     return n * U32 / (1.0 - n * U32)
 
 
-def fp32_error_bound(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, sum_terms: int) -> np.ndarray:
+def fp32_error_bound(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, sum_terms: int,
+                     weight_rel: float = 0.0) -> np.ndarray:
     """Bound on |out_fp32 - out| per query head for an fp32 evaluation of `attend`.
 
     q [Hq, D], k [n, Hkv, D], v [n, Hkv, Dv] as in `attend`.  An fp32
@@ -84,7 +94,10 @@ def fp32_error_bound(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, 
     roundoff relative to the argument (4 u (|scale s_j| log2 e + 1)).  Weights
     perturbed by at most delta relative change the weighted mean by at most
     4 delta max|v|, and the numerator / denominator sums of at most
-    `sum_terms` terms add 2 gamma(sum_terms) max|v|.
+    `sum_terms` terms add 2 gamma(sum_terms) max|v|.  ``weight_rel`` is any
+    further relative error of each weight as the evaluation uses it (e.g. a
+    weight split into two bf16 parts for a matrix-core product: 2^-16); it
+    adds to delta.
     """
     hq, d = q.shape
     hkv = k.shape[1]
@@ -96,7 +109,7 @@ def fp32_error_bound(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, 
         h = g // group
         a = (np.abs(k[:, h, :]) @ np.abs(q[g])).max()
         s_max = np.abs(scale * (k[:, h, :] @ q[g])).max() * 1.4426950408889634
-        delta = scale * gamma(d) * a + 4 * U32 * (s_max + 1.0)
+        delta = scale * gamma(d) * a + 4 * U32 * (s_max + 1.0) + weight_rel
         vmax = np.abs(v[:, h, :]).max()
         bound[g] = 4 * delta * vmax + 2 * gamma(sum_terms) * vmax
     return bound
@@ -104,7 +117,7 @@ def fp32_error_bound(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, 
 
 def decode_attention(pool, sub: int, layer: int, q_bits: np.ndarray, block_table, seq_lens, window: int,
                      scale: float, max_seq_len: int | None = None, read=None, requests=None,
-                     bound_terms: int | None = None):
+                     bound_terms: int | None = None, v_dim: int | None = None, weight_rel: float = 0.0):
     """Decode attention of every request over its positions in the pool's dense views.
 
     q_bits: [R, Hq, D] bf16 bits (uint16); block_table: [R, width] int32
@@ -112,16 +125,22 @@ def decode_attention(pool, sub: int, layer: int, q_bits: np.ndarray, block_table
     returns the uint16 words at a byte offset of the pool (default: the
     pool's own buffer), so that an addresses-only pool can be served from
     values generated on demand.  ``requests`` limits the work to some
-    requests (the others stay zero).  Returns (out float64 [R, Hq, Dv], set
-    of condition names raised), and with ``bound_terms`` also the
-    fp32_error_bound [R, Hq] of every request (0 where nothing is read).
+    requests (the others stay zero).  An MLA sub-pool needs ``v_dim``, the
+    value width taken from the front of each latent row.  Returns (out
+    float64 [R, Hq, Dv], set of condition names raised), and with
+    ``bound_terms`` also the fp32_error_bound [R, Hq] of every request (0
+    where nothing is read; ``weight_rel`` as there).
     """
     if read is None:
         def read(off, nbytes):
             return pool.raw[off: off + nbytes].view(np.uint16)
     spec = pool.specs[sub]
-    assert spec.kind == 0, "decode attention reads an MHA sub-pool"
-    hkv, d, dv = spec.head_num, spec.head_dim, spec.v_head_dim
+    mla = spec.kind == 1
+    if mla:
+        assert v_dim is not None and 0 < v_dim <= spec.head_dim, "MLA attention needs 0 < v_dim <= latent width"
+        hkv, d, dv = 1, spec.head_dim, v_dim
+    else:
+        hkv, d, dv = spec.head_num, spec.head_dim, spec.v_head_dim
     ps = pool.page_size
     bpp = pool.plan.subs[sub].blocks_per_page
     bt = np.asarray(block_table, dtype=np.int64)
@@ -129,8 +148,10 @@ def decode_attention(pool, sub: int, layer: int, q_bits: np.ndarray, block_table
     lens = np.asarray(seq_lens, dtype=np.int64)
     R, hq = q_bits.shape[0], q_bits.shape[1]
     assert hq % hkv == 0
-    k_base, v_base = pool.view_base(sub, layer, 0), pool.view_base(sub, layer, 1)
-    k_row_bytes, v_row_bytes = hkv * d * spec.elem_bytes, hkv * dv * spec.elem_bytes
+    k_base = pool.view_base(sub, layer, 0)
+    v_base = k_base if mla else pool.view_base(sub, layer, 1)  # MLA: values are the latent rows' front
+    k_row_bytes = hkv * d * spec.elem_bytes
+    v_row_bytes = k_row_bytes if mla else hkv * dv * spec.elem_bytes
     out = np.zeros((R, hq, dv))
     bound = np.zeros((R, hq))
     flags = set()
@@ -155,15 +176,20 @@ def decode_attention(pool, sub: int, layer: int, q_bits: np.ndarray, block_table
             flags.add("bad_block")
             continue
         k = np.stack([read(k_base + row * k_row_bytes, k_row_bytes) for row in rows])
-        v = np.stack([read(v_base + row * v_row_bytes, v_row_bytes) for row in rows])
+        v = k[:, :dv] if mla else np.stack([read(v_base + row * v_row_bytes, v_row_bytes) for row in rows])
         qf, kf, vf = (bf16_bits_to_f64(q_bits[r]), bf16_bits_to_f64(k).reshape(-1, hkv, d),
                       bf16_bits_to_f64(v).reshape(-1, hkv, dv))
         out[r] = attend(qf, kf, vf, scale)
         if bound_terms is not None:
-            bound[r] = fp32_error_bound(qf, kf, vf, scale, bound_terms)
+            bound[r] = fp32_error_bound(qf, kf, vf, scale, bound_terms, weight_rel)
     if bound_terms is not None:
         return out, frozenset(flags), bound
     return out, frozenset(flags)
+
+
+# A weight p split into bf16 parts p_hi = bf16(p), p_lo = bf16(p - p_hi) keeps
+# p_hi + p_lo within 2^-16 |p| (two 8-bit significands, round to nearest).
+BF16_SPLIT_REL = 2.0 ** -16
 
 
 def default_scale(head_dim: int) -> float:

@@ -787,3 +787,139 @@ def test_fp32_error_bound_covers_a_float32_evaluation(n, hkv, group, d):
     err = np.abs(out32 - exact).max(axis=1)
     assert (err <= bound).all(), (err, bound)
     assert (bound < 5e-3).all()
+
+
+# ---------------------------------------------------------------------------
+# decode attention over an MLA sub-pool's latent view
+# ---------------------------------------------------------------------------
+
+def _sdpa_reference_mla(ref, layer, pages, lens, window, q_bits, lat, v_dim, scale):
+    """torch's SDPA in float64: one latent 'head' for every query head, values its front."""
+    import torch
+
+    hq = q_bits.shape[1]
+    out = np.zeros((len(lens), hq, v_dim))
+    for r, (pg, n) in enumerate(zip(pages, lens)):
+        if n <= 0:
+            continue
+        c, none = ref.gather_pages(layer, [pg], [n], window)
+        assert none is None
+        c = torch.from_numpy(A.bf16_bits_to_f64(c.view(np.uint16)).reshape(-1, lat))
+        k = c.unsqueeze(0).expand(hq, -1, -1).unsqueeze(0).contiguous()  # [1, Hq, n, lat]
+        v = c[:, :v_dim].unsqueeze(0).expand(hq, -1, -1).unsqueeze(0).contiguous()
+        q = torch.from_numpy(A.bf16_bits_to_f64(q_bits[r])).unsqueeze(0).unsqueeze(2)  # [1, Hq, 1, lat]
+        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale)
+        out[r] = o[0, :, 0, :].numpy()
+    return out
+
+
+@pytest.mark.parametrize("lat,v_dim,hq,window", [(24, 16, 4, 0), (24, 16, 4, 5), (576, 512, 16, 0), (40, 40, 2, 7)])
+def test_mla_decode_attention_matches_torch_sdpa(lat, v_dim, hq, window):
+    ps, P, L = 4, 20, 3
+    lens = np.array([1, 6, 15, 0, 19], dtype=np.int32)
+    pool, raw = _gauss_pool([W.mla(L, P, latent_dim=lat)], ps)
+    pages = _requests(21, P, ps, lens)
+    bt, flags = pool.translate_pages(0, W.padded_table(pages))
+    assert flags == frozenset()
+    q = W.irwin_hall_bf16_host(23, 0, 2 * lens.size * hq * lat).reshape(lens.size, hq, lat)
+    scale = A.default_scale(lat)
+    ref = _strided(pool, 0)
+    for layer in (0, L - 1):
+        out, fl = A.decode_attention(pool, 0, layer, q, bt, lens, window, scale, v_dim=v_dim)
+        assert fl == frozenset() and out.shape == (lens.size, hq, v_dim)
+        exp = _sdpa_reference_mla(ref, layer, pages, lens, window, q, lat, v_dim, scale)
+        assert np.abs(out - exp).max() < 1e-12
+        assert not np.allclose(out[1], 0) and np.allclose(out[3], 0)
+
+
+def test_mla_decode_attention_closed_forms_and_conditions():
+    ps, P, lat, v_dim, hq = 4, 12, 24, 16, 4
+    lens = np.array([7, 1, 9], dtype=np.int32)
+    pool, raw = _gauss_pool([W.mla(2, P, latent_dim=lat)], ps)
+    ref = _strided(pool, 0)
+    pages = _requests(5, P, ps, lens)
+    bt, _ = pool.translate_pages(0, W.padded_table(pages))
+    q = W.irwin_hall_bf16_host(6, 0, 2 * lens.size * hq * lat).reshape(lens.size, hq, lat)
+    # request 0: latent rows that differ only in their value front, and a query that is
+    # zero there: every score is the same, so the weights are uniform and the output is
+    # the mean of the value fronts (the scores read the part past the values too)
+    k0 = ref.row(1, 0, int(pages[0][0]), 0).copy()
+    for j in range(7):
+        row = ref.env[int(pages[0][j // ps]), 1, 0, j % ps]
+        row[2 * v_dim:] = k0[2 * v_dim:]
+    q0 = q.copy()
+    q0[0, :, :v_dim] = 0
+    out, fl = A.decode_attention(pool, 0, 1, q0, bt, lens, 0, 0.7, v_dim=v_dim)
+    assert fl == frozenset()
+    c, _ = ref.gather_pages(1, [pages[0]], [7], 0)
+    cmean = A.bf16_bits_to_f64(c.view(np.uint16)).reshape(7, lat)[:, :v_dim].mean(axis=0)
+    for g in range(hq):
+        assert np.allclose(out[0, g], cmean, rtol=0, atol=1e-14)
+    assert not np.allclose(out[2], cmean)  # other requests keep their own weights
+    # a single position: exactly its value front, whatever q and the scale
+    out, _ = A.decode_attention(pool, 0, 1, q, bt, lens, 0, 3.0, v_dim=v_dim)
+    c1, _ = ref.gather_pages(1, [pages[1]], [1], 0)
+    c1 = A.bf16_bits_to_f64(c1.view(np.uint16)).reshape(lat)[:v_dim]
+    for g in range(hq):
+        assert np.array_equal(out[1, g], c1)
+    # scale 0 over a window: the mean of the window's value fronts
+    out0, _ = A.decode_attention(pool, 0, 0, q, bt, lens, 3, 0.0, v_dim=v_dim)
+    c3, _ = ref.gather_pages(0, [pages[2]], [9], 3)
+    c3 = A.bf16_bits_to_f64(c3.view(np.uint16)).reshape(3, lat)[:, :v_dim].mean(axis=0)
+    assert np.allclose(out0[2, 2], c3, rtol=0, atol=1e-14)
+    # the same conditions as the MHA read: bad entries, narrow tables, lengths past the bound
+    good, _ = A.decode_attention(pool, 0, 0, q, bt, lens, 0, 0.5, v_dim=v_dim)
+    b = bt.copy()
+    b[2, 1] = bt[2, 1] + 1  # not a multiple of blocks_per_page
+    out, fl = A.decode_attention(pool, 0, 0, q, b, lens, 0, 0.5, v_dim=v_dim)
+    assert fl == {"bad_block"} and np.allclose(out[2], 0) and np.array_equal(out[:2], good[:2])
+    out, fl = A.decode_attention(pool, 0, 0, q, bt, lens, 0, 0.5, max_seq_len=8, v_dim=v_dim)
+    assert fl == {"layout"} and np.allclose(out[2], 0) and np.array_equal(out[:2], good[:2])
+    with pytest.raises(AssertionError):
+        A.decode_attention(pool, 0, 0, q, bt, lens, 0, 0.5)  # an MLA read needs its value width
+
+
+@pytest.mark.parametrize("n,hq,sparse", [(1, 16, False), (45, 16, False), (900, 32, False), (3000, 16, False),
+                                         (45, 16, True), (3000, 16, True)])
+def test_split_weight_bound_covers_a_matrix_core_style_evaluation(n, hq, sparse):
+    """An fp32 evaluation that splits each weight into bf16 high and low parts
+    (scores from exact bf16 products, fp32 sums) stays inside the bound with
+    weight_rel = 2^-16, on 576-wide latents with 512-wide values.  With a
+    query that is zero but for a few dims (some in the value part, some past
+    it) the score term of the bound all but vanishes, and the bound is tight
+    enough to reject the same evaluation with the low parts dropped (on
+    short requests: over thousands of positions the sums' own term leads)."""
+    g = np.random.default_rng(n + hq + 7 * sparse)
+    bits = lambda m: W.irwin_hall_bf16_host(int(g.integers(1 << 30)), 0, 2 * m)
+    lat, v_dim = 576, 512
+    q = A.bf16_bits_to_f64(bits(hq * lat)).reshape(hq, lat)
+    if sparse:
+        keep = np.zeros(lat, bool)
+        keep[[3, 200, 511, 512, 575]] = True
+        q[:, ~keep] = 0.0
+    c = A.bf16_bits_to_f64(bits(n * lat)).reshape(n, 1, lat)
+    scale = A.default_scale(192)
+    exact = A.attend(q, c, c[:, :, :v_dim], scale)
+    bound = A.fp32_error_bound(q, c, c[:, :, :v_dim], scale, n + 2, A.BF16_SPLIT_REL)
+    import torch
+
+    def bf16(x):
+        return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+
+    out = np.zeros_like(exact)
+    hi_only = np.zeros_like(exact)
+    for h in range(hq):
+        s = (c[:, 0, :].astype(np.float32) @ q[h].astype(np.float32)) * np.float32(scale)
+        p = np.exp2((s - s.max()) * np.float32(1.4426950408889634)).astype(np.float32)
+        hi = bf16(p)
+        lo = bf16(p - hi)
+        num = hi @ c[:, 0, :v_dim].astype(np.float32) + lo @ c[:, 0, :v_dim].astype(np.float32)
+        out[h] = num / p.sum(dtype=np.float32)
+        hi_only[h] = (hi @ c[:, 0, :v_dim].astype(np.float32)) / p.sum(dtype=np.float32)
+        assert (np.abs(hi + lo - p) <= A.BF16_SPLIT_REL * p).all()
+    err = np.abs(out - exact).max(axis=1)
+    assert (err <= bound).all(), (err, bound)
+    assert (bound < (2e-3 if sparse else 0.05)).all()
+    if sparse and n <= 100:  # a dropped low part (bf16 weights) is caught on short requests, where
+        # the sums' term 2 gamma(n) max|v| stays small
+        assert (np.abs(hi_only - exact).max(axis=1) > bound).any()
