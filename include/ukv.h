@@ -385,6 +385,46 @@ uint64_t ukv_decode_attention_workspace_bytes(const ukv_pool *pool, int32_t sub,
                                               int32_t max_seq_len, int32_t window);
 
 /*
+ * Decode attention over an MLA sub-pool's dense latent view (DKV 功能与动机:
+ * the MLA sub-pool already exposes dense per-layer views, read through one
+ * dense tensor plus the shared block table).  The pages print no MLA
+ * attention; this is the absorbed form: every query head attends to the one
+ * latent row c_j of each position, the scores using the whole row and the
+ * values its first v_dim elements.  For request r with len = seq_lens[r] > 0,
+ * positions j0 <= j < len (j0 = len - window when 0 < window < len, else 0):
+ *     out[r][g] = sum_j softmax_j(scale * q[r][g] . c_j) * c_j[0 : v_dim],
+ * c_j being row block_table[r][j / ps] * ps + j % ps of the layer's view.
+ * Sub-pool: MLA, bf16, latent width (head_dim) 576; v_dim must be 512;
+ * q_heads a positive multiple of 16.
+ * q_dev: bf16 [num_reqs, q_heads, 576], contiguous, 16-byte aligned (the
+ *   query in the latent space: its non-rotary part already absorbed).
+ * block_table_dev, seq_lens_dev, max_seq_len: as ukv_decode_attention.
+ * out_dev: fp32 [num_reqs, q_heads, v_dim], 16-byte aligned, overlapping
+ *   neither q, the workspace nor the pool.
+ * workspace_dev: at least ukv_mla_decode_attention_workspace_bytes(...)
+ *   bytes, 16-byte aligned, owned by the caller.
+ * Arithmetic: both products on the matrix cores from bf16 inputs with fp32
+ * accumulation; each softmax weight enters the value product as two bf16
+ * parts (relative error <= 2^-16); softmax and the merge in fp32.
+ * Conditions: as ukv_decode_attention (zeros for len <= 0; zeros and
+ * UKV_FLAG_LAYOUT past max_seq_len; zeros and UKV_FLAG_BAD_BLOCK for a bad
+ * or missing table entry).
+ */
+int ukv_mla_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const void *q_dev, int32_t q_heads,
+                             int32_t v_dim, const int32_t *block_table_dev, int64_t bt_stride,
+                             const int32_t *seq_lens_dev, int32_t num_reqs, int32_t max_seq_len, int32_t window,
+                             float scale, float *out_dev, void *workspace_dev, uint64_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
+ * Workspace bytes ukv_mla_decode_attention needs for these sizes (0 when
+ * none, or for a bad pool / sub-pool or q_heads not a multiple of 16).
+ */
+uint64_t ukv_mla_decode_attention_workspace_bytes(const ukv_pool *pool, int32_t sub, int32_t num_reqs,
+                                                  int32_t q_heads, int32_t v_dim, int32_t max_seq_len,
+                                                  int32_t window);
+
+/*
  * Reads and clears the pool's sticky flags (UKV_FLAG_*): enqueued on
  * `stream` after the work already there, then synchronises that stream.
  */

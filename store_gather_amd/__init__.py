@@ -43,6 +43,7 @@ EXPORTS = (
     "ukv_gather_kv", "ukv_gather_kv_layers", "ukv_move_kv", "ukv_pool_error_flags", "ukv_last_error",
     "ukv_status_name", "ukv_translate_loc", "ukv_move_pages", "ukv_remap_pages", "ukv_evict_window",
     "ukv_build_page_table", "ukv_decode_attention", "ukv_decode_attention_workspace_bytes",
+    "ukv_mla_decode_attention", "ukv_mla_decode_attention_workspace_bytes",
 )
 
 
@@ -114,6 +115,8 @@ def _load() -> ctypes.CDLL:
         "ukv_evict_window": [vp, vp, i64, vp, i64, vp, i32, i32, vp],
         "ukv_build_page_table": [vp, i32, vp, i64, vp, i32, vp, i64, vp, vp],
         "ukv_decode_attention": [vp, i32, i32, vp, i32, vp, i64, vp, i32, i32, i32, ctypes.c_float, vp, vp, u64, vp],
+        "ukv_mla_decode_attention": [vp, i32, i32, vp, i32, i32, vp, i64, vp, i32, i32, i32, ctypes.c_float, vp, vp,
+                                     u64, vp],
     }
     for name, args in sigs.items():
         fn = getattr(L, name)
@@ -121,6 +124,8 @@ def _load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     L.ukv_decode_attention_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32]
     L.ukv_decode_attention_workspace_bytes.restype = u64
+    L.ukv_mla_decode_attention_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32]
+    L.ukv_mla_decode_attention_workspace_bytes.restype = u64
     L.ukv_last_error.argtypes = []
     L.ukv_last_error.restype = ctypes.c_char_p
     L.ukv_status_name.argtypes = [ctypes.c_int]
@@ -549,6 +554,50 @@ def ukv_decode_attention(pool: Pool, sub: int, layer: int, q: torch.Tensor, bloc
     return out
 
 
+def ukv_mla_decode_attention_workspace_bytes(pool: Pool, sub: int, num_reqs: int, q_heads: int, v_dim: int,
+                                             max_seq_len: int, window: int = 0) -> int:
+    return int(_lib.ukv_mla_decode_attention_workspace_bytes(pool.handle, sub, num_reqs, q_heads, v_dim, max_seq_len,
+                                                             window))
+
+
+def ukv_mla_decode_attention(pool: Pool, sub: int, layer: int, q: torch.Tensor, block_table: torch.Tensor,
+                             seq_lens: torch.Tensor, max_seq_len: int, window: int, scale: float, v_dim: int = 512,
+                             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+    """Decode attention of q [num_reqs, q_heads, latent] (bf16) over each request's latent rows
+    in the layer's dense MLA view; returns fp32 [num_reqs, q_heads, v_dim].  ``workspace``
+    (uint8, at least ukv_mla_decode_attention_workspace_bytes) is allocated when None."""
+    d = pool.device
+    _dev_ptr(q, "q", d, torch.bfloat16)
+    _dev_ptr(block_table, "block_table", d, torch.int32)
+    _dev_ptr(seq_lens, "seq_lens", d, torch.int32)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [num_reqs, q_heads, latent] tensor")
+    num_reqs, q_heads, _ = q.shape
+    if seq_lens.numel() != num_reqs or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous with one length per request")
+    if block_table.dim() != 2 or block_table.shape[0] != num_reqs or (
+            block_table.numel() > 0 and block_table.stride(1) != 1):
+        raise ValueError("block_table must be [num_reqs, width] with unit inner stride")
+    if out is None:
+        out = torch.empty((num_reqs, q_heads, v_dim), dtype=torch.float32, device=d)
+    _dev_ptr(out, "out", d, torch.float32)
+    if tuple(out.shape) != (num_reqs, q_heads, v_dim) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 [num_reqs, q_heads, v_dim] tensor")
+    need = ukv_mla_decode_attention_workspace_bytes(pool, sub, num_reqs, q_heads, v_dim, max_seq_len, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=d)
+    _dev_ptr(workspace, "workspace", d)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _check(_lib.ukv_mla_decode_attention(pool.handle, sub, layer, q.data_ptr(), q_heads, v_dim,
+                                         block_table.data_ptr(), block_table.stride(0) if block_table.numel() else 0,
+                                         seq_lens.data_ptr(), num_reqs, int(max_seq_len), int(window), float(scale),
+                                         out.data_ptr(), workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), _stream_handle(stream)))
+    return out
+
+
 def ukv_pool_error_flags(pool: Pool, stream=None) -> frozenset:
     """Read and clear the pool's sticky flags (synchronises the stream)."""
     out = ctypes.c_uint32(0)
@@ -563,4 +612,5 @@ __all__ = [
     "ukv_gather_kv", "ukv_gather_kv_layers", "ukv_move_kv", "ukv_pool_error_flags", "ukv_last_error", "EXPORTS",
     "STATUS", "FLAGS", "ukv_translate_loc", "ukv_move_pages", "ukv_remap_pages", "ukv_evict_window",
     "ukv_build_page_table", "ukv_decode_attention", "ukv_decode_attention_workspace_bytes",
+    "ukv_mla_decode_attention", "ukv_mla_decode_attention_workspace_bytes",
 ]

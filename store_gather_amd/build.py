@@ -10,7 +10,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libukv.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("ukv_plan.cpp", "ukv_runtime.hip", "ukv_attention.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("ukv_plan.cpp", "ukv_runtime.hip", "ukv_attention.hip",
+                                                        "ukv_mla_attention.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

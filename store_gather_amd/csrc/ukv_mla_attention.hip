@@ -1,0 +1,471 @@
+// libukv read path for MLA sub-pools on gfx950 (MI355X): paged decode
+// attention straight from a layer's dense latent view.
+//
+// Source: report page "PR #34602: feat(unified-memory): dense KV views for
+// uniform-row MHA/SWA models", 功能与动机 (motivation): the MLA sub-pool
+// already exposes dense per-layer views, and a backend reads a layer through
+// one dense tensor and one block table shared by all layers.  The pages print
+// no attention kernel; this is the textbook decode attention of the
+// absorbed MLA form: every query head attends to the one latent row per
+// position, scores over the whole row (576 wide: the compressed KV part and
+// the rotary part), values the row's first 512 elements.
+//
+// Design (one query token per request, q_heads a multiple of 16, bf16 latent
+// rows and queries, fp32 accumulation and output).  At 16 query heads the
+// read is ~30 FLOP per byte, beyond what the vector ALUs sustain at HBM
+// bandwidth, so both products run on the matrix cores:
+//
+//  - split-K over positions: one 64-lane wave owns (unit of positions,
+//    request, group of 16 query heads) and writes an unnormalised partial
+//    (running max, row sum, 16 x 512 sums) to a workspace; a second kernel
+//    merges the units of each (request, head).
+//  - per 16 positions, S^T = C Q^T on v_mfma_f32_16x16x32_bf16 (18 k-steps
+//    over 576): the latent rows are the A operand straight from HBM (lane l
+//    loads 16 bytes of position l % 16), the 16 heads' queries the B
+//    operand, so lane l ends with the scores of positions 4 (l / 16) + i for
+//    head l % 16.
+//  - the rows' first 512 elements also go to LDS (row-major), and P V runs
+//    on v_mfma_f32_16x16x32_bf16 over pairs of 16-position tiles: the K
+//    (position) order of the product is chosen so that a lane's eight
+//    weights are exactly its own scores of the two tiles (no exchange), and
+//    the value operand comes out of LDS through the gfx950 transposing read
+//    ds_read_b64_tr_b16, four positions of one dim per lane per read.
+//  - each weight p enters the product as two bf16 parts, bf16(p) and
+//    bf16(p - bf16(p)), so the weights keep about 16 significant bits
+//    (relative error <= 2^-16) at twice the P V matrix work, which the
+//    matrix cores have to spare at this intensity.
+//  - base-2 online softmax with a lazy rescale (the running max moves only
+//    when a tile pair's max exceeds it by more than 8).
+//  - the next tile's latent rows are loaded while the current one is
+//    multiplied (two register buffers).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "ukv_internal.h"
+
+using ukv::check_launch;
+using ukv::check_pool_call;
+using ukv::fail;
+using ukv::ranges_overlap;
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int64_t kMaxGrid = 0x7fffffff;
+constexpr int kTile = 16;         // positions per score tile
+constexpr int kHeads = 16;        // query heads per wave (the MFMA width)
+constexpr int kMaxChunk = 1024;   // positions per wave (split-K unit), at most
+constexpr int kMinChunk = 128;
+constexpr int64_t kBusyWaves = 4096;
+constexpr float kRescaleGap = 8.0f;
+constexpr int kLatent = 576;      // supported latent width (elements)
+constexpr int kValue = 512;       // supported value width (elements)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct MlaArgs {
+    const uint8_t *pool;
+    uint64_t base;       // byte offset of the layer's latent view (row 0)
+    uint32_t row_bytes;  // latent width * 2
+    uint32_t ps;
+    uint32_t bpp;
+    uint32_t num_pages;
+    const uint16_t *q;  // [num_reqs, q_heads, latent] bf16
+    const int32_t *bt;  // [num_reqs, bt_stride] kernel-facing page indices
+    int64_t bt_stride;
+    const int32_t *seq_lens;
+    int32_t num_reqs;
+    int32_t q_heads;
+    int32_t groups;  // q_heads / 16
+    int32_t window;
+    int32_t max_seq_len;
+    int32_t max_chunks;
+    int32_t chunk;     // positions per unit, a multiple of 32
+    float scale_log2;  // softmax scale * log2(e)
+    double inv_bpp;
+    float *part_o;   // [num_reqs, max_chunks, q_heads, value]
+    float *part_ml;  // [num_reqs, max_chunks, q_heads, 2]: running max (log2 units), row sum; sum < 0: bad unit
+    float *out;      // [num_reqs, q_heads, value]
+    uint32_t *flags;
+};
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ __forceinline__ int32_t first_position(int32_t len, int32_t window) {
+    return (window > 0 && len > window) ? len - window : 0;
+}
+
+__device__ __forceinline__ u32x4 load16(const uint8_t *p) { return *(const u32x4 *)p; }
+
+// e is a multiple of bpp: floor(e / bpp) by a double reciprocal is off by at
+// most one for e < 2^31, fixed by one correction step.
+__device__ __forceinline__ bool multiple_of(int32_t e, int32_t bpp, double inv_bpp) {
+    int32_t q = (int32_t)((double)e * inv_bpp);
+    int32_t r = e - q * bpp;
+    if (r < 0) r += bpp;
+    if (r >= bpp) r -= bpp;
+    return r == 0;
+}
+
+// Row pitch of the LDS value tile: 512 bf16 plus 32 bytes, so that the
+// sixteen rows one transposing read touches spread over the banks.
+constexpr int kPitch = kValue * 2 + 32;
+
+template <int KS, int NB>
+__global__ __launch_bounds__(kWave) void mla_attn_chunk_kernel(MlaArgs a) {
+    static_assert(KS * 32 == kLatent && NB * 16 == kValue, "latent / value width");
+    constexpr int VS = NB / 2;  // 16-byte chunks of a lane's row slice that hold values (dims < 512)
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTile * kPitch];
+    const int lane = lane_id();
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+
+    // one wave per block, chunk-major order (every request's unit 0 first)
+    const int64_t wave = blockIdx.x;
+    const int64_t per_chunk = (int64_t)a.num_reqs * a.groups;
+    const int32_t c = (int32_t)(wave / per_chunk);
+    if (c >= a.max_chunks) return;
+    const int32_t rem = (int32_t)(wave - (int64_t)c * per_chunk);
+    const int32_t r = rem / a.groups;
+    const int32_t hg = rem - r * a.groups;
+    const int32_t len = a.seq_lens[r];
+    if (len <= 0 || len > a.max_seq_len) return;
+    const int32_t j0 = first_position(len, a.window);
+    const int32_t pbeg = j0 + c * a.chunk;
+    if (pbeg >= len) return;
+    const int32_t pend = min(len, pbeg + a.chunk);
+    const int32_t tiles = (pend - pbeg + kTile - 1) / kTile;
+    const int32_t pairs = (tiles + 1) / 2;
+    const int64_t unit = ((int64_t)r * a.max_chunks + c) * a.q_heads + (int64_t)hg * kHeads;  // first head's slot
+
+    // queries as the B operand: column col is head hg*16 + col, lane group grp
+    // holds dims [8 (4 s + grp), +8) at k-step s
+    const uint16_t *qrow = a.q + ((int64_t)r * a.q_heads + hg * kHeads + col) * kLatent;
+    bf16x8 qb[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * s + grp)));
+
+    const uint8_t *view = a.pool + a.base;
+    const uint32_t ps = a.ps;
+    const uint32_t q16 = (uint32_t)kTile / ps, r16 = (uint32_t)kTile - q16 * ps;
+    const int32_t *bt_row = a.bt + (int64_t)r * a.bt_stride;
+    const int32_t entry_lim = (int32_t)(a.num_pages * a.bpp);  // num_pages * bpp * ps < 2^31
+    // the lane's position in tile t is pbeg + 16 t + col; (table column,
+    // page offset) advance by 16 positions per tile without a division
+    int32_t pj = pbeg + col;
+    uint32_t pcol = (uint32_t)pj / ps;
+    uint32_t poff = (uint32_t)pj - pcol * ps;
+    bool bad = false;
+    // dense row of the lane's position in the current tile (-1: past the unit), then step
+    auto next_row = [&]() -> int32_t {
+        int32_t row = -1;
+        if (pj < pend) {
+            const int32_t e = (int64_t)pcol < a.bt_stride ? bt_row[pcol] : -1;
+            if (e < 0 || e >= entry_lim || !multiple_of(e, (int32_t)a.bpp, a.inv_bpp))
+                bad = true;
+            else
+                row = e * (int32_t)ps + (int32_t)poff;  // < n_rows < 2^31
+        }
+        pj += kTile;
+        pcol += q16;
+        poff += r16;
+        if (poff >= ps) {
+            poff -= ps;
+            ++pcol;
+        }
+        return row;
+    };
+    auto load_tile = [&](u32x4 (&k)[KS], int32_t row) {
+        const uint8_t *p = view + (uint64_t)(uint32_t)(row < 0 ? 0 : row) * a.row_bytes + 16 * grp;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) k[s] = row >= 0 ? load16(p + 64 * s) : u32x4{0, 0, 0, 0};
+    };
+    auto scores = [&](const u32x4 (&k)[KS]) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[s]), qb[s], acc, 0, 0, 0);
+        return acc;
+    };
+    // the value part of the lane's row slice into LDS row `lrow` (row-major)
+    auto stage = [&](const u32x4 (&k)[KS], int lrow) {
+        uint8_t *p = lds + lrow * kPitch + 16 * grp;
+#pragma unroll
+        for (int s = 0; s < VS; ++s) *(u32x4 *)(p + 64 * s) = k[s];
+    };
+
+    f32x4 o[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY;  // running max of head col, log2 units
+    float l_run = 0.0f;       // row sum over this lane's positions
+
+    // transposing reads: lane (grp, col) points at position 4 grp + col / 4 of a
+    // tile, dims 16 nb + 4 (col % 4) .. +3; it receives dim 16 nb + col of
+    // positions 4 grp .. 4 grp + 3
+    const int tr_off = (4 * grp + col / 4) * kPitch + 8 * (col % 4);
+
+    u32x4 ka[KS], kb[KS];
+    int32_t row = next_row();
+    if (__any(bad)) goto bad_unit;
+    load_tile(ka, row);
+    for (int t = 0; t < pairs; ++t) {
+        // tile 2t (in ka): the loads of tile 2t+1 go out first
+        row = next_row();
+        if (__any(bad)) goto bad_unit;
+        load_tile(kb, row);
+        const f32x4 sa = scores(ka);
+        stage(ka, col);
+        // tile 2t+1 (in kb): the loads of tile 2t+2 go out first
+        row = next_row();
+        if (__any(bad)) goto bad_unit;
+        if (t + 1 < pairs) load_tile(ka, row);
+        const f32x4 sb = scores(kb);
+        stage(kb, kTile + col);
+
+        const int32_t base_a = pbeg + 2 * t * kTile + 4 * grp;
+        float xa[4], xb[4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xa[i] = base_a + i < pend ? sa[i] * a.scale_log2 : -INFINITY;
+            xb[i] = base_a + kTile + i < pend ? sb[i] * a.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, fmaxf(xa[i], xb[i]));
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const bool need = tmax > m_run + kRescaleGap;
+        if (__any(need)) {
+            const float alpha = need ? exp2f(m_run - tmax) : 1.0f;
+            if (need) m_run = tmax;
+            l_run *= alpha;
+            // o[nb] holds heads 4 grp + i: their factors sit on lanes 4 grp + i
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * grp + i);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[nb][i] *= al[i];
+        }
+        // weights as two bf16 parts; K slots 8 grp + i <- tile 2t, 8 grp + 4 + i <- tile 2t+1
+        bf16x8 whi, wlo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float pa = exp2f(xa[i] - m_run);
+            const float pb = exp2f(xb[i] - m_run);
+            l_run += pa + pb;
+            const __bf16 ha = (__bf16)pa, hb = (__bf16)pb;
+            whi[i] = ha;
+            whi[4 + i] = hb;
+            wlo[i] = (__bf16)(pa - (float)ha);
+            wlo[4 + i] = (__bf16)(pb - (float)hb);
+        }
+        __syncthreads();  // one wave per block: orders the LDS rows written above before the reads
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(lds + tr_off + 32 * nb));
+            const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(lds + kTile * kPitch + tr_off + 32 * nb));
+            const s16x4 vv[2] = {va, vb};
+            const bf16x8 v = __builtin_bit_cast(bf16x8, vv);
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, v, o[nb], 0, 0, 0);
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, v, o[nb], 0, 0, 0);
+        }
+        __syncthreads();  // the reads finish before the next pair overwrites the rows
+    }
+    {
+        // row sums over the four position groups
+        l_run += __shfl_xor(l_run, 16);
+        l_run += __shfl_xor(l_run, 32);
+        // o[nb][i]: head 4 grp + i, dim 16 nb + col
+        float *po = a.part_o + unit * kValue + col;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) po[(4 * grp + i) * kValue + 16 * nb] = o[nb][i];
+        if (lane < kHeads) {
+            a.part_ml[(unit + lane) * 2] = m_run;
+            a.part_ml[(unit + lane) * 2 + 1] = l_run;
+        }
+        return;
+    }
+bad_unit:
+    atomicOr(a.flags, UKV_FLAG_BAD_BLOCK);
+    if (lane < kHeads) a.part_ml[(unit + lane) * 2 + 1] = -1.0f;
+}
+
+// Merge the units of (request, head): out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
+// A bad unit, a request past max_seq_len (UKV_FLAG_LAYOUT) or an empty one
+// gives zeros.  One wave per (request, head); lane l sums dims l + 64 k.
+__global__ __launch_bounds__(kWave) void mla_attn_combine_kernel(MlaArgs a) {
+    constexpr int E = kValue / kWave;
+    const int lane = lane_id();
+    const int32_t r = (int32_t)(blockIdx.x / (uint32_t)a.q_heads);
+    const int32_t h = (int32_t)(blockIdx.x - (uint32_t)r * a.q_heads);
+    float *o = a.out + ((int64_t)r * a.q_heads + h) * kValue;
+    const int32_t len = a.seq_lens[r];
+    int32_t chunks = 0;
+    if (len > a.max_seq_len) {
+        if (h == 0 && lane == 0) atomicOr(a.flags, UKV_FLAG_LAYOUT);
+    } else if (len > 0) {
+        const int32_t n = len - first_position(len, a.window);
+        chunks = (n + a.chunk - 1) / a.chunk;
+    }
+    const int64_t slot0 = (int64_t)r * a.max_chunks * a.q_heads + h;  // unit c of this head: slot0 + c * q_heads
+    float mx = -INFINITY, den = 0.0f;
+    bool bad = false;
+    for (int c = lane; c < chunks; c += kWave) {
+        const float2 ml = *(const float2 *)(a.part_ml + (slot0 + (int64_t)c * a.q_heads) * 2);
+        bad |= ml.y < 0.0f;
+        if (ml.x > mx) {
+            den = den * exp2f(mx - ml.x) + ml.y;
+            mx = ml.x;
+        } else {
+            den += exp2f(ml.x - mx) * ml.y;
+        }
+    }
+    float mh = mx;
+    for (int sh = kWave / 2; sh >= 1; sh >>= 1) mh = fmaxf(mh, __shfl_xor(mh, sh));
+    den = mx == -INFINITY ? 0.0f : den * exp2f(mx - mh);
+    for (int sh = kWave / 2; sh >= 1; sh >>= 1) den += __shfl_xor(den, sh);
+    const bool ok = chunks > 0 && !__any(bad);
+    float acc[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) acc[k] = 0.0f;
+    if (ok) {
+        for (int c = 0; c < chunks; ++c) {
+            const int64_t slot = slot0 + (int64_t)c * a.q_heads;
+            const float w = exp2f(a.part_ml[slot * 2] - mh);
+            const float *po = a.part_o + slot * kValue;
+#pragma unroll
+            for (int k = 0; k < E; ++k) acc[k] = fmaf(w, po[lane + kWave * k], acc[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < E; ++k) o[lane + kWave * k] = ok ? acc[k] / den : 0.0f;
+}
+
+// Positions per unit: the largest of 1024, 768, 512, 384, 256, 128 that
+// still gives about kBusyWaves waves for the batch's bound.
+int32_t mla_chunk_for(int32_t num_reqs, int32_t groups, int32_t max_seq_len, int32_t window) {
+    const int64_t n = (window > 0 && window < max_seq_len) ? window : max_seq_len;
+    int32_t chunk = kMaxChunk;
+    while (chunk > kMinChunk && (int64_t)num_reqs * groups * ((n + chunk - 1) / chunk) < kBusyWaves)
+        chunk = chunk > 512 ? chunk - 256 : chunk - 128;
+    return chunk;
+}
+
+int64_t mla_max_chunks_for(int32_t max_seq_len, int32_t window, int32_t chunk) {
+    const int64_t n = (window > 0 && window < max_seq_len) ? window : max_seq_len;
+    return n > 0 ? (n + chunk - 1) / chunk : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t ukv_mla_decode_attention_workspace_bytes(const ukv_pool *pool, int32_t sub, int32_t num_reqs,
+                                                  int32_t q_heads, int32_t v_dim, int32_t max_seq_len,
+                                                  int32_t window) {
+    if (pool == nullptr || sub < 0 || sub >= pool->plan.n_sub) return 0;
+    if (num_reqs <= 0 || q_heads <= 0 || q_heads % kHeads != 0 || v_dim <= 0 || max_seq_len <= 0) return 0;
+    if (window < 0) window = 0;
+    const int32_t chunk = mla_chunk_for(num_reqs, q_heads / kHeads, max_seq_len, window);
+    return (uint64_t)num_reqs * (uint64_t)mla_max_chunks_for(max_seq_len, window, chunk) * (uint64_t)q_heads *
+           ((uint64_t)v_dim + 2) * sizeof(float);
+}
+
+int ukv_mla_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const void *q_dev, int32_t q_heads,
+                             int32_t v_dim, const int32_t *block_table_dev, int64_t bt_stride,
+                             const int32_t *seq_lens_dev, int32_t num_reqs, int32_t max_seq_len, int32_t window,
+                             float scale, float *out_dev, void *workspace_dev, uint64_t workspace_bytes,
+                             hipStream_t stream) {
+    const char *who = "ukv_mla_decode_attention";
+    int rc = check_pool_call(pool, sub, who);
+    if (rc != UKV_OK) return rc;
+    const ukv_subpool_spec &s = pool->spec[sub];
+    const ukv_subpool_plan &p = pool->plan.sub[sub];
+    if (s.kind != UKV_MLA) return fail(UKV_ERR_INVALID_ARG, "%s: sub-pool %d is not MLA", who, sub);
+    if (s.elem_bytes != 2) return fail(UKV_ERR_INVALID_ARG, "%s: latent rows must be bf16 (itemsize %d)", who, s.elem_bytes);
+    if (layer < 0 || layer >= s.layer_num)
+        return fail(UKV_ERR_INVALID_ARG, "%s: layer %d outside [0, %d)", who, layer, s.layer_num);
+    if (s.head_dim != kLatent || v_dim != kValue)
+        return fail(UKV_ERR_INVALID_ARG, "%s: latent width %d / value width %d (supported: %d / %d)", who, s.head_dim,
+                    v_dim, kLatent, kValue);
+    if (q_heads <= 0 || q_heads % kHeads != 0)
+        return fail(UKV_ERR_INVALID_ARG, "%s: q_heads %d is not a positive multiple of %d", who, q_heads, kHeads);
+    if (num_reqs < 0 || window < 0 || max_seq_len < 0 || bt_stride < 0)
+        return fail(UKV_ERR_INVALID_ARG, "%s: negative size", who);
+    if (!std::isfinite(scale)) return fail(UKV_ERR_INVALID_ARG, "%s: scale is not finite", who);
+    if (num_reqs == 0) return UKV_OK;
+    if (q_dev == nullptr || seq_lens_dev == nullptr || out_dev == nullptr)
+        return fail(UKV_ERR_INVALID_ARG, "%s: null q, seq_lens or output", who);
+    if (((uintptr_t)q_dev % 16) != 0 || ((uintptr_t)out_dev % 16) != 0)
+        return fail(UKV_ERR_ALIGNMENT, "%s: q and out must be 16-byte aligned", who);
+    ukv_view vw;
+    ukv::view_of(pool->plan, s, sub, layer, 0, &vw);
+    if (((uintptr_t)pool->raw + vw.byte_offset) % 16 != 0)
+        return fail(UKV_ERR_ALIGNMENT, "%s: the layer's view is not 16-byte aligned", who);
+    const int32_t groups = q_heads / kHeads;
+    const int32_t chunk = mla_chunk_for(num_reqs, groups, max_seq_len, window);
+    const int64_t chunks = mla_max_chunks_for(max_seq_len, window, chunk);
+    const uint64_t need =
+        ukv_mla_decode_attention_workspace_bytes(pool, sub, num_reqs, q_heads, v_dim, max_seq_len, window);
+    if (chunks > 0) {
+        if (block_table_dev == nullptr || bt_stride < 1)
+            return fail(UKV_ERR_INVALID_ARG, "%s: null block table or bt_stride < 1", who);
+        if (workspace_dev == nullptr || workspace_bytes < need)
+            return fail(UKV_ERR_INVALID_ARG, "%s: workspace of %llu bytes, %llu needed", who,
+                        (unsigned long long)workspace_bytes, (unsigned long long)need);
+        if (((uintptr_t)workspace_dev % 16) != 0)
+            return fail(UKV_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", who);
+    }
+    const uint64_t out_bytes = (uint64_t)num_reqs * q_heads * kValue * sizeof(float);
+    if (ranges_overlap(out_dev, out_bytes, q_dev, (uint64_t)num_reqs * q_heads * kLatent * 2) ||
+        ranges_overlap(out_dev, out_bytes, workspace_dev, need) ||
+        ranges_overlap(out_dev, out_bytes, pool->raw, pool->raw_bytes))
+        return fail(UKV_ERR_INVALID_ARG, "%s: output overlaps q, the workspace or the pool", who);
+    const int64_t grid = (int64_t)num_reqs * chunks * groups;  // one wave per block
+    if (grid > kMaxGrid || (int64_t)num_reqs * q_heads > kMaxGrid)
+        return fail(UKV_ERR_INVALID_ARG, "%s: batch too large for one launch", who);
+    MlaArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.pool = pool->raw;
+    a.base = vw.byte_offset;
+    a.row_bytes = (uint32_t)p.row_bytes;
+    a.ps = (uint32_t)pool->plan.page_size;
+    a.bpp = (uint32_t)p.blocks_per_page;
+    a.num_pages = (uint32_t)s.num_pages;
+    a.q = (const uint16_t *)q_dev;
+    a.bt = block_table_dev;
+    a.bt_stride = bt_stride;
+    a.seq_lens = seq_lens_dev;
+    a.num_reqs = num_reqs;
+    a.q_heads = q_heads;
+    a.groups = groups;
+    a.window = window;
+    a.max_seq_len = max_seq_len;
+    a.max_chunks = (int32_t)chunks;
+    a.chunk = chunk;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    a.inv_bpp = 1.0 / (double)p.blocks_per_page;
+    float *ws = (float *)workspace_dev;
+    a.part_o = ws;
+    a.part_ml = ws == nullptr ? nullptr : ws + (uint64_t)num_reqs * chunks * q_heads * kValue;
+    a.out = out_dev;
+    a.flags = pool->flags_dev;
+    if (grid > 0)
+        hipLaunchKernelGGL((mla_attn_chunk_kernel<kLatent / 32, kValue / 16>), dim3((unsigned)grid), dim3(kWave), 0,
+                           stream, a);
+    hipLaunchKernelGGL(mla_attn_combine_kernel, dim3((unsigned)(num_reqs * q_heads)), dim3(kWave), 0, stream, a);
+    return check_launch(who);
+}
+
+}  // extern "C"
