@@ -45,9 +45,10 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "KV store/gather/move HBM GB/s and % of peak, Llama-3-8B-shape pool"
 KERNEL_SRC = os.path.join(ROOT, "store_gather_amd", "csrc", "ukv_runtime.hip")
 ATTN_SRC = os.path.join(ROOT, "store_gather_amd", "csrc", "ukv_attention.hip")
+MLA_ATTN_SRC = os.path.join(ROOT, "store_gather_amd", "csrc", "ukv_mla_attention.hip")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 WORKLOADS = ("decode_8b", "prefill_8b", "hybrid", "move_70b", "tiny", "decode_8b_fused", "prefill_8b_fused",
-             "compact_8b", "swa_decode", "decode_attn_8b")
+             "compact_8b", "swa_decode", "decode_attn_8b", "decode_attn_mla")
 
 
 def log(msg):
@@ -61,7 +62,8 @@ def num(x, nd):
 
 def kernel_source_hash(kernel: str = "") -> str:
     """First 16 hex digits of the SHA-256 of the source file that holds `kernel`."""
-    with open(ATTN_SRC if kernel.startswith("attn") else KERNEL_SRC, "rb") as f:
+    src = MLA_ATTN_SRC if kernel.startswith("mla_attn") else ATTN_SRC if kernel.startswith("attn") else KERNEL_SRC
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -125,7 +127,7 @@ def op_rows(op: Op, s: "Script") -> int:
         return int(s.arrays[f"msrc{op.sub}"].size) * (int(a["l1"]) - int(a["l0"]))
     if op.kind == "move_pages":
         return int(s.arrays[f"psrc{op.sub}"].size) * s.page_size * s.shapes[op.sub].layer_num
-    if op.kind == "attention":
+    if op.kind in ("attention", "mla_attention"):
         return int(s.arrays[f"lens{op.sub}"].astype(np.int64).sum())
     return 0
 
@@ -174,6 +176,13 @@ DESCRIPTIONS = {
                       "of U[1024, 8192] positions with 32 query heads each (GQA 4); per step: translate the 256 new "
                       "slots and build the prefix-only page table once, then per layer store the 256 new K/V rows "
                       "and run decode attention over every request straight from the dense views (fp32 output)",
+    "decode_attn_mla": "decode_attn_mla: the read path on the hybrid workload's MLA sub-pool (24 layers, one "
+                       "576-wide bf16 latent row per token, page 64, 16,538 pages, ~28 GiB) of Irwin-Hall bf16 "
+                       "values; 128 requests of U[256, 16384] positions, 16 query heads each (a 128-head MLA model's "
+                       "share of one GPU at 8-way tensor parallelism); per step: translate the 128 new slots and "
+                       "build the prefix-only page table once, then per layer store the 128 new latent rows and run "
+                       "decode attention over every request straight from the dense latent view (scores over the "
+                       "whole row, values its first 512 elements, fp32 output)",
     "compact_8b": "compact_8b: the prefill_8b pool (16,384 pages of 2 MiB) with its 16 requests addressed through a "
                   "virtual-to-physical table; per step: internal ids of the batch (translate_loc), relocation of every "
                   "live page above the watermark into the free pages below it (whole page envelopes, all 32 layers, "
@@ -190,6 +199,8 @@ def build_script(name: str, W, reduced: bool = False) -> Script:
         return swa_script(W, reduced)
     if name == "decode_attn_8b":
         return attention_script(W, reduced)
+    if name == "decode_attn_mla":
+        return attention_mla_script(W, reduced)
     if name.endswith("_fused"):
         return fuse_layers(build_script(name[: -len("_fused")], W, reduced), name,
                            gathers=name.startswith("prefill"))
@@ -402,6 +413,44 @@ def attention_script(W, reduced: bool) -> Script:
                   lambda op: op.kind == "attention", "attn_chunk", counts, dtype="bf16")
 
 
+ATTN_MLA_Q_HEADS = 16  # a 128-head MLA model at 8-way tensor parallelism
+ATTN_MLA_SCALE = 192 ** -0.5  # 1 / sqrt(query-key head dim of the unabsorbed form: 128 + 64)
+MLA_V_DIM = 512  # value width: the latent's compressed part ahead of its 64 rotary elements
+
+
+def attention_mla_script(W, reduced: bool) -> Script:
+    """The MLA read path's decode step: page table, then per layer store + MLA decode attention."""
+    w = W.hybrid(num_reqs=12) if reduced else W.hybrid()
+    ps = w.page_size
+    shape = w.shapes[1]
+    lens = w.req_lens[1].astype(np.int32)
+    pages = w.req_pages[1]
+    R, hq, lat = lens.size, ATTN_MLA_Q_HEADS, shape.head_dim
+    rb = shape.row_bytes
+    # the token decoded now sits at each request's last position
+    slots = W.slots_of_requests(pages, lens, ps).astype(np.int64)[np.cumsum(lens.astype(np.int64)) - 1]
+    req = W.padded_table(pages)
+    arrays = {"slots0": slots, "req0": req, "lens0": lens,
+              "q0": W.irwin_hall_bf16_host(43, 0, 2 * R * hq * lat).view(np.int16).reshape(R, hq, lat)}
+    pages_read = _pages_read(pages, lens, 0, ps)
+    attn_bytes = (int(lens.astype(np.int64).sum()) * rb + R * hq * (lat * 2 + MLA_V_DIM * 4) + pages_read * 4
+                  + R * 4)
+    ops = [Op("translate", 0, "translate sub0", {"inp": "slots0", "out": "ids0"}, R * 12),
+           Op("build_table", 0, "build_page_table sub0", {"inp": "req0", "out": "bt0"}, req.size * 8 + R * 4)]
+    for layer in range(shape.layer_num):
+        ops.append(Op("store", 0, "store mla sub0", {"layer": layer, "ids": "ids0", "row0": layer * R, "n": R},
+                      R * (2 * rb + 4)))
+        ops.append(Op("mla_attention", 0, "mla_attention sub0", {"layer": layer, "max_len": int(lens.max())},
+                      attn_bytes))
+    buffers = {"src0_0": (shape.layer_num * R, rb)}
+    pos = int(lens.astype(np.int64).sum())
+    counts = {"layers": shape.layer_num, "requests": int(R), "q_heads": hq, "latent": lat, "v_dim": MLA_V_DIM,
+              "attended_positions_per_layer": pos,
+              "attention_flops_per_layer": int(2 * pos * hq * (lat + MLA_V_DIM))}
+    return Script("decode_attn_mla", DESCRIPTIONS["decode_attn_mla"], [shape], ps, arrays, buffers, ops,
+                  lambda op: op.kind == "mla_attention", "mla_attn_chunk", counts, dtype="bf16")
+
+
 def fuse_layers(s: Script, name: str, gathers: bool) -> Script:
     """The same step with each sub-pool's per-layer stores (and, if asked, its per-layer
     gathers, when they share one window) replaced by one launch over all layers."""
@@ -451,7 +500,7 @@ class GpuRunner:
         n = (int(plan.required_bytes) + 7) // 8 * 8
         self.pool = U.allocate_pool(script.shapes, script.page_size, device=device,
                                     extra_bytes=n - int(plan.required_bytes))
-        attn = any(op.kind == "attention" for op in script.ops)
+        attn = any(op.kind in ("attention", "mla_attention") for op in script.ops)
         if fill and attn:
             W.irwin_hall_fill_device(self.pool.raw, 1)  # attention reads whole rows: finite bf16 values
         elif fill:
@@ -460,9 +509,15 @@ class GpuRunner:
         if attn:
             q = self.t["q0"].view(torch.bfloat16)
             self.t["q0"] = q
-            mx = max(op.args["max_len"] for op in script.ops if op.kind == "attention")
-            self.t["attn_out"] = torch.empty(q.shape, dtype=torch.float32, device=device)
-            need = U.ukv_decode_attention_workspace_bytes(self.pool, 0, q.shape[0], q.shape[1], mx, 0)
+            mx = max(op.args["max_len"] for op in script.ops if op.kind in ("attention", "mla_attention"))
+            if any(op.kind == "mla_attention" for op in script.ops):
+                self.t["attn_out"] = torch.empty((q.shape[0], q.shape[1], MLA_V_DIM), dtype=torch.float32,
+                                                 device=device)
+                need = U.ukv_mla_decode_attention_workspace_bytes(self.pool, 0, q.shape[0], q.shape[1], MLA_V_DIM,
+                                                                  mx, 0)
+            else:
+                self.t["attn_out"] = torch.empty(q.shape, dtype=torch.float32, device=device)
+                need = U.ukv_decode_attention_workspace_bytes(self.pool, 0, q.shape[0], q.shape[1], mx, 0)
             self.t["attn_ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
         for op in script.ops:  # int32 outputs of the translations, shaped like their inputs
             if "out" in op.args and op.args["out"] not in self.t:
@@ -494,6 +549,10 @@ class GpuRunner:
         elif op.kind == "attention":
             U.ukv_decode_attention(self.pool, sub, a["layer"], t["q0"], t[f"bt{sub}"], t[f"lens{sub}"], a["max_len"],
                                    0, ATTN_SCALE, out=t["attn_out"], workspace=t["attn_ws"])
+        elif op.kind == "mla_attention":
+            U.ukv_mla_decode_attention(self.pool, sub, a["layer"], t["q0"], t[f"bt{sub}"], t[f"lens{sub}"],
+                                       a["max_len"], 0, ATTN_MLA_SCALE, v_dim=MLA_V_DIM, out=t["attn_out"],
+                                       workspace=t["attn_ws"])
         elif op.kind == "move_pages":
             U.ukv_move_pages(self.pool, sub, t[f"pdst{sub}"], t[f"psrc{sub}"])
         elif op.kind == "remap_pages":
@@ -536,8 +595,8 @@ def cpu_baseline(name: str, W, budget_s: float = 12.0) -> dict:
              for x in s.shapes]
     req = oracle.plan(specs, s.page_size).required_bytes
     # pages touched up front; 0x3F3F is the finite bf16 value 0.746 for the attention reads
-    pool = oracle.OraclePool(specs, s.page_size, np.full(req, 0x3F if name == "decode_attn_8b" else 0x5A,
-                                                         dtype=np.uint8))
+    attn = name in ("decode_attn_8b", "decode_attn_mla")
+    pool = oracle.OraclePool(specs, s.page_size, np.full(req, 0x3F if attn else 0x5A, dtype=np.uint8))
     h = dict(s.arrays)
     bufs = {k: np.full((rows, rb), 7, dtype=np.uint8) for k, (rows, rb) in s.buffers.items()}
     done_bytes = 0
@@ -564,6 +623,14 @@ def cpu_baseline(name: str, W, budget_s: float = 12.0) -> dict:
             with threadpool_limits(limits=1):  # numpy's BLAS on one thread, like the C oracle
                 oracle_attention.decode_attention(pool, sub, a["layer"], h["q0"].view(np.uint16), h[f"bt{sub}"],
                                                   h[f"lens{sub}"], 0, ATTN_SCALE, a["max_len"])
+        elif op.kind == "mla_attention":
+            from threadpoolctl import threadpool_limits
+
+            from oracle import attention as oracle_attention
+            with threadpool_limits(limits=1):
+                oracle_attention.decode_attention(pool, sub, a["layer"], h["q0"].view(np.uint16), h[f"bt{sub}"],
+                                                  h[f"lens{sub}"], 0, ATTN_MLA_SCALE, a["max_len"],
+                                                  v_dim=MLA_V_DIM)
         elif op.kind == "move_pages":
             pool.move_pages(sub, h[f"pdst{sub}"], h[f"psrc{sub}"])
         elif op.kind == "remap_pages":
@@ -602,6 +669,9 @@ def cpu_baseline(name: str, W, budget_s: float = 12.0) -> dict:
     if name == "decode_attn_8b":
         shrunk = (" (16 of the 256 requests on 1,024 pages of the same geometry; fp64 numpy attention, one "
                   "BLAS thread, over rows the C oracle addresses)")
+    if name == "decode_attn_mla":
+        shrunk = (" (12 of the 128 requests, their pool sized to fit, same latent geometry; fp64 numpy attention, "
+                  "one BLAS thread, over rows the C oracle addresses)")
     return {
         "value": round(done_bytes / dt / 1e9, 3),
         "unit": "GB/s",

@@ -15,10 +15,18 @@
 // read is ~30 FLOP per byte, beyond what the vector ALUs sustain at HBM
 // bandwidth, so both products run on the matrix cores:
 //
-//  - split-K over positions: one 64-lane wave owns (unit of positions,
-//    request, group of 16 query heads) and writes an unnormalised partial
-//    (running max, row sum, 16 x 512 sums) to a workspace; a second kernel
-//    merges the units of each (request, head).
+//  - balanced split-K: the batch's positions, request after request, form
+//    one sequence that is cut into equal spans, one per wave (about one wave
+//    per SIMD of the chip, so every wave streams the same number of bytes
+//    and none is left over for a second round).  A wave walks its span
+//    request by request and writes an unnormalised partial (running max, row
+//    sum, 16 x 512 sums) for each request it touches to slot (wave +
+//    request), which is unique; a second kernel merges each request's slots.
+//    Every wave finds its first request by a prefix sum over the lengths;
+//    the first wave also leaves the prefix sums for the merge.
+//  - the query-head groups of one span sit on one XCD (blocks b with the
+//    same b % 8), so the latent rows they share are read once into that
+//    XCD's L2.
 //  - per 16 positions, S^T = C Q^T on v_mfma_f32_16x16x32_bf16 (18 k-steps
 //    over 576): the latent rows are the A operand straight from HBM (lane l
 //    loads 16 bytes of position l % 16), the 16 heads' queries the B
@@ -32,12 +40,13 @@
 //    ds_read_b64_tr_b16, four positions of one dim per lane per read.
 //  - each weight p enters the product as two bf16 parts, bf16(p) and
 //    bf16(p - bf16(p)), so the weights keep about 16 significant bits
-//    (relative error <= 2^-16) at twice the P V matrix work, which the
+//    (relative error <= 2^-16), at twice the P V matrix work, which the
 //    matrix cores have to spare at this intensity.
 //  - base-2 online softmax with a lazy rescale (the running max moves only
-//    when a tile pair's max exceeds it by more than 8).
+//    when a tile's max exceeds it by more than 8).
 //  - the next tile's latent rows are loaded while the current one is
-//    multiplied (two register buffers).
+//    multiplied (two register buffers; one wave per SIMD holds the 16 x 512
+//    fp32 sums, the queries and the two tiles).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -54,14 +63,14 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int64_t kMaxGrid = 0x7fffffff;
-constexpr int kTile = 16;         // positions per score tile
-constexpr int kHeads = 16;        // query heads per wave (the MFMA width)
-constexpr int kMaxChunk = 1024;   // positions per wave (split-K unit), at most
-constexpr int kMinChunk = 128;
-constexpr int64_t kBusyWaves = 4096;
+constexpr int kTile = 16;                // positions per tile
+constexpr int kHeads = 16;               // query heads per wave (the MFMA width)
+constexpr int64_t kTargetWaves = 1024;   // one per SIMD of MI355X (256 CUs x 4) at this kernel's occupancy
+constexpr int64_t kMinSpan = 256;        // positions per wave, at least (a partial is 32 KiB)
+constexpr int kXcds = 8;                 // workgroups go round-robin over the 8 XCDs
 constexpr float kRescaleGap = 8.0f;
-constexpr int kLatent = 576;      // supported latent width (elements)
-constexpr int kValue = 512;       // supported value width (elements)
+constexpr int kLatent = 576;             // supported latent width (elements)
+constexpr int kValue = 512;              // supported value width (elements)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -84,12 +93,12 @@ struct MlaArgs {
     int32_t groups;  // q_heads / 16
     int32_t window;
     int32_t max_seq_len;
-    int32_t max_chunks;
-    int32_t chunk;     // positions per unit, a multiple of 32
+    int32_t spans;     // waves per head group, a multiple of 8
     float scale_log2;  // softmax scale * log2(e)
     double inv_bpp;
-    float *part_o;   // [num_reqs, max_chunks, q_heads, value]
-    float *part_ml;  // [num_reqs, max_chunks, q_heads, 2]: running max (log2 units), row sum; sum < 0: bad unit
+    int64_t *cum;    // [num_reqs + 2]: exclusive prefix sums of the attended lengths, their total, the span
+    float *part_o;   // [spans + num_reqs slots, q_heads, value]
+    float *part_ml;  // [spans + num_reqs slots, q_heads, 2]: running max (log2 units), row sum; sum < 0: bad
     float *out;      // [num_reqs, q_heads, value]
     uint32_t *flags;
 };
@@ -98,6 +107,20 @@ __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1
 
 __device__ __forceinline__ int32_t first_position(int32_t len, int32_t window) {
     return (window > 0 && len > window) ? len - window : 0;
+}
+
+// Positions request r attends to: 0 when it is empty or past the caller's bound.
+__device__ __forceinline__ int32_t attended(const MlaArgs &a, int32_t len) {
+    return (len <= 0 || len > a.max_seq_len) ? 0 : len - first_position(len, a.window);
+}
+
+__device__ __forceinline__ int64_t wave_inclusive_scan(int64_t v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int64_t u = __shfl_up(v, (unsigned)d);
+        if (lane >= d) v += u;
+    }
+    return v;
 }
 
 __device__ __forceinline__ u32x4 load16(const uint8_t *p) { return *(const u32x4 *)p; }
@@ -112,198 +135,239 @@ __device__ __forceinline__ bool multiple_of(int32_t e, int32_t bpp, double inv_b
     return r == 0;
 }
 
-// Row pitch of the LDS value tile: 512 bf16 plus 32 bytes, so that the
+// Row pitch of the LDS value tiles: 512 bf16 plus 32 bytes, so that the
 // sixteen rows one transposing read touches spread over the banks.
 constexpr int kPitch = kValue * 2 + 32;
 
 template <int KS, int NB>
-__global__ __launch_bounds__(kWave) void mla_attn_chunk_kernel(MlaArgs a) {
+__global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
     static_assert(KS * 32 == kLatent && NB * 16 == kValue, "latent / value width");
     constexpr int VS = NB / 2;  // 16-byte chunks of a lane's row slice that hold values (dims < 512)
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTile * kPitch];
+
     const int lane = lane_id();
     const int grp = lane >> 4;
     const int col = lane & 15;
 
-    // one wave per block, chunk-major order (every request's unit 0 first)
-    const int64_t wave = blockIdx.x;
-    const int64_t per_chunk = (int64_t)a.num_reqs * a.groups;
-    const int32_t c = (int32_t)(wave / per_chunk);
-    if (c >= a.max_chunks) return;
-    const int32_t rem = (int32_t)(wave - (int64_t)c * per_chunk);
-    const int32_t r = rem / a.groups;
-    const int32_t hg = rem - r * a.groups;
-    const int32_t len = a.seq_lens[r];
-    if (len <= 0 || len > a.max_seq_len) return;
-    const int32_t j0 = first_position(len, a.window);
-    const int32_t pbeg = j0 + c * a.chunk;
-    if (pbeg >= len) return;
-    const int32_t pend = min(len, pbeg + a.chunk);
-    const int32_t tiles = (pend - pbeg + kTile - 1) / kTile;
-    const int32_t pairs = (tiles + 1) / 2;
-    const int64_t unit = ((int64_t)r * a.max_chunks + c) * a.q_heads + (int64_t)hg * kHeads;  // first head's slot
+    // block b -> (span w, head group hg), with every group of a span on XCD b % 8
+    const int32_t b = (int32_t)blockIdx.x;
+    const int32_t y = b / kXcds;
+    const int32_t hg = y % a.groups;
+    const int32_t w = (y / a.groups) * kXcds + (b - y * kXcds);
+    const bool writer = w == 0 && hg == 0;
+
+    // total attended positions N (the first wave records the prefix sums), then the span
+    int64_t carry = 0;
+    for (int32_t base = 0; base < a.num_reqs; base += kWave) {
+        const int32_t r = base + lane;
+        const int64_t n = r < a.num_reqs ? attended(a, a.seq_lens[r]) : 0;
+        const int64_t incl = wave_inclusive_scan(n, lane);
+        if (writer && r < a.num_reqs) a.cum[r] = carry + incl - n;
+        carry += __shfl(incl, kWave - 1);
+    }
+    const int64_t total = carry;
+    int64_t span = (total + a.spans - 1) / a.spans;
+    span = span < kMinSpan ? kMinSpan : span;
+    if (writer && lane == 0) {
+        a.cum[a.num_reqs] = total;
+        a.cum[a.num_reqs + 1] = span;
+    }
+    const int64_t start = (int64_t)w * span;
+    if (start >= total) return;
+    const int64_t end = start + span < total ? start + span : total;
+    // the request holding position `start`, and its prefix sum
+    int32_t r = -1;
+    int64_t rbase = 0;
+    carry = 0;
+    for (int32_t base = 0; base < a.num_reqs && r < 0; base += kWave) {
+        const int32_t rr = base + lane;
+        const int64_t n = rr < a.num_reqs ? attended(a, a.seq_lens[rr]) : 0;
+        const int64_t incl = wave_inclusive_scan(n, lane);
+        const int64_t excl = carry + incl - n;
+        const uint64_t hit = __ballot(n > 0 && excl <= start && start < excl + n);
+        if (hit != 0) {
+            const int l = __ffsll((unsigned long long)hit) - 1;
+            r = base + l;
+            rbase = __shfl(excl, l);
+        }
+        carry += __shfl(incl, kWave - 1);
+    }
 
     // queries as the B operand: column col is head hg*16 + col, lane group grp
-    // holds dims [8 (4 s + grp), +8) at k-step s
-    const uint16_t *qrow = a.q + ((int64_t)r * a.q_heads + hg * kHeads + col) * kLatent;
+    // holds dims [8 (4 s + grp), +8) at k-step s (loaded per request)
     bf16x8 qb[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * s + grp)));
-
     const uint8_t *view = a.pool + a.base;
     const uint32_t ps = a.ps;
     const uint32_t q16 = (uint32_t)kTile / ps, r16 = (uint32_t)kTile - q16 * ps;
-    const int32_t *bt_row = a.bt + (int64_t)r * a.bt_stride;
     const int32_t entry_lim = (int32_t)(a.num_pages * a.bpp);  // num_pages * bpp * ps < 2^31
-    // the lane's position in tile t is pbeg + 16 t + col; (table column,
-    // page offset) advance by 16 positions per tile without a division
-    int32_t pj = pbeg + col;
-    uint32_t pcol = (uint32_t)pj / ps;
-    uint32_t poff = (uint32_t)pj - pcol * ps;
-    bool bad = false;
-    // dense row of the lane's position in the current tile (-1: past the unit), then step
-    auto next_row = [&]() -> int32_t {
-        int32_t row = -1;
-        if (pj < pend) {
-            const int32_t e = (int64_t)pcol < a.bt_stride ? bt_row[pcol] : -1;
-            if (e < 0 || e >= entry_lim || !multiple_of(e, (int32_t)a.bpp, a.inv_bpp))
-                bad = true;
-            else
-                row = e * (int32_t)ps + (int32_t)poff;  // < n_rows < 2^31
-        }
-        pj += kTile;
-        pcol += q16;
-        poff += r16;
-        if (poff >= ps) {
-            poff -= ps;
-            ++pcol;
-        }
-        return row;
-    };
-    auto load_tile = [&](u32x4 (&k)[KS], int32_t row) {
-        const uint8_t *p = view + (uint64_t)(uint32_t)(row < 0 ? 0 : row) * a.row_bytes + 16 * grp;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) k[s] = row >= 0 ? load16(p + 64 * s) : u32x4{0, 0, 0, 0};
-    };
-    auto scores = [&](const u32x4 (&k)[KS]) {
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[s]), qb[s], acc, 0, 0, 0);
-        return acc;
-    };
-    // the value part of the lane's row slice into LDS row `lrow` (row-major)
-    auto stage = [&](const u32x4 (&k)[KS], int lrow) {
-        uint8_t *p = lds + lrow * kPitch + 16 * grp;
-#pragma unroll
-        for (int s = 0; s < VS; ++s) *(u32x4 *)(p + 64 * s) = k[s];
-    };
-
-    f32x4 o[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY;  // running max of head col, log2 units
-    float l_run = 0.0f;       // row sum over this lane's positions
-
-    // transposing reads: lane (grp, col) points at position 4 grp + col / 4 of a
-    // tile, dims 16 nb + 4 (col % 4) .. +3; it receives dim 16 nb + col of
+    // transposing reads: lane (grp, col) points at position 4 grp + col / 4 of
+    // the tile, dims 16 nb + 4 (col % 4) .. +3; it receives dim 16 nb + col of
     // positions 4 grp .. 4 grp + 3
     const int tr_off = (4 * grp + col / 4) * kPitch + 8 * (col % 4);
 
-    u32x4 ka[KS], kb[KS];
-    int32_t row = next_row();
-    if (__any(bad)) goto bad_unit;
-    load_tile(ka, row);
-    for (int t = 0; t < pairs; ++t) {
-        // tile 2t (in ka): the loads of tile 2t+1 go out first
-        row = next_row();
-        if (__any(bad)) goto bad_unit;
-        load_tile(kb, row);
-        const f32x4 sa = scores(ka);
-        stage(ka, col);
-        // tile 2t+1 (in kb): the loads of tile 2t+2 go out first
-        row = next_row();
-        if (__any(bad)) goto bad_unit;
-        if (t + 1 < pairs) load_tile(ka, row);
-        const f32x4 sb = scores(kb);
-        stage(kb, kTile + col);
-
-        const int32_t base_a = pbeg + 2 * t * kTile + 4 * grp;
-        float xa[4], xb[4];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xa[i] = base_a + i < pend ? sa[i] * a.scale_log2 : -INFINITY;
-            xb[i] = base_a + kTile + i < pend ? sb[i] * a.scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, fmaxf(xa[i], xb[i]));
+    f32x4 o[NB];
+    u32x4 k0[KS], k1[KS];
+    int64_t cur = start;
+    while (cur < end) {
+        r = __builtin_amdgcn_readfirstlane(r);
+        const int32_t len = a.seq_lens[r];
+        const int32_t n = attended(a, len);
+        if (n == 0) {
+            ++r;
+            continue;
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const bool need = tmax > m_run + kRescaleGap;
-        if (__any(need)) {
-            const float alpha = need ? exp2f(m_run - tmax) : 1.0f;
-            if (need) m_run = tmax;
-            l_run *= alpha;
-            // o[nb] holds heads 4 grp + i: their factors sit on lanes 4 grp + i
-            float al[4];
+        const int64_t seg = (rbase + n < end ? rbase + n : end) - cur;
+        const int32_t pbeg = first_position(len, a.window) + (int32_t)(cur - rbase);
+        const int32_t pend = pbeg + (int32_t)seg;
+        const int32_t tiles = (pend - pbeg + kTile - 1) / kTile;
+        const int64_t slot = (int64_t)w + r;
+
+        const uint16_t *qrow = a.q + ((int64_t)r * a.q_heads + hg * kHeads + col) * kLatent;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * grp + i);
+        for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * s + grp)));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        float m_run = -INFINITY;  // running max of head col, log2 units
+        float l_run = 0.0f;       // row sum over this lane's positions
+
+        // the lane's position in tile t is pbeg + 16 t + col; (table column,
+        // page offset) advance by 16 positions per tile without a division
+        const int32_t *bt_row = a.bt + (int64_t)r * a.bt_stride;
+        int32_t pj = pbeg + col;
+        uint32_t pcol = (uint32_t)pj / ps;
+        uint32_t poff = (uint32_t)pj - pcol * ps;
+        bool bad = false;
+        auto next_row = [&]() -> int32_t {
+            int32_t row = -1;
+            if (pj < pend) {
+                const int32_t e = (int64_t)pcol < a.bt_stride ? bt_row[pcol] : -1;
+                if (e < 0 || e >= entry_lim || !multiple_of(e, (int32_t)a.bpp, a.inv_bpp))
+                    bad = true;
+                else
+                    row = e * (int32_t)ps + (int32_t)poff;  // < n_rows < 2^31
+            }
+            pj += kTile;
+            pcol += q16;
+            poff += r16;
+            if (poff >= ps) {
+                poff -= ps;
+                ++pcol;
+            }
+            return row;
+        };
+        auto load_tile = [&](u32x4 (&k)[KS], int32_t row) {
+            const uint8_t *p = view + (uint64_t)(uint32_t)(row < 0 ? 0 : row) * a.row_bytes + 16 * grp;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) k[s] = row >= 0 ? load16(p + 64 * s) : u32x4{0, 0, 0, 0};
+        };
+        auto scores = [&](const u32x4 (&k)[KS]) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[s]), qb[s], acc, 0, 0, 0);
+            return acc;
+        };
+        auto stage = [&](const u32x4 (&k)[KS], int lrow) {
+            uint8_t *st = lds + lrow * kPitch + 16 * grp;
+#pragma unroll
+            for (int s = 0; s < VS; ++s) *(u32x4 *)(st + 64 * s) = k[s];
+        };
+        const int32_t pairs = (tiles + 1) / 2;
+        int32_t row = next_row();
+        bool seg_bad = __any(bad);
+        if (!seg_bad) {
+            load_tile(k0, row);
+            for (int32_t t = 0; t < pairs; ++t) {
+                row = next_row();
+                if (__any(bad)) { seg_bad = true; break; }
+                load_tile(k1, row);
+                const f32x4 sa = scores(k0);
+                stage(k0, col);
+                row = next_row();
+                if (__any(bad)) { seg_bad = true; break; }
+                if (t + 1 < pairs) load_tile(k0, row);
+                const f32x4 sb = scores(k1);
+                stage(k1, kTile + col);
+                const int32_t base_a = pbeg + 2 * t * kTile + 4 * grp;
+                float xa[4], xb[4];
+                float tmax = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xa[i] = base_a + i < pend ? sa[i] * a.scale_log2 : -INFINITY;
+                    xb[i] = base_a + kTile + i < pend ? sb[i] * a.scale_log2 : -INFINITY;
+                    tmax = fmaxf(tmax, fmaxf(xa[i], xb[i]));
+                }
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                const bool need = tmax > m_run + kRescaleGap;
+                if (__any(need)) {
+                    const float alpha = need ? exp2f(m_run - tmax) : 1.0f;
+                    if (need) m_run = tmax;
+                    l_run *= alpha;
+                    float al[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * grp + i);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o[nb][i] *= al[i];
+                }
+                bf16x8 whi, wlo;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pa = exp2f(xa[i] - m_run);
+                    const float pb = exp2f(xb[i] - m_run);
+                    l_run += pa + pb;
+                    const __bf16 ha = (__bf16)pa, hb = (__bf16)pb;
+                    whi[i] = ha;
+                    whi[4 + i] = hb;
+                    wlo[i] = (__bf16)(pa - (float)ha);
+                    wlo[4 + i] = (__bf16)(pb - (float)hb);
+                }
+                __syncthreads();
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(lds + tr_off + 32 * nb));
+                    const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(lds + kTile * kPitch + tr_off + 32 * nb));
+                    const s16x4 vv[2] = {va, vb};
+                    const bf16x8 v = __builtin_bit_cast(bf16x8, vv);
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, v, o[nb], 0, 0, 0);
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, v, o[nb], 0, 0, 0);
+                }
+                __syncthreads();
+            }
+        }
+        // the partial of (slot, head group)
+        const int64_t head0 = slot * a.q_heads + (int64_t)hg * kHeads;
+        if (seg_bad) {
+            atomicOr(a.flags, UKV_FLAG_BAD_BLOCK);
+            if (lane < kHeads) a.part_ml[(head0 + lane) * 2 + 1] = -1.0f;
+        } else {
+            l_run += __shfl_xor(l_run, 16);
+            l_run += __shfl_xor(l_run, 32);
+            // o[nb][i]: head 4 grp + i, dim 16 nb + col
+            float *po = a.part_o + head0 * kValue + col;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[nb][i] *= al[i];
+                for (int i = 0; i < 4; ++i) po[(4 * grp + i) * kValue + 16 * nb] = o[nb][i];
+            if (lane < kHeads) {
+                a.part_ml[(head0 + lane) * 2] = m_run;
+                a.part_ml[(head0 + lane) * 2 + 1] = l_run;
+            }
         }
-        // weights as two bf16 parts; K slots 8 grp + i <- tile 2t, 8 grp + 4 + i <- tile 2t+1
-        bf16x8 whi, wlo;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float pa = exp2f(xa[i] - m_run);
-            const float pb = exp2f(xb[i] - m_run);
-            l_run += pa + pb;
-            const __bf16 ha = (__bf16)pa, hb = (__bf16)pb;
-            whi[i] = ha;
-            whi[4 + i] = hb;
-            wlo[i] = (__bf16)(pa - (float)ha);
-            wlo[4 + i] = (__bf16)(pb - (float)hb);
-        }
-        __syncthreads();  // one wave per block: orders the LDS rows written above before the reads
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(lds + tr_off + 32 * nb));
-            const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(lds + kTile * kPitch + tr_off + 32 * nb));
-            const s16x4 vv[2] = {va, vb};
-            const bf16x8 v = __builtin_bit_cast(bf16x8, vv);
-            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, v, o[nb], 0, 0, 0);
-            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, v, o[nb], 0, 0, 0);
-        }
-        __syncthreads();  // the reads finish before the next pair overwrites the rows
+        cur += seg;
+        rbase += n;
+        ++r;
     }
-    {
-        // row sums over the four position groups
-        l_run += __shfl_xor(l_run, 16);
-        l_run += __shfl_xor(l_run, 32);
-        // o[nb][i]: head 4 grp + i, dim 16 nb + col
-        float *po = a.part_o + unit * kValue + col;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) po[(4 * grp + i) * kValue + 16 * nb] = o[nb][i];
-        if (lane < kHeads) {
-            a.part_ml[(unit + lane) * 2] = m_run;
-            a.part_ml[(unit + lane) * 2 + 1] = l_run;
-        }
-        return;
-    }
-bad_unit:
-    atomicOr(a.flags, UKV_FLAG_BAD_BLOCK);
-    if (lane < kHeads) a.part_ml[(unit + lane) * 2 + 1] = -1.0f;
 }
 
-// Merge the units of (request, head): out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
-// A bad unit, a request past max_seq_len (UKV_FLAG_LAYOUT) or an empty one
-// gives zeros.  One wave per (request, head); lane l sums dims l + 64 k.
+// Merge the slots of (request, head): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// over the slots w + r of the waves w whose spans meet the request.  A bad
+// slot, a request past max_seq_len (UKV_FLAG_LAYOUT) or an empty one gives
+// zeros.  One wave per (request, head); lane l sums dims l + 64 k.
 __global__ __launch_bounds__(kWave) void mla_attn_combine_kernel(MlaArgs a) {
     constexpr int E = kValue / kWave;
     const int lane = lane_id();
@@ -311,18 +375,19 @@ __global__ __launch_bounds__(kWave) void mla_attn_combine_kernel(MlaArgs a) {
     const int32_t h = (int32_t)(blockIdx.x - (uint32_t)r * a.q_heads);
     float *o = a.out + ((int64_t)r * a.q_heads + h) * kValue;
     const int32_t len = a.seq_lens[r];
-    int32_t chunks = 0;
-    if (len > a.max_seq_len) {
-        if (h == 0 && lane == 0) atomicOr(a.flags, UKV_FLAG_LAYOUT);
-    } else if (len > 0) {
-        const int32_t n = len - first_position(len, a.window);
-        chunks = (n + a.chunk - 1) / a.chunk;
+    if (len > a.max_seq_len && h == 0 && lane == 0) atomicOr(a.flags, UKV_FLAG_LAYOUT);
+    const int32_t n = attended(a, len);
+    int64_t w0 = 0, slots = 0;
+    if (n > 0) {
+        const int64_t c0 = a.cum[r], span = a.cum[a.num_reqs + 1];
+        w0 = c0 / span;
+        slots = (c0 + n - 1) / span - w0 + 1;
     }
-    const int64_t slot0 = (int64_t)r * a.max_chunks * a.q_heads + h;  // unit c of this head: slot0 + c * q_heads
+    auto head_of = [&](int64_t k) { return ((w0 + k + r) * a.q_heads + h); };  // slot w0 + k + r, head h
     float mx = -INFINITY, den = 0.0f;
     bool bad = false;
-    for (int c = lane; c < chunks; c += kWave) {
-        const float2 ml = *(const float2 *)(a.part_ml + (slot0 + (int64_t)c * a.q_heads) * 2);
+    for (int64_t k = lane; k < slots; k += kWave) {
+        const float2 ml = *(const float2 *)(a.part_ml + head_of(k) * 2);
         bad |= ml.y < 0.0f;
         if (ml.x > mx) {
             den = den * exp2f(mx - ml.x) + ml.y;
@@ -335,37 +400,37 @@ __global__ __launch_bounds__(kWave) void mla_attn_combine_kernel(MlaArgs a) {
     for (int sh = kWave / 2; sh >= 1; sh >>= 1) mh = fmaxf(mh, __shfl_xor(mh, sh));
     den = mx == -INFINITY ? 0.0f : den * exp2f(mx - mh);
     for (int sh = kWave / 2; sh >= 1; sh >>= 1) den += __shfl_xor(den, sh);
-    const bool ok = chunks > 0 && !__any(bad);
+    const bool ok = slots > 0 && !__any(bad);
     float acc[E];
 #pragma unroll
     for (int k = 0; k < E; ++k) acc[k] = 0.0f;
     if (ok) {
-        for (int c = 0; c < chunks; ++c) {
-            const int64_t slot = slot0 + (int64_t)c * a.q_heads;
-            const float w = exp2f(a.part_ml[slot * 2] - mh);
-            const float *po = a.part_o + slot * kValue;
+        for (int64_t k = 0; k < slots; ++k) {
+            const int64_t hs = head_of(k);
+            const float wgt = exp2f(a.part_ml[hs * 2] - mh);
+            const float *po = a.part_o + hs * kValue;
 #pragma unroll
-            for (int k = 0; k < E; ++k) acc[k] = fmaf(w, po[lane + kWave * k], acc[k]);
+            for (int e = 0; e < E; ++e) acc[e] = fmaf(wgt, po[lane + kWave * e], acc[e]);
         }
     }
 #pragma unroll
-    for (int k = 0; k < E; ++k) o[lane + kWave * k] = ok ? acc[k] / den : 0.0f;
+    for (int e = 0; e < E; ++e) o[lane + kWave * e] = ok ? acc[e] / den : 0.0f;
 }
 
-// Positions per unit: the largest of 1024, 768, 512, 384, 256, 128 that
-// still gives about kBusyWaves waves for the batch's bound.
-int32_t mla_chunk_for(int32_t num_reqs, int32_t groups, int32_t max_seq_len, int32_t window) {
+// Waves per head group (a multiple of 8): about one per SIMD over all groups,
+// fewer when the batch's bound would give spans under kMinSpan positions.
+int64_t mla_spans_for(int32_t num_reqs, int32_t groups, int32_t max_seq_len, int32_t window) {
     const int64_t n = (window > 0 && window < max_seq_len) ? window : max_seq_len;
-    int32_t chunk = kMaxChunk;
-    while (chunk > kMinChunk && (int64_t)num_reqs * groups * ((n + chunk - 1) / chunk) < kBusyWaves)
-        chunk = chunk > 512 ? chunk - 256 : chunk - 128;
-    return chunk;
+    const int64_t bound = (int64_t)num_reqs * (n > 0 ? n : 0);
+    if (bound <= 0) return 0;
+    int64_t w = kTargetWaves / groups;
+    const int64_t by_span = (bound + kMinSpan - 1) / kMinSpan;
+    w = w < by_span ? w : by_span;
+    w = w < 1 ? 1 : w;
+    return (w + kXcds - 1) / kXcds * kXcds;
 }
 
-int64_t mla_max_chunks_for(int32_t max_seq_len, int32_t window, int32_t chunk) {
-    const int64_t n = (window > 0 && window < max_seq_len) ? window : max_seq_len;
-    return n > 0 ? (n + chunk - 1) / chunk : 0;
-}
+uint64_t mla_header_bytes(int32_t num_reqs) { return ((uint64_t)(num_reqs + 2) * 8 + 15) / 16 * 16; }
 
 }  // namespace
 
@@ -377,9 +442,9 @@ uint64_t ukv_mla_decode_attention_workspace_bytes(const ukv_pool *pool, int32_t 
     if (pool == nullptr || sub < 0 || sub >= pool->plan.n_sub) return 0;
     if (num_reqs <= 0 || q_heads <= 0 || q_heads % kHeads != 0 || v_dim <= 0 || max_seq_len <= 0) return 0;
     if (window < 0) window = 0;
-    const int32_t chunk = mla_chunk_for(num_reqs, q_heads / kHeads, max_seq_len, window);
-    return (uint64_t)num_reqs * (uint64_t)mla_max_chunks_for(max_seq_len, window, chunk) * (uint64_t)q_heads *
-           ((uint64_t)v_dim + 2) * sizeof(float);
+    const int64_t spans = mla_spans_for(num_reqs, q_heads / kHeads, max_seq_len, window);
+    return mla_header_bytes(num_reqs) +
+           (uint64_t)(spans + num_reqs) * (uint64_t)q_heads * ((uint64_t)v_dim + 2) * sizeof(float);
 }
 
 int ukv_mla_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const void *q_dev, int32_t q_heads,
@@ -414,11 +479,10 @@ int ukv_mla_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, c
     if (((uintptr_t)pool->raw + vw.byte_offset) % 16 != 0)
         return fail(UKV_ERR_ALIGNMENT, "%s: the layer's view is not 16-byte aligned", who);
     const int32_t groups = q_heads / kHeads;
-    const int32_t chunk = mla_chunk_for(num_reqs, groups, max_seq_len, window);
-    const int64_t chunks = mla_max_chunks_for(max_seq_len, window, chunk);
+    const int64_t spans = mla_spans_for(num_reqs, groups, max_seq_len, window);
     const uint64_t need =
         ukv_mla_decode_attention_workspace_bytes(pool, sub, num_reqs, q_heads, v_dim, max_seq_len, window);
-    if (chunks > 0) {
+    if (spans > 0) {
         if (block_table_dev == nullptr || bt_stride < 1)
             return fail(UKV_ERR_INVALID_ARG, "%s: null block table or bt_stride < 1", who);
         if (workspace_dev == nullptr || workspace_bytes < need)
@@ -432,7 +496,7 @@ int ukv_mla_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, c
         ranges_overlap(out_dev, out_bytes, workspace_dev, need) ||
         ranges_overlap(out_dev, out_bytes, pool->raw, pool->raw_bytes))
         return fail(UKV_ERR_INVALID_ARG, "%s: output overlaps q, the workspace or the pool", who);
-    const int64_t grid = (int64_t)num_reqs * chunks * groups;  // one wave per block
+    const int64_t grid = spans * groups;  // one wave per block
     if (grid > kMaxGrid || (int64_t)num_reqs * q_heads > kMaxGrid)
         return fail(UKV_ERR_INVALID_ARG, "%s: batch too large for one launch", who);
     MlaArgs a;
@@ -452,17 +516,19 @@ int ukv_mla_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, c
     a.groups = groups;
     a.window = window;
     a.max_seq_len = max_seq_len;
-    a.max_chunks = (int32_t)chunks;
-    a.chunk = chunk;
+    a.spans = (int32_t)spans;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
     a.inv_bpp = 1.0 / (double)p.blocks_per_page;
-    float *ws = (float *)workspace_dev;
-    a.part_o = ws;
-    a.part_ml = ws == nullptr ? nullptr : ws + (uint64_t)num_reqs * chunks * q_heads * kValue;
+    if (workspace_dev != nullptr && spans > 0) {
+        uint8_t *ws = (uint8_t *)workspace_dev;
+        a.cum = (int64_t *)ws;
+        a.part_ml = (float *)(ws + mla_header_bytes(num_reqs));
+        a.part_o = a.part_ml + (uint64_t)(spans + num_reqs) * q_heads * 2;
+    }
     a.out = out_dev;
     a.flags = pool->flags_dev;
     if (grid > 0)
-        hipLaunchKernelGGL((mla_attn_chunk_kernel<kLatent / 32, kValue / 16>), dim3((unsigned)grid), dim3(kWave), 0,
+        hipLaunchKernelGGL((mla_attn_span_kernel<kLatent / 32, kValue / 16>), dim3((unsigned)grid), dim3(kWave), 0,
                            stream, a);
     hipLaunchKernelGGL(mla_attn_combine_kernel, dim3((unsigned)(num_reqs * q_heads)), dim3(kWave), 0, stream, a);
     return check_launch(who);

@@ -23,13 +23,26 @@ from test_gpu_attention import GaussPair, requests
 pytestmark = pytest.mark.gpu
 
 LAT, VD = 576, 512
-MAX_CHUNK, MIN_CHUNK = 1024, 128  # positions per split-K unit of the kernel, by batch size
+TARGET_WAVES, MIN_SPAN = 1024, 256  # the kernel's split: waves over all head groups, positions per wave
 
 
-def bound_terms(max_len):
-    """The kernel's longest fp32 sum chain: a unit's products (two bf16 parts per weight),
-    two lane reductions of the row sums, the merge over units and the division."""
-    return 2 * MAX_CHUNK + 2 + (max_len + MIN_CHUNK - 1) // MIN_CHUNK + 2
+def span_of(lens, hq, max_len, window):
+    """Positions per wave of the kernel's balanced split for this batch."""
+    lens = np.asarray(lens, dtype=np.int64)
+    n_max = window if 0 < window < max_len else max_len
+    spans = min(TARGET_WAVES // (hq // 16), -(-len(lens) * n_max // MIN_SPAN))
+    spans = -(-max(spans, 1) // 8) * 8
+    ok = (lens > 0) & (lens <= max_len)
+    att = np.where(ok, np.minimum(lens, window) if window > 0 else lens, 0)
+    return max(-(-int(att.sum()) // spans), MIN_SPAN), int(att.max(initial=0))
+
+
+def bound_terms(lens, hq, max_len, window=0):
+    """The kernel's longest fp32 sum chain: a wave's products over its span (two bf16
+    parts per weight), two lane reductions of the row sums, the merge of the slots of
+    the longest request, and the division."""
+    span, longest = span_of(lens, hq, max_len, window)
+    return 2 * span + 2 + (longest + span - 1) // span + 2 + 2
 
 
 @pytest.fixture(autouse=True)
@@ -58,8 +71,8 @@ def run_mla(pair, layer, q_bits, bt, lens, window, scale, max_len, sub=0, worksp
 
 def oracle_mla(pair, layer, q_bits, bt, lens, window, scale, max_len, sub=0, requests=None):
     return A.decode_attention(pair.orc, sub, layer, q_bits, bt, lens, window, scale, max_len, read=pair.read,
-                              requests=requests, bound_terms=bound_terms(max_len), v_dim=VD,
-                              weight_rel=A.BF16_SPLIT_REL)
+                              requests=requests, bound_terms=bound_terms(lens, q_bits.shape[1], max_len, window),
+                              v_dim=VD, weight_rel=A.BF16_SPLIT_REL)
 
 
 def check_close(got, exp, bound, what):
@@ -95,17 +108,19 @@ def test_mla_decode_attention_parity(hq, ps, window, sparse):
         assert np.isfinite(got).all()
 
 
-@pytest.mark.parametrize("num_reqs,hq,len_hi,window", [(512, 16, 8192, 0), (512, 16, 7000, 0), (256, 16, 9000, 0),
-                                                       (256, 16, 7000, 0), (96, 32, 8000, 0), (16, 16, 3000, 0),
-                                                       (8, 48, 2000, 700)])
-def test_mla_decode_attention_unit_sizes(num_reqs, hq, len_hi, window):
-    """Batches whose size makes the kernel pick 1024-, 768-, 512-, 384-, 256- and
-    128-position units (the last two with 128); sampled requests checked (shared pages
-    keep the pool small)."""
+@pytest.mark.parametrize("num_reqs,hq,len_hi,window", [(512, 16, 8192, 0), (1, 16, 60000, 0), (300, 16, 40, 0),
+                                                       (96, 32, 8000, 0), (8, 48, 2000, 700), (130, 16, 3000, 0)])
+def test_mla_decode_attention_span_shapes(num_reqs, hq, len_hi, window):
+    """Batches that cut the balanced split differently: ~2,000-position spans over 512
+    requests, one request merged from 235 waves, waves that cross a dozen tiny
+    requests, two and three head groups (one with a window), and empty requests among
+    the rest; sampled requests checked (shared pages keep the pool small)."""
     ps = 64
     g = np.random.default_rng(num_reqs + len_hi)
     lens = g.integers(1, len_hi, size=num_reqs, endpoint=True).astype(np.int32)
     lens[0] = len_hi
+    if num_reqs == 130:
+        lens[g.choice(num_reqs - 1, 30, replace=False) + 1] = 0
     P = 700
     pair = GaussPair([W.mla(1, P)], ps, seed=num_reqs)
     pages = requests(4, P, ps, lens, share=True)
@@ -113,8 +128,9 @@ def test_mla_decode_attention_unit_sizes(num_reqs, hq, len_hi, window):
     q = queries(num_reqs, num_reqs, hq)
     scale = A.default_scale(192)
     got, gf = run_mla(pair, 0, q, bt, lens, window, scale, len_hi)
-    sample = sorted({0, 1, num_reqs // 2, num_reqs - 1, int(np.argmin(lens))})
+    sample = sorted({0, min(1, num_reqs - 1), num_reqs // 2, num_reqs - 1, int(np.argmin(lens))})
     exp, ef, bound = oracle_mla(pair, 0, q, bt, lens, window, scale, len_hi, requests=sample)
+    assert np.array_equal(got[lens == 0], np.zeros_like(got[lens == 0]))
     assert gf == ef == frozenset()
     check_close(got[sample], exp[sample], bound[sample], f"{num_reqs} requests up to {len_hi}")
     assert np.isfinite(got).all()
