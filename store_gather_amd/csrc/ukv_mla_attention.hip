@@ -51,6 +51,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <type_traits>
 
 #include "ukv_internal.h"
 
@@ -68,7 +69,7 @@ constexpr int kHeads = 16;               // query heads per wave (the MFMA width
 constexpr int64_t kTargetWaves = 1024;   // one per SIMD of MI355X (256 CUs x 4) at this kernel's occupancy
 constexpr int64_t kMinSpan = 256;        // positions per wave, at least (a partial is 32 KiB)
 constexpr int kXcds = 8;                 // workgroups go round-robin over the 8 XCDs
-constexpr float kRescaleGap = 8.0f;
+constexpr float kGrowGap = 64.0f;       // log2 headroom of the weights over their reference
 constexpr int kLatent = 576;             // supported latent width (elements)
 constexpr int kValue = 512;              // supported value width (elements)
 
@@ -136,14 +137,17 @@ __device__ __forceinline__ bool multiple_of(int32_t e, int32_t bpp, double inv_b
 }
 
 // Row pitch of the LDS value tiles: 512 bf16 plus 32 bytes, so that the
-// sixteen rows one transposing read touches spread over the banks.
+// sixteen rows one transposing read touches spread over the banks; the
+// queries' rows (576 bf16) get 16 bytes for the same reason.
 constexpr int kPitch = kValue * 2 + 32;
+constexpr int kQPitch = kLatent * 2 + 16;
 
 template <int KS, int NB>
 __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
     static_assert(KS * 32 == kLatent && NB * 16 == kValue, "latent / value width");
     constexpr int VS = NB / 2;  // 16-byte chunks of a lane's row slice that hold values (dims < 512)
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTile * kPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kTile * kPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kHeads * kQPitch];
 
     const int lane = lane_id();
     const int grp = lane >> 4;
@@ -193,9 +197,9 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
         carry += __shfl(incl, kWave - 1);
     }
 
-    // queries as the B operand: column col is head hg*16 + col, lane group grp
-    // holds dims [8 (4 s + grp), +8) at k-step s (loaded per request)
-    bf16x8 qb[KS];
+    // queries as the B operand, from LDS: column col is head hg*16 + col, lane
+    // group grp reads dims [8 (4 s + grp), +8) at k-step s
+    const uint8_t *qsrc = qlds + col * kQPitch + 16 * grp;
     const uint8_t *view = a.pool + a.base;
     const uint32_t ps = a.ps;
     const uint32_t q16 = (uint32_t)kTile / ps, r16 = (uint32_t)kTile - q16 * ps;
@@ -205,7 +209,6 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
     // positions 4 grp .. 4 grp + 3
     const int tr_off = (4 * grp + col / 4) * kPitch + 8 * (col % 4);
 
-    f32x4 o[NB];
     u32x4 k0[KS], k1[KS];
     int64_t cur = start;
     while (cur < end) {
@@ -222,123 +225,187 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
         const int32_t tiles = (pend - pbeg + kTile - 1) / kTile;
         const int64_t slot = (int64_t)w + r;
 
-        const uint16_t *qrow = a.q + ((int64_t)r * a.q_heads + hg * kHeads + col) * kLatent;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * s + grp)));
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        float m_run = -INFINITY;  // running max of head col, log2 units
+        {  // this request's 16 queries into LDS: 16 x 72 chunks of 16 bytes
+            const uint8_t *qg = (const uint8_t *)(a.q + ((int64_t)r * a.q_heads + hg * kHeads) * kLatent);
+            __syncthreads();  // the previous request's queries are no longer read
+            for (int c = lane; c < kHeads * (kLatent / 8); c += kWave) {
+                const int hq = c / (kLatent / 8), off = (c - hq * (kLatent / 8)) * 16;
+                *(u32x4 *)(qlds + hq * kQPitch + off) = load16(qg + (int64_t)hq * kLatent * 2 + off);
+            }
+            __syncthreads();
+        }
+        f32x4 o[NB];
+        float m_run = -INFINITY;  // the weights' reference (log2 units) of head col
         float l_run = 0.0f;       // row sum over this lane's positions
-
         // the lane's position in tile t is pbeg + 16 t + col; (table column,
-        // page offset) advance by 16 positions per tile without a division
+        // page offset) advance by 16 positions per tile without a division.
+        // Table entries are read two tiles ahead of their rows' loads, so that
+        // using one never waits behind a tile's loads (loads complete in order).
         const int32_t *bt_row = a.bt + (int64_t)r * a.bt_stride;
-        int32_t pj = pbeg + col;
-        uint32_t pcol = (uint32_t)pj / ps;
-        uint32_t poff = (uint32_t)pj - pcol * ps;
-        bool bad = false;
-        auto next_row = [&]() -> int32_t {
-            int32_t row = -1;
-            if (pj < pend) {
-                const int32_t e = (int64_t)pcol < a.bt_stride ? bt_row[pcol] : -1;
-                if (e < 0 || e >= entry_lim || !multiple_of(e, (int32_t)a.bpp, a.inv_bpp))
-                    bad = true;
-                else
-                    row = e * (int32_t)ps + (int32_t)poff;  // < n_rows < 2^31
-            }
-            pj += kTile;
-            pcol += q16;
-            poff += r16;
-            if (poff >= ps) {
-                poff -= ps;
-                ++pcol;
-            }
-            return row;
+        struct Pos {
+            int32_t j;
+            uint32_t col, off;
         };
+        auto advance = [&](Pos p) {
+            p.j += kTile;
+            p.col += q16;
+            p.off += r16;
+            if (p.off >= ps) {
+                p.off -= ps;
+                ++p.col;
+            }
+            return p;
+        };
+        // table entry of a position (a load), -1 past the table; nothing past the segment
+        auto entry = [&](const Pos &p) -> int32_t {
+            return (p.j < pend && (int64_t)p.col < a.bt_stride) ? bt_row[p.col] : -1;
+        };
+        bool bad = false;
+        auto row_of = [&](const Pos &p, int32_t e) -> int32_t {
+            if (p.j >= pend) return -1;
+            if (e < 0 || e >= entry_lim || !multiple_of(e, (int32_t)a.bpp, a.inv_bpp)) {
+                bad = true;
+                return -1;
+            }
+            return e * (int32_t)ps + (int32_t)p.off;  // < n_rows < 2^31
+        };
+        // the rows are loaded unconditionally (a position past the segment reads
+        // row 0); its scores are masked and its values zeroed in LDS
         auto load_tile = [&](u32x4 (&k)[KS], int32_t row) {
             const uint8_t *p = view + (uint64_t)(uint32_t)(row < 0 ? 0 : row) * a.row_bytes + 16 * grp;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) k[s] = row >= 0 ? load16(p + 64 * s) : u32x4{0, 0, 0, 0};
+            for (int s = 0; s < KS; ++s) k[s] = load16(p + 64 * s);
         };
         auto scores = [&](const u32x4 (&k)[KS]) {
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < KS; ++s)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[s]), qb[s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[s]),
+                                                              __builtin_bit_cast(bf16x8, load16(qsrc + 64 * s)), acc,
+                                                              0, 0, 0);
             return acc;
         };
-        auto stage = [&](const u32x4 (&k)[KS], int lrow) {
+        auto stage = [&](const u32x4 (&k)[KS], int lrow, bool valid) {
             uint8_t *st = lds + lrow * kPitch + 16 * grp;
+            if (valid) {
 #pragma unroll
-            for (int s = 0; s < VS; ++s) *(u32x4 *)(st + 64 * s) = k[s];
+                for (int s = 0; s < VS; ++s) *(u32x4 *)(st + 64 * s) = k[s];
+            } else {
+#pragma unroll
+                for (int s = 0; s < VS; ++s) *(u32x4 *)(st + 64 * s) = u32x4{0, 0, 0, 0};
+            }
         };
-        const int32_t pairs = (tiles + 1) / 2;
-        int32_t row = next_row();
-        bool seg_bad = __any(bad);
-        if (!seg_bad) {
-            load_tile(k0, row);
-            for (int32_t t = 0; t < pairs; ++t) {
-                row = next_row();
-                if (__any(bad)) { seg_bad = true; break; }
-                load_tile(k1, row);
-                const f32x4 sa = scores(k0);
-                stage(k0, col);
-                row = next_row();
-                if (__any(bad)) { seg_bad = true; break; }
-                if (t + 1 < pairs) load_tile(k0, row);
-                const f32x4 sb = scores(k1);
-                stage(k1, kTile + col);
-                const int32_t base_a = pbeg + 2 * t * kTile + 4 * grp;
-                float xa[4], xb[4];
+        // One pass over the segment, one tile at a time: tile t sits in k[t % 2];
+        // once it has been multiplied and its values staged, the rows of tile
+        // t + 2 go out into the same buffer, so two tiles are in flight during
+        // the value product.  Table entries are read two tiles ahead of their
+        // rows' loads.  The weights are 2^(x - ref) for a fixed reference ref,
+        // so the 16 x 512 sums are never rescaled (the sums stay in the matrix
+        // cores' accumulators):
+        //   MODE 0: ref = the first tile's max score; returns false (sums
+        //           unusable) as soon as a score exceeds ref + kGrowGap;
+        //   MODE 1: a given ref, at least every score (nothing to check);
+        //   MODE 2: no sums, ref becomes the segment's max score.
+        auto pass = [&](auto mode_tag) -> bool {
+            constexpr int MODE = decltype(mode_tag)::value;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            l_run = 0.0f;
+            Pos q0 = {pbeg + col, 0u, 0u};
+            q0.col = (uint32_t)q0.j / ps;
+            q0.off = (uint32_t)q0.j - q0.col * ps;
+            const int32_t e0 = entry(q0);
+            const Pos q1 = advance(q0);
+            const int32_t e1 = entry(q1);
+            Pos q2 = advance(q1);
+            int32_t e2 = entry(q2);
+            Pos q3 = advance(q2);
+            int32_t e3 = entry(q3);
+            const int32_t row0 = row_of(q0, e0), row1 = row_of(q1, e1);
+            if (__any(bad)) return true;
+            load_tile(k0, row0);
+            load_tile(k1, row1);
+            bool va = row0 >= 0, vb = row1 >= 0;
+            // scores of tile t -> weights, row sums and P V; false: the reference was outgrown
+            auto tile_math = [&](const f32x4 &sc, int32_t t) -> bool {
+                const int32_t p0 = pbeg + t * kTile + 4 * grp;
+                float x[4];
                 float tmax = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    xa[i] = base_a + i < pend ? sa[i] * a.scale_log2 : -INFINITY;
-                    xb[i] = base_a + kTile + i < pend ? sb[i] * a.scale_log2 : -INFINITY;
-                    tmax = fmaxf(tmax, fmaxf(xa[i], xb[i]));
+                    x[i] = p0 + i < pend ? sc[i] * a.scale_log2 : -INFINITY;
+                    tmax = fmaxf(tmax, x[i]);
                 }
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-                const bool need = tmax > m_run + kRescaleGap;
-                if (__any(need)) {
-                    const float alpha = need ? exp2f(m_run - tmax) : 1.0f;
-                    if (need) m_run = tmax;
-                    l_run *= alpha;
-                    float al[4];
+                if constexpr (MODE == 2) {
+                    m_run = fmaxf(m_run, tmax);
+                    return true;
+                } else {
+                    if constexpr (MODE == 0) {
+                        if (t == 0) m_run = tmax;
+                        if (__any(tmax > m_run + kGrowGap)) return false;
+                    }
+                    s16x4 whi, wlo;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * grp + i);
+                    for (int i = 0; i < 4; ++i) {
+                        const float pw = exp2f(x[i] - m_run);
+                        l_run += pw;
+                        const __bf16 h = (__bf16)pw;
+                        const __bf16 lo = (__bf16)(pw - (float)h);
+                        whi[i] = __builtin_bit_cast(short, h);
+                        wlo[i] = __builtin_bit_cast(short, lo);
+                    }
+                    __syncthreads();  // one wave per block: the staged rows are in LDS before the reads
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) o[nb][i] *= al[i];
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4 *)(lds + tr_off + 32 * nb));
+                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(whi, v, o[nb], 0, 0, 0);
+                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wlo, v, o[nb], 0, 0, 0);
+                    }
+                    __syncthreads();  // and read before the next tile's rows replace them
+                    return true;
                 }
-                bf16x8 whi, wlo;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float pa = exp2f(xa[i] - m_run);
-                    const float pb = exp2f(xb[i] - m_run);
-                    l_run += pa + pb;
-                    const __bf16 ha = (__bf16)pa, hb = (__bf16)pb;
-                    whi[i] = ha;
-                    whi[4 + i] = hb;
-                    wlo[i] = (__bf16)(pa - (float)ha);
-                    wlo[4 + i] = (__bf16)(pb - (float)hb);
-                }
-                __syncthreads();
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4 *)(lds + tr_off + 32 * nb));
-                    const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4 *)(lds + kTile * kPitch + tr_off + 32 * nb));
-                    const s16x4 vv[2] = {va, vb};
-                    const bf16x8 v = __builtin_bit_cast(bf16x8, vv);
-                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(whi, v, o[nb], 0, 0, 0);
-                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wlo, v, o[nb], 0, 0, 0);
-                }
-                __syncthreads();
+            };
+            for (int32_t t = 0; t < tiles; t += 2) {
+                // tile t (k0)
+                const Pos q4 = advance(q3);
+                const int32_t e4 = entry(q4);
+                const f32x4 sa = scores(k0);
+                if constexpr (MODE != 2) stage(k0, col, va);
+                const int32_t row2 = row_of(q2, e2);
+                if (__any(bad)) return true;
+                if (t + 2 < tiles) load_tile(k0, row2);
+                va = row2 >= 0;
+                if (!tile_math(sa, t)) return false;
+                if (t + 1 >= tiles) break;
+                // tile t + 1 (k1)
+                const Pos q5 = advance(q4);
+                const int32_t e5 = entry(q5);
+                const f32x4 sb = scores(k1);
+                if constexpr (MODE != 2) stage(k1, col, vb);
+                const int32_t row3 = row_of(q3, e3);
+                if (__any(bad)) return true;
+                if (t + 3 < tiles) load_tile(k1, row3);
+                vb = row3 >= 0;
+                if (!tile_math(sb, t + 1)) return false;
+                q2 = q4;
+                e2 = e4;
+                q3 = q5;
+                e3 = e5;
             }
+            return true;
+        };
+        bool seg_bad = false;
+        if (!pass(std::integral_constant<int, 0>())) {
+            // a score outgrew the first tile's by more than 2^kGrowGap: the
+            // segment's max first, then the sums against it
+            m_run = -INFINITY;
+            pass(std::integral_constant<int, 2>());
+            if (!__any(bad)) pass(std::integral_constant<int, 1>());
         }
+        seg_bad = __any(bad);
         // the partial of (slot, head group)
         const int64_t head0 = slot * a.q_heads + (int64_t)hg * kHeads;
         if (seg_bad) {

@@ -248,3 +248,37 @@ def test_mla_decode_attention_full_hybrid_sampled():
             check_close(got[sample], exp[sample], bound[sample], f"layer {layer}")
             assert np.isfinite(got).all()
     assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+
+
+@pytest.mark.parametrize("where", ["late", "first", "moderate"])
+def test_mla_decode_attention_dominant_scores(where):
+    """Scores far apart: one position's score exceeds the rest by ~1,000 (log2 units) late in
+    a request (past the first tile, so the weights' reference is outgrown and the kernel
+    takes its max-first pass), or in the first tile, or a later tile exceeds the first by
+    ~30 (weights up to 2^30 against the first tile's reference)."""
+    ps, hq = 16, 16
+    lens = np.array([700, 300, 45, 2000], dtype=np.int32)
+    P = int(sum((int(n) + ps - 1) // ps for n in lens)) + 4
+    pair = GaussPair([W.mla(2, P)], ps, seed=17)
+    pages = requests(9, P, ps, lens)
+    bt, _ = pair.orc.translate_pages(0, W.padded_table(pages))
+    q = queries(3, lens.size, hq)
+    dim = 540  # a rotary dim: the planted values change scores, not values
+    big = {"late": 100.0, "first": 100.0, "moderate": 24.0}[where]
+    q[:, :, dim] = np.float32(big).view(np.uint32) >> 16  # bf16 bits of an exact value
+    rb = pair.orc.row_bytes(0)
+    for r, n in enumerate(lens):
+        j = {"late": int(n) - 5, "first": 3, "moderate": int(n) // 2}[where]
+        kid = int(pages[r][j // ps]) * pair.orc.plan.subs[0].blocks_per_page * ps + j % ps
+        off = pair.orc.view_base(0, 1, 0) + kid * rb + 2 * dim
+        bits = np.array([np.float32(big).view(np.uint32) >> 16], dtype=np.uint16).view(np.uint8)
+        pair.orc.raw[off: off + 2] = bits
+        pair.gpu.raw[off: off + 2] = torch.from_numpy(bits.copy()).to("cuda")
+    scale = A.default_scale(192)
+    got, gf = run_mla(pair, 1, q, bt, lens, 0, scale, int(lens.max()))
+    exp, ef, bound = oracle_mla(pair, 1, q, bt, lens, 0, scale, int(lens.max()))
+    assert gf == ef == frozenset()
+    check_close(got, exp, bound, where)
+    assert np.isfinite(got).all()
+    if where != "moderate":  # one position takes (nearly) all the weight
+        assert np.abs(got - exp).max() < 1e-5
