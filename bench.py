@@ -448,7 +448,7 @@ def attention_mla_script(W, reduced: bool) -> Script:
               "attended_positions_per_layer": pos,
               "attention_flops_per_layer": int(2 * pos * hq * (lat + MLA_V_DIM))}
     return Script("decode_attn_mla", DESCRIPTIONS["decode_attn_mla"], [shape], ps, arrays, buffers, ops,
-                  lambda op: op.kind == "mla_attention", "mla_attn_chunk", counts, dtype="bf16")
+                  lambda op: op.kind == "mla_attention", "mla_attn_span", counts, dtype="bf16")
 
 
 def fuse_layers(s: Script, name: str, gathers: bool) -> Script:

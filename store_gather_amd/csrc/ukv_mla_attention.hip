@@ -31,22 +31,25 @@
 //    over 576): the latent rows are the A operand straight from HBM (lane l
 //    loads 16 bytes of position l % 16), the 16 heads' queries the B
 //    operand, so lane l ends with the scores of positions 4 (l / 16) + i for
-//    head l % 16.
-//  - the rows' first 512 elements also go to LDS (row-major), and P V runs
-//    on v_mfma_f32_16x16x32_bf16 over pairs of 16-position tiles: the K
-//    (position) order of the product is chosen so that a lane's eight
-//    weights are exactly its own scores of the two tiles (no exchange), and
-//    the value operand comes out of LDS through the gfx950 transposing read
-//    ds_read_b64_tr_b16, four positions of one dim per lane per read.
+//    head l % 16 -- exactly the A operand layout of v_mfma_f32_16x16x16_bf16,
+//    which then takes P V with no exchange between lanes.
+//  - the rows' first 512 elements also go to LDS (row-major), and the value
+//    operand comes out of LDS through the gfx950 transposing read
+//    ds_read_b64_tr_b16: four positions of one dim per lane per read.
 //  - each weight p enters the product as two bf16 parts, bf16(p) and
 //    bf16(p - bf16(p)), so the weights keep about 16 significant bits
 //    (relative error <= 2^-16), at twice the P V matrix work, which the
 //    matrix cores have to spare at this intensity.
-//  - base-2 online softmax with a lazy rescale (the running max moves only
-//    when a tile's max exceeds it by more than 8).
-//  - the next tile's latent rows are loaded while the current one is
-//    multiplied (two register buffers; one wave per SIMD holds the 16 x 512
-//    fp32 sums, the queries and the two tiles).
+//  - base-2 softmax against a fixed reference per segment (the first tile's
+//    max score): the 16 x 512 sums never need rescaling, so they live in
+//    the matrix cores' accumulator registers throughout.  A score that
+//    outgrows the reference by more than 2^64 sends the segment through a
+//    max-first pass instead (weights then never exceed 1).
+//  - two register buffers of latent rows: as soon as a tile has been
+//    multiplied and its values staged, the rows of the tile two ahead go out
+//    into its buffer, so two tiles are in flight during the value product;
+//    block-table entries are read two tiles ahead of their rows.  One wave
+//    per SIMD holds the sums, the queries and the two tiles.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -136,18 +139,15 @@ __device__ __forceinline__ bool multiple_of(int32_t e, int32_t bpp, double inv_b
     return r == 0;
 }
 
-// Row pitch of the LDS value tiles: 512 bf16 plus 32 bytes, so that the
-// sixteen rows one transposing read touches spread over the banks; the
-// queries' rows (576 bf16) get 16 bytes for the same reason.
+// Row pitch of the LDS value tile: 512 bf16 plus 32 bytes, so that the
+// sixteen rows one transposing read touches spread over the banks.
 constexpr int kPitch = kValue * 2 + 32;
-constexpr int kQPitch = kLatent * 2 + 16;
 
 template <int KS, int NB>
 __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
     static_assert(KS * 32 == kLatent && NB * 16 == kValue, "latent / value width");
     constexpr int VS = NB / 2;  // 16-byte chunks of a lane's row slice that hold values (dims < 512)
     __shared__ __attribute__((aligned(16))) uint8_t lds[kTile * kPitch];
-    __shared__ __attribute__((aligned(16))) uint8_t qlds[kHeads * kQPitch];
 
     const int lane = lane_id();
     const int grp = lane >> 4;
@@ -197,9 +197,9 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
         carry += __shfl(incl, kWave - 1);
     }
 
-    // queries as the B operand, from LDS: column col is head hg*16 + col, lane
-    // group grp reads dims [8 (4 s + grp), +8) at k-step s
-    const uint8_t *qsrc = qlds + col * kQPitch + 16 * grp;
+    // queries as the B operand: column col is head hg*16 + col, lane group grp
+    // holds dims [8 (4 s + grp), +8) at k-step s (loaded per request)
+    bf16x8 qb[KS];
     const uint8_t *view = a.pool + a.base;
     const uint32_t ps = a.ps;
     const uint32_t q16 = (uint32_t)kTile / ps, r16 = (uint32_t)kTile - q16 * ps;
@@ -225,14 +225,10 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
         const int32_t tiles = (pend - pbeg + kTile - 1) / kTile;
         const int64_t slot = (int64_t)w + r;
 
-        {  // this request's 16 queries into LDS: 16 x 72 chunks of 16 bytes
-            const uint8_t *qg = (const uint8_t *)(a.q + ((int64_t)r * a.q_heads + hg * kHeads) * kLatent);
-            __syncthreads();  // the previous request's queries are no longer read
-            for (int c = lane; c < kHeads * (kLatent / 8); c += kWave) {
-                const int hq = c / (kLatent / 8), off = (c - hq * (kLatent / 8)) * 16;
-                *(u32x4 *)(qlds + hq * kQPitch + off) = load16(qg + (int64_t)hq * kLatent * 2 + off);
-            }
-            __syncthreads();
+        {
+            const uint16_t *qrow = a.q + ((int64_t)r * a.q_heads + hg * kHeads + col) * kLatent;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * s + grp)));
         }
         f32x4 o[NB];
         float m_run = -INFINITY;  // the weights' reference (log2 units) of head col
@@ -281,8 +277,7 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
 #pragma unroll
             for (int s = 0; s < KS; ++s)
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[s]),
-                                                              __builtin_bit_cast(bf16x8, load16(qsrc + 64 * s)), acc,
-                                                              0, 0, 0);
+                                                              qb[s], acc, 0, 0, 0);
             return acc;
         };
         auto stage = [&](const u32x4 (&k)[KS], int lrow, bool valid) {
