@@ -16,14 +16,15 @@
 // bandwidth, so both products run on the matrix cores:
 //
 //  - balanced split-K: the batch's positions, request after request, form
-//    one sequence that is cut into equal spans, one per wave (about one wave
-//    per SIMD of the chip, so every wave streams the same number of bytes
-//    and none is left over for a second round).  A wave walks its span
-//    request by request and writes an unnormalised partial (running max, row
-//    sum, 16 x 512 sums) for each request it touches to slot (wave +
-//    request), which is unique; a second kernel merges each request's slots.
-//    Every wave finds its first request by a prefix sum over the lengths;
-//    the first wave also leaves the prefix sums for the merge.
+//    one sequence that is cut into equal spans, one per workgroup (1,024
+//    over all head groups: four per CU, so every workgroup streams the same
+//    number of bytes and none is left over for a second round).  A
+//    workgroup walks its span request by request and writes an unnormalised
+//    partial (max, row sum, 16 x 512 sums) for each request it touches to
+//    slot (span + request), which is unique; a second kernel merges each
+//    request's slots.  Every wave finds its first request by a prefix sum
+//    over the lengths; the first wave also leaves the prefix sums for the
+//    merge.
 //  - the query-head groups of one span sit on one XCD (blocks b with the
 //    same b % 8), so the latent rows they share are read once into that
 //    XCD's L2.
@@ -41,15 +42,21 @@
 //    (relative error <= 2^-16), at twice the P V matrix work, which the
 //    matrix cores have to spare at this intensity.
 //  - base-2 softmax against a fixed reference per segment (the first tile's
-//    max score): the 16 x 512 sums never need rescaling, so they live in
-//    the matrix cores' accumulator registers throughout.  A score that
+//    max score): the sums never need a vector rescale, which keeps the
+//    register pressure where the compiler does not spill.  A score that
 //    outgrows the reference by more than 2^64 sends the segment through a
 //    max-first pass instead (weights then never exceed 1).
-//  - two register buffers of latent rows: as soon as a tile has been
-//    multiplied and its values staged, the rows of the tile two ahead go out
-//    into its buffer, so two tiles are in flight during the value product;
-//    block-table entries are read two tiles ahead of their rows.  One wave
-//    per SIMD holds the sums, the queries and the two tiles.
+//  - two waves per workgroup split each row: wave h loads the chunks of
+//    its 256 value dims and 32 of the rotary dims, computes the partial
+//    scores over them, and the two add each other's partials through LDS
+//    (the same sum, bit for bit, in both), then each multiplies the weights
+//    into its own 256 value dims.  Per wave: 16 x 256 fp32 sums and two
+//    9-chunk row buffers, ~250 registers, so two waves per SIMD; the
+//    queries sit in LDS once for both.
+//  - as soon as a tile has been multiplied and staged, the rows of the tile
+//    two ahead go out into its buffer, so two tiles are in flight during the
+//    value product; block-table entries are read two tiles ahead of their
+//    rows.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -69,7 +76,8 @@ constexpr int kWave = 64;
 constexpr int64_t kMaxGrid = 0x7fffffff;
 constexpr int kTile = 16;                // positions per tile
 constexpr int kHeads = 16;               // query heads per wave (the MFMA width)
-constexpr int64_t kTargetWaves = 1024;   // one per SIMD of MI355X (256 CUs x 4) at this kernel's occupancy
+constexpr int kWavesPerCu = 8;          // the span kernel's occupancy: two waves per SIMD
+constexpr int64_t kTargetGroups = 1024;  // two-wave workgroups: 4 per CU x 256 CUs, one round
 constexpr int64_t kMinSpan = 256;        // positions per wave, at least (a partial is 32 KiB)
 constexpr int kXcds = 8;                 // workgroups go round-robin over the 8 XCDs
 constexpr float kGrowGap = 64.0f;       // log2 headroom of the weights over their reference
@@ -140,25 +148,40 @@ __device__ __forceinline__ bool multiple_of(int32_t e, int32_t bpp, double inv_b
 }
 
 // Row pitch of the LDS value tile: 512 bf16 plus 32 bytes, so that the
-// sixteen rows one transposing read touches spread over the banks.
+// sixteen rows one transposing read touches spread over the banks; the
+// queries' rows (576 bf16) get 16 bytes for the same reason.
 constexpr int kPitch = kValue * 2 + 32;
+constexpr int kQPitch = kLatent * 2 + 16;
 
+// A workgroup of two waves owns (span, head group).  Wave `half` loads the
+// row chunks s = 8 half .. 8 half + 7 (its 256 value dims) and s = 16 + half
+// (its 32 rotary dims) of every row, computes the partial scores over those
+// 288 dims, and the two waves add each other's partials through LDS; both
+// then hold the same scores and take the same softmax decisions, and each
+// multiplies the weights into its own 256 value dims.  Per wave: 16 x 256
+// fp32 sums (64 registers), 9 query chunks, two 9-chunk row buffers -- two
+// waves per SIMD.
 template <int KS, int NB>
-__global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
-    static_assert(KS * 32 == kLatent && NB * 16 == kValue, "latent / value width");
-    constexpr int VS = NB / 2;  // 16-byte chunks of a lane's row slice that hold values (dims < 512)
+__global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_attn_span_kernel(MlaArgs a) {
+    static_assert(KS * 32 == kLatent && NB * 16 == kValue && KS == NB / 2 + 2, "latent / value width");
+    constexpr int KH = KS / 2;      // row chunks per wave: 8 value chunks and 1 rotary chunk
+    constexpr int VH = NB / 2;      // 16-dim value blocks per wave
     __shared__ __attribute__((aligned(16))) uint8_t lds[kTile * kPitch];
-
+    __shared__ __attribute__((aligned(16))) f32x4 xch[2][2][kWave];  // partial scores by tile parity and wave
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kHeads * kQPitch];  // the request's 16 queries
+    const int half = (int)(threadIdx.x / kWave);
     const int lane = lane_id();
     const int grp = lane >> 4;
     const int col = lane & 15;
+    // the wave's row chunks: j < 8 -> value chunk 8 half + j, j = 8 -> rotary chunk 16 + half
+    auto chunk = [&](int j) { return j < KH - 1 ? (KH - 1) * half + j : 2 * (KH - 1) + half; };
 
     // block b -> (span w, head group hg), with every group of a span on XCD b % 8
     const int32_t b = (int32_t)blockIdx.x;
     const int32_t y = b / kXcds;
     const int32_t hg = y % a.groups;
     const int32_t w = (y / a.groups) * kXcds + (b - y * kXcds);
-    const bool writer = w == 0 && hg == 0;
+    const bool writer = w == 0 && hg == 0 && half == 0;
 
     // total attended positions N (the first wave records the prefix sums), then the span
     int64_t carry = 0;
@@ -177,7 +200,7 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
         a.cum[a.num_reqs + 1] = span;
     }
     const int64_t start = (int64_t)w * span;
-    if (start >= total) return;
+    if (start >= total) return;  // both waves of the workgroup leave together
     const int64_t end = start + span < total ? start + span : total;
     // the request holding position `start`, and its prefix sum
     int32_t r = -1;
@@ -197,19 +220,19 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
         carry += __shfl(incl, kWave - 1);
     }
 
-    // queries as the B operand: column col is head hg*16 + col, lane group grp
-    // holds dims [8 (4 s + grp), +8) at k-step s (loaded per request)
-    bf16x8 qb[KS];
+    // queries as the B operand, from LDS (one copy for both waves): column col
+    // is head hg*16 + col, lane group grp reads dims [8 (4 s + grp), +8) at k-step s
+    const uint8_t *qsrc = qlds + col * kQPitch + 16 * grp;
     const uint8_t *view = a.pool + a.base;
     const uint32_t ps = a.ps;
     const uint32_t q16 = (uint32_t)kTile / ps, r16 = (uint32_t)kTile - q16 * ps;
     const int32_t entry_lim = (int32_t)(a.num_pages * a.bpp);  // num_pages * bpp * ps < 2^31
     // transposing reads: lane (grp, col) points at position 4 grp + col / 4 of
     // the tile, dims 16 nb + 4 (col % 4) .. +3; it receives dim 16 nb + col of
-    // positions 4 grp .. 4 grp + 3
-    const int tr_off = (4 * grp + col / 4) * kPitch + 8 * (col % 4);
+    // positions 4 grp .. 4 grp + 3 (nb in this wave's blocks)
+    const int tr_off = (4 * grp + col / 4) * kPitch + 8 * (col % 4) + 32 * VH * half;
 
-    u32x4 k0[KS], k1[KS];
+    u32x4 k0[KH], k1[KH];
     int64_t cur = start;
     while (cur < end) {
         r = __builtin_amdgcn_readfirstlane(r);
@@ -224,19 +247,20 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
         const int32_t pend = pbeg + (int32_t)seg;
         const int32_t tiles = (pend - pbeg + kTile - 1) / kTile;
         const int64_t slot = (int64_t)w + r;
-
-        {
-            const uint16_t *qrow = a.q + ((int64_t)r * a.q_heads + hg * kHeads + col) * kLatent;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) qb[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qrow + 8 * (4 * s + grp)));
+        {  // this request's 16 queries into LDS: 16 x 72 chunks of 16 bytes over both waves
+            const uint8_t *qg = (const uint8_t *)(a.q + ((int64_t)r * a.q_heads + hg * kHeads) * kLatent);
+            __syncthreads();  // the previous request's queries are no longer read
+            for (int c = (int)threadIdx.x; c < kHeads * (kLatent / 8); c += 2 * kWave) {
+                const int hq = c / (kLatent / 8), off = (c - hq * (kLatent / 8)) * 16;
+                *(u32x4 *)(qlds + hq * kQPitch + off) = load16(qg + (int64_t)hq * kLatent * 2 + off);
+            }
+            __syncthreads();
         }
-        f32x4 o[NB];
+        f32x4 o[VH];
         float m_run = -INFINITY;  // the weights' reference (log2 units) of head col
         float l_run = 0.0f;       // row sum over this lane's positions
         // the lane's position in tile t is pbeg + 16 t + col; (table column,
         // page offset) advance by 16 positions per tile without a division.
-        // Table entries are read two tiles ahead of their rows' loads, so that
-        // using one never waits behind a tile's loads (loads complete in order).
         const int32_t *bt_row = a.bt + (int64_t)r * a.bt_stride;
         struct Pos {
             int32_t j;
@@ -265,29 +289,35 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
             }
             return e * (int32_t)ps + (int32_t)p.off;  // < n_rows < 2^31
         };
-        // the rows are loaded unconditionally (a position past the segment reads
-        // row 0); its scores are masked and its values zeroed in LDS
-        auto load_tile = [&](u32x4 (&k)[KS], int32_t row) {
+        // the wave's chunks of a tile's rows, loaded unconditionally (a position
+        // past the segment reads row 0; its scores are masked and its values
+        // zeroed in LDS)
+        auto load_tile = [&](u32x4 (&k)[KH], int32_t row) {
             const uint8_t *p = view + (uint64_t)(uint32_t)(row < 0 ? 0 : row) * a.row_bytes + 16 * grp;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) k[s] = load16(p + 64 * s);
+            for (int j = 0; j < KH; ++j) k[j] = load16(p + 64 * chunk(j));
         };
-        auto scores = [&](const u32x4 (&k)[KS]) {
+        // this wave's partial scores, then the other wave's added (through LDS, by tile parity)
+        auto scores = [&](const u32x4 (&k)[KH], int32_t t) {
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[s]),
-                                                              qb[s], acc, 0, 0, 0);
-            return acc;
+            for (int j = 0; j < KH; ++j)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, k[j]), __builtin_bit_cast(bf16x8, load16(qsrc + 64 * chunk(j))), acc, 0,
+                    0, 0);
+            xch[t & 1][half][lane] = acc;
+            __syncthreads();
+            const f32x4 other = xch[t & 1][1 - half][lane];
+            return half == 0 ? acc + other : other + acc;  // the same sum, bit for bit, in both waves
         };
-        auto stage = [&](const u32x4 (&k)[KS], int lrow, bool valid) {
-            uint8_t *st = lds + lrow * kPitch + 16 * grp;
+        auto stage = [&](const u32x4 (&k)[KH], bool valid) {
+            uint8_t *st = lds + col * kPitch + 16 * grp + 512 * half;
             if (valid) {
 #pragma unroll
-                for (int s = 0; s < VS; ++s) *(u32x4 *)(st + 64 * s) = k[s];
+                for (int j = 0; j < KH - 1; ++j) *(u32x4 *)(st + 64 * j) = k[j];
             } else {
 #pragma unroll
-                for (int s = 0; s < VS; ++s) *(u32x4 *)(st + 64 * s) = u32x4{0, 0, 0, 0};
+                for (int j = 0; j < KH - 1; ++j) *(u32x4 *)(st + 64 * j) = u32x4{0, 0, 0, 0};
             }
         };
         // One pass over the segment, one tile at a time: tile t sits in k[t % 2];
@@ -295,16 +325,19 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
         // t + 2 go out into the same buffer, so two tiles are in flight during
         // the value product.  Table entries are read two tiles ahead of their
         // rows' loads.  The weights are 2^(x - ref) for a fixed reference ref,
-        // so the 16 x 512 sums are never rescaled (the sums stay in the matrix
-        // cores' accumulators):
+        // so the sums are never rescaled (they stay in the matrix cores'
+        // accumulators):
         //   MODE 0: ref = the first tile's max score; returns false (sums
         //           unusable) as soon as a score exceeds ref + kGrowGap;
         //   MODE 1: a given ref, at least every score (nothing to check);
         //   MODE 2: no sums, ref becomes the segment's max score.
+        // Both waves see the same scores, so they take every branch together.
         auto pass = [&](auto mode_tag) -> bool {
             constexpr int MODE = decltype(mode_tag)::value;
+            // the score exchange restarts at tile 0: the other wave has read the last one
+            __syncthreads();
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int nb = 0; nb < VH; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             l_run = 0.0f;
             Pos q0 = {pbeg + col, 0u, 0u};
             q0.col = (uint32_t)q0.j / ps;
@@ -351,15 +384,16 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
                         whi[i] = __builtin_bit_cast(short, h);
                         wlo[i] = __builtin_bit_cast(short, lo);
                     }
-                    __syncthreads();  // one wave per block: the staged rows are in LDS before the reads
+                    // the wave reads only the value half it staged itself: LDS runs a
+                    // wave's operations in order, and the compiler may not move the reads
+                    // above the writes of the same array
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
+                    for (int nb = 0; nb < VH; ++nb) {
                         const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (__attribute__((address_space(3))) s16x4 *)(lds + tr_off + 32 * nb));
                         o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(whi, v, o[nb], 0, 0, 0);
                         o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wlo, v, o[nb], 0, 0, 0);
                     }
-                    __syncthreads();  // and read before the next tile's rows replace them
                     return true;
                 }
             };
@@ -367,8 +401,8 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
                 // tile t (k0)
                 const Pos q4 = advance(q3);
                 const int32_t e4 = entry(q4);
-                const f32x4 sa = scores(k0);
-                if constexpr (MODE != 2) stage(k0, col, va);
+                if constexpr (MODE != 2) stage(k0, va);
+                const f32x4 sa = scores(k0, t);
                 const int32_t row2 = row_of(q2, e2);
                 if (__any(bad)) return true;
                 if (t + 2 < tiles) load_tile(k0, row2);
@@ -378,8 +412,8 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
                 // tile t + 1 (k1)
                 const Pos q5 = advance(q4);
                 const int32_t e5 = entry(q5);
-                const f32x4 sb = scores(k1);
-                if constexpr (MODE != 2) stage(k1, col, vb);
+                if constexpr (MODE != 2) stage(k1, vb);
+                const f32x4 sb = scores(k1, t + 1);
                 const int32_t row3 = row_of(q3, e3);
                 if (__any(bad)) return true;
                 if (t + 3 < tiles) load_tile(k1, row3);
@@ -392,7 +426,6 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
             }
             return true;
         };
-        bool seg_bad = false;
         if (!pass(std::integral_constant<int, 0>())) {
             // a score outgrew the first tile's by more than 2^kGrowGap: the
             // segment's max first, then the sums against it
@@ -400,22 +433,24 @@ __global__ __launch_bounds__(kWave) void mla_attn_span_kernel(MlaArgs a) {
             pass(std::integral_constant<int, 2>());
             if (!__any(bad)) pass(std::integral_constant<int, 1>());
         }
-        seg_bad = __any(bad);
-        // the partial of (slot, head group)
+        const bool seg_bad = __any(bad);
+        // the partial of (slot, head group): this wave's value half
         const int64_t head0 = slot * a.q_heads + (int64_t)hg * kHeads;
         if (seg_bad) {
-            atomicOr(a.flags, UKV_FLAG_BAD_BLOCK);
-            if (lane < kHeads) a.part_ml[(head0 + lane) * 2 + 1] = -1.0f;
+            if (half == 0) {
+                atomicOr(a.flags, UKV_FLAG_BAD_BLOCK);
+                if (lane < kHeads) a.part_ml[(head0 + lane) * 2 + 1] = -1.0f;
+            }
         } else {
             l_run += __shfl_xor(l_run, 16);
             l_run += __shfl_xor(l_run, 32);
-            // o[nb][i]: head 4 grp + i, dim 16 nb + col
-            float *po = a.part_o + head0 * kValue + col;
+            // o[nb][i]: head 4 grp + i, dim 256 half + 16 nb + col
+            float *po = a.part_o + head0 * kValue + (kValue / 2) * half + col;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int nb = 0; nb < VH; ++nb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) po[(4 * grp + i) * kValue + 16 * nb] = o[nb][i];
-            if (lane < kHeads) {
+            if (half == 0 && lane < kHeads) {
                 a.part_ml[(head0 + lane) * 2] = m_run;
                 a.part_ml[(head0 + lane) * 2 + 1] = l_run;
             }
@@ -485,7 +520,7 @@ int64_t mla_spans_for(int32_t num_reqs, int32_t groups, int32_t max_seq_len, int
     const int64_t n = (window > 0 && window < max_seq_len) ? window : max_seq_len;
     const int64_t bound = (int64_t)num_reqs * (n > 0 ? n : 0);
     if (bound <= 0) return 0;
-    int64_t w = kTargetWaves / groups;
+    int64_t w = kTargetGroups / groups;
     const int64_t by_span = (bound + kMinSpan - 1) / kMinSpan;
     w = w < by_span ? w : by_span;
     w = w < 1 ? 1 : w;
@@ -558,7 +593,7 @@ int ukv_mla_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, c
         ranges_overlap(out_dev, out_bytes, workspace_dev, need) ||
         ranges_overlap(out_dev, out_bytes, pool->raw, pool->raw_bytes))
         return fail(UKV_ERR_INVALID_ARG, "%s: output overlaps q, the workspace or the pool", who);
-    const int64_t grid = spans * groups;  // one wave per block
+    const int64_t grid = spans * groups;  // two waves per block
     if (grid > kMaxGrid || (int64_t)num_reqs * q_heads > kMaxGrid)
         return fail(UKV_ERR_INVALID_ARG, "%s: batch too large for one launch", who);
     MlaArgs a;
@@ -590,7 +625,7 @@ int ukv_mla_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, c
     a.out = out_dev;
     a.flags = pool->flags_dev;
     if (grid > 0)
-        hipLaunchKernelGGL((mla_attn_span_kernel<kLatent / 32, kValue / 16>), dim3((unsigned)grid), dim3(kWave), 0,
+        hipLaunchKernelGGL((mla_attn_span_kernel<kLatent / 32, kValue / 16>), dim3((unsigned)grid), dim3(2 * kWave), 0,
                            stream, a);
     hipLaunchKernelGGL(mla_attn_combine_kernel, dim3((unsigned)(num_reqs * q_heads)), dim3(kWave), 0, stream, a);
     return check_launch(who);
