@@ -32,15 +32,16 @@
 //    over 576): the latent rows are the A operand straight from HBM (lane l
 //    loads 16 bytes of position l % 16), the 16 heads' queries the B
 //    operand, so lane l ends with the scores of positions 4 (l / 16) + i for
-//    head l % 16 -- exactly the A operand layout of v_mfma_f32_16x16x16_bf16,
-//    which then takes P V with no exchange between lanes.
+//    head l % 16 -- the weights of those four positions are then already
+//    where the P V product wants them, with no exchange between lanes.
 //  - the rows' first 512 elements also go to LDS (row-major), and the value
 //    operand comes out of LDS through the gfx950 transposing read
 //    ds_read_b64_tr_b16: four positions of one dim per lane per read.
 //  - each weight p enters the product as two bf16 parts, bf16(p) and
 //    bf16(p - bf16(p)), so the weights keep about 16 significant bits
-//    (relative error <= 2^-16), at twice the P V matrix work, which the
-//    matrix cores have to spare at this intensity.
+//    (relative error <= 2^-16): one K = 32 product per 16 value dims takes
+//    both parts of a lane's four positions, against the four transposed
+//    values twice (v_mfma_f32_16x16x32_bf16 again).
 //  - base-2 softmax against a fixed reference per segment (the first tile's
 //    max score): the sums never need a vector rescale, which keeps the
 //    register pressure where the compiler does not spill.  A score that
@@ -50,13 +51,12 @@
 //    its 256 value dims and 32 of the rotary dims, computes the partial
 //    scores over them, and the two add each other's partials through LDS
 //    (the same sum, bit for bit, in both), then each multiplies the weights
-//    into its own 256 value dims.  Per wave: 16 x 256 fp32 sums and two
-//    9-chunk row buffers, ~250 registers, so two waves per SIMD; the
-//    queries sit in LDS once for both.
-//  - as soon as a tile has been multiplied and staged, the rows of the tile
-//    two ahead go out into its buffer, so two tiles are in flight during the
-//    value product; block-table entries are read two tiles ahead of their
-//    rows.
+//    into its own 256 value dims.  Per wave: 16 x 256 fp32 sums and one
+//    9-chunk row buffer, ~200 registers, so two waves per SIMD; the queries
+//    sit in LDS once for both.
+//  - once a tile has been staged and its scores taken, the next tile's rows
+//    go out into the same registers and stay in flight during the value
+//    product; block-table entries are read a tile ahead of their rows.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -86,6 +86,7 @@ constexpr int kValue = 512;              // supported value width (elements)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -159,8 +160,8 @@ constexpr int kQPitch = kLatent * 2 + 16;
 // 288 dims, and the two waves add each other's partials through LDS; both
 // then hold the same scores and take the same softmax decisions, and each
 // multiplies the weights into its own 256 value dims.  Per wave: 16 x 256
-// fp32 sums (64 registers), 9 query chunks, two 9-chunk row buffers -- two
-// waves per SIMD.
+// fp32 sums (64 registers) and one 9-chunk row buffer -- two waves per
+// SIMD.
 template <int KS, int NB>
 __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_attn_span_kernel(MlaArgs a) {
     static_assert(KS * 32 == kLatent && NB * 16 == kValue && KS == NB / 2 + 2, "latent / value width");
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     // positions 4 grp .. 4 grp + 3 (nb in this wave's blocks)
     const int tr_off = (4 * grp + col / 4) * kPitch + 8 * (col % 4) + 32 * VH * half;
 
-    u32x4 k0[KH], k1[KH];
+    u32x4 k0[KH];
     int64_t cur = start;
     while (cur < end) {
         r = __builtin_amdgcn_readfirstlane(r);
@@ -310,21 +311,20 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
             const f32x4 other = xch[t & 1][1 - half][lane];
             return half == 0 ? acc + other : other + acc;  // the same sum, bit for bit, in both waves
         };
-        auto stage = [&](const u32x4 (&k)[KH], bool valid) {
+        auto stage = [&](const u32x4 (&k)[KH], bool valid, int32_t t) {
             uint8_t *st = lds + col * kPitch + 16 * grp + 512 * half;
-            if (valid) {
+            if (pbeg + (t + 1) * kTile <= pend) {  // every position of the tile is in the segment (uniform)
 #pragma unroll
                 for (int j = 0; j < KH - 1; ++j) *(u32x4 *)(st + 64 * j) = k[j];
-            } else {
+            } else {  // the segment's last tile: positions past its end stage zeros
 #pragma unroll
-                for (int j = 0; j < KH - 1; ++j) *(u32x4 *)(st + 64 * j) = u32x4{0, 0, 0, 0};
+                for (int j = 0; j < KH - 1; ++j) *(u32x4 *)(st + 64 * j) = valid ? k[j] : u32x4{0, 0, 0, 0};
             }
         };
-        // One pass over the segment, one tile at a time: tile t sits in k[t % 2];
-        // once it has been multiplied and its values staged, the rows of tile
-        // t + 2 go out into the same buffer, so two tiles are in flight during
-        // the value product.  Table entries are read two tiles ahead of their
-        // rows' loads.  The weights are 2^(x - ref) for a fixed reference ref,
+        // One pass over the segment, one tile at a time: once tile t has been
+        // staged and its scores taken, the rows of tile t + 1 go out into the
+        // same registers and stay in flight during the value product.  Table
+        // entries are read a tile ahead of their rows' loads.  The weights are 2^(x - ref) for a fixed reference ref,
         // so the sums are never rescaled (they stay in the matrix cores'
         // accumulators):
         //   MODE 0: ref = the first tile's max score; returns false (sums
@@ -343,17 +343,12 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
             q0.col = (uint32_t)q0.j / ps;
             q0.off = (uint32_t)q0.j - q0.col * ps;
             const int32_t e0 = entry(q0);
-            const Pos q1 = advance(q0);
-            const int32_t e1 = entry(q1);
-            Pos q2 = advance(q1);
-            int32_t e2 = entry(q2);
-            Pos q3 = advance(q2);
-            int32_t e3 = entry(q3);
-            const int32_t row0 = row_of(q0, e0), row1 = row_of(q1, e1);
+            Pos qn = advance(q0);
+            int32_t en = entry(qn);
+            const int32_t row0 = row_of(q0, e0);
             if (__any(bad)) return true;
             load_tile(k0, row0);
-            load_tile(k1, row1);
-            bool va = row0 >= 0, vb = row1 >= 0;
+            bool va = row0 >= 0;
             // scores of tile t -> weights, row sums and P V; false: the reference was outgrown
             auto tile_math = [&](const f32x4 &sc, int32_t t) -> bool {
                 const int32_t p0 = pbeg + t * kTile + 4 * grp;
@@ -384,45 +379,34 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
                         whi[i] = __builtin_bit_cast(short, h);
                         wlo[i] = __builtin_bit_cast(short, lo);
                     }
-                    // the wave reads only the value half it staged itself: LDS runs a
-                    // wave's operations in order, and the compiler may not move the reads
-                    // above the writes of the same array
+                    // one K = 32 product per block: k = 8 grp + i is position 4 grp + i % 4,
+                    // its high part for i < 4 and its low part for i >= 4, so the value
+                    // operand is the four transposed values twice.  The wave reads only
+                    // the value half it staged itself: LDS runs a wave's operations in
+                    // order, and the compiler may not move the reads above the writes of
+                    // the same array.
+                    const s16x8 w8 = __builtin_shufflevector(whi, wlo, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                     for (int nb = 0; nb < VH; ++nb) {
                         const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (__attribute__((address_space(3))) s16x4 *)(lds + tr_off + 32 * nb));
-                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(whi, v, o[nb], 0, 0, 0);
-                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wlo, v, o[nb], 0, 0, 0);
+                        const s16x8 v8 = __builtin_shufflevector(v, v, 0, 1, 2, 3, 0, 1, 2, 3);
+                        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w8),
+                                                                        __builtin_bit_cast(bf16x8, v8), o[nb], 0, 0, 0);
                     }
                     return true;
                 }
             };
-            for (int32_t t = 0; t < tiles; t += 2) {
-                // tile t (k0)
-                const Pos q4 = advance(q3);
-                const int32_t e4 = entry(q4);
-                if constexpr (MODE != 2) stage(k0, va);
+            for (int32_t t = 0; t < tiles; ++t) {
+                if constexpr (MODE != 2) stage(k0, va, t);
                 const f32x4 sa = scores(k0, t);
-                const int32_t row2 = row_of(q2, e2);
+                const int32_t rown = row_of(qn, en);
                 if (__any(bad)) return true;
-                if (t + 2 < tiles) load_tile(k0, row2);
-                va = row2 >= 0;
+                qn = advance(qn);
+                en = entry(qn);
+                if (t + 1 < tiles) load_tile(k0, rown);
+                va = rown >= 0;
                 if (!tile_math(sa, t)) return false;
-                if (t + 1 >= tiles) break;
-                // tile t + 1 (k1)
-                const Pos q5 = advance(q4);
-                const int32_t e5 = entry(q5);
-                if constexpr (MODE != 2) stage(k1, vb);
-                const f32x4 sb = scores(k1, t + 1);
-                const int32_t row3 = row_of(q3, e3);
-                if (__any(bad)) return true;
-                if (t + 3 < tiles) load_tile(k1, row3);
-                vb = row3 >= 0;
-                if (!tile_math(sb, t + 1)) return false;
-                q2 = q4;
-                e2 = e4;
-                q3 = q5;
-                e3 = e5;
             }
             return true;
         };
