@@ -729,9 +729,11 @@ def run_workload(name, args, torch, U, W, device) -> dict:
     step_bytes = sum(op.nbytes for op in script.ops)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     step_rows = sum(op_rows(op, script) for op in script.ops if not op.kind.startswith("translate"))
-    roof_ms = roof_bytes = achieved = None
+    roof_ms = roof_bytes = achieved = roof_med = roof_min = None
     if timed:
-        roof_ms = float(np.mean([e0.elapsed_time(e1) for _, e0, e1 in timed]))
+        roof_times = [e0.elapsed_time(e1) for _, e0, e1 in timed]
+        roof_ms = float(np.mean(roof_times))
+        roof_med, roof_min = float(np.median(roof_times)), float(np.min(roof_times))
         roof_bytes = float(np.mean([op.nbytes for op, _, _ in timed]))
         achieved = roof_bytes / (roof_ms * 1e-3) / 1e9
 
@@ -801,6 +803,8 @@ def run_workload(name, args, torch, U, W, device) -> dict:
             "traffic": traffic_from_profile(name, script.roofline_kernel),
             "algorithmic_bytes_per_launch": int(roof_bytes) if roof_bytes else None,
             "ms_per_launch": num(roof_ms, 5),
+            "ms_per_launch_median": num(roof_med, 5),
+            "ms_per_launch_min": num(roof_min, 5),
         },
         "ops": ops_out,
         "cpu_baseline": cpu,
