@@ -23,14 +23,14 @@ from test_gpu_attention import GaussPair, requests
 pytestmark = pytest.mark.gpu
 
 LAT, VD = 576, 512
-TARGET_WAVES, MIN_SPAN = 1024, 256  # the kernel's split: waves over all head groups, positions per wave
+TARGET_GROUPS, MIN_SPAN = 1024, 256  # the kernel's split: workgroups over all head groups, positions per span
 
 
 def span_of(lens, hq, max_len, window):
-    """Positions per wave of the kernel's balanced split for this batch."""
+    """Positions per span (one workgroup's share) of the kernel's balanced split for this batch."""
     lens = np.asarray(lens, dtype=np.int64)
     n_max = window if 0 < window < max_len else max_len
-    spans = min(TARGET_WAVES // (hq // 16), -(-len(lens) * n_max // MIN_SPAN))
+    spans = min(TARGET_GROUPS // (hq // 16), -(-len(lens) * n_max // MIN_SPAN))
     spans = -(-max(spans, 1) // 8) * 8
     ok = (lens > 0) & (lens <= max_len)
     att = np.where(ok, np.minimum(lens, window) if window > 0 else lens, 0)
@@ -112,7 +112,7 @@ def test_mla_decode_attention_parity(hq, ps, window, sparse):
                                                        (96, 32, 8000, 0), (8, 48, 2000, 700), (130, 16, 3000, 0)])
 def test_mla_decode_attention_span_shapes(num_reqs, hq, len_hi, window):
     """Batches that cut the balanced split differently: ~2,000-position spans over 512
-    requests, one request merged from 235 waves, waves that cross a dozen tiny
+    requests, one request merged from 235 spans, spans that cross a dozen tiny
     requests, two and three head groups (one with a window), and empty requests among
     the rest; sampled requests checked (shared pages keep the pool small)."""
     ps = 64
