@@ -17,13 +17,16 @@
 //
 //  - balanced split-K: the batch's positions, request after request, form
 //    one sequence that is cut into equal spans, one per workgroup (1,024
-//    over all head groups: four per CU, so every workgroup streams the same
-//    number of bytes and none is left over for a second round).  A
-//    workgroup walks its span request by request and writes an unnormalised
-//    partial (max, row sum, 16 x 512 sums) for each request it touches to
-//    slot (span + request), which is unique; a second kernel merges each
-//    request's slots.  Every wave finds its first request by a prefix sum
-//    over the lengths; the first wave also leaves the prefix sums for the
+//    over all head groups: four per CU, so every workgroup has the same work
+//    and none is left over for a second round).  The cut is by cost: each
+//    request costs its positions plus a fixed start-up share (its queries,
+//    the restart of the tile stream, its partial), so a span that takes a
+//    request boundary takes fewer positions.  A workgroup walks its span
+//    request by request and writes an unnormalised partial (max, row sum,
+//    16 x 512 sums) for each request it touches to slot (span + request),
+//    which is unique; a second kernel merges each request's slots.  Every
+//    wave finds its first request by a prefix sum over the costs; the first
+//    wave also leaves, per request, where its positions start, for the
 //    merge.
 //  - the query-head groups of one span sit on one XCD (blocks b with the
 //    same b % 8), so the latent rows they share are read once into that
@@ -79,6 +82,7 @@ constexpr int kHeads = 16;               // query heads per wave (the MFMA width
 constexpr int kWavesPerCu = 8;          // the span kernel's occupancy: two waves per SIMD
 constexpr int64_t kTargetGroups = 1024;  // two-wave workgroups: 4 per CU x 256 CUs, one round
 constexpr int64_t kMinSpan = 256;        // positions per wave, at least (a partial is 32 KiB)
+constexpr int64_t kSegCost = 128;        // a span's cost of starting a request, in positions' worth of time
 constexpr int kXcds = 8;                 // workgroups go round-robin over the 8 XCDs
 constexpr float kGrowGap = 64.0f;       // log2 headroom of the weights over their reference
 constexpr int kLatent = 576;             // supported latent width (elements)
@@ -109,7 +113,7 @@ struct MlaArgs {
     int32_t spans;     // waves per head group, a multiple of 8
     float scale_log2;  // softmax scale * log2(e)
     double inv_bpp;
-    int64_t *cum;    // [num_reqs + 2]: exclusive prefix sums of the attended lengths, their total, the span
+    int64_t *cum;    // [num_reqs + 2]: where each request's positions start in cost units, the total cost, the span
     float *part_o;   // [spans + num_reqs slots, q_heads, value]
     float *part_ml;  // [spans + num_reqs slots, q_heads, 2]: running max (log2 units), row sum; sum < 0: bad
     float *out;      // [num_reqs, q_heads, value]
@@ -184,13 +188,18 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int32_t w = (y / a.groups) * kXcds + (b - y * kXcds);
     const bool writer = w == 0 && hg == 0 && half == 0;
 
-    // total attended positions N (the first wave records the prefix sums), then the span
+    // The split runs in cost units: a request of n > 0 attended positions costs
+    // kSegCost + n (its positions come after the start-up share), so a span
+    // that takes a request boundary gets that many fewer positions.  Total
+    // cost T (the first wave records, per request, where its positions start
+    // in cost units), then the span.
     int64_t carry = 0;
     for (int32_t base = 0; base < a.num_reqs; base += kWave) {
         const int32_t r = base + lane;
         const int64_t n = r < a.num_reqs ? attended(a, a.seq_lens[r]) : 0;
-        const int64_t incl = wave_inclusive_scan(n, lane);
-        if (writer && r < a.num_reqs) a.cum[r] = carry + incl - n;
+        const int64_t c = n > 0 ? n + kSegCost : 0;
+        const int64_t incl = wave_inclusive_scan(c, lane);
+        if (writer && r < a.num_reqs) a.cum[r] = carry + incl - c + kSegCost;
         carry += __shfl(incl, kWave - 1);
     }
     const int64_t total = carry;
@@ -203,16 +212,17 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int64_t start = (int64_t)w * span;
     if (start >= total) return;  // both waves of the workgroup leave together
     const int64_t end = start + span < total ? start + span : total;
-    // the request holding position `start`, and its prefix sum
+    // the request whose cost interval holds `start`, and its cost base
     int32_t r = -1;
     int64_t rbase = 0;
     carry = 0;
     for (int32_t base = 0; base < a.num_reqs && r < 0; base += kWave) {
         const int32_t rr = base + lane;
         const int64_t n = rr < a.num_reqs ? attended(a, a.seq_lens[rr]) : 0;
-        const int64_t incl = wave_inclusive_scan(n, lane);
-        const int64_t excl = carry + incl - n;
-        const uint64_t hit = __ballot(n > 0 && excl <= start && start < excl + n);
+        const int64_t c = n > 0 ? n + kSegCost : 0;
+        const int64_t incl = wave_inclusive_scan(c, lane);
+        const int64_t excl = carry + incl - c;
+        const uint64_t hit = __ballot(c > 0 && excl <= start && start < excl + c);
         if (hit != 0) {
             const int l = __ffsll((unsigned long long)hit) - 1;
             r = base + l;
@@ -243,8 +253,18 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
             ++r;
             continue;
         }
-        const int64_t seg = (rbase + n < end ? rbase + n : end) - cur;
-        const int32_t pbeg = first_position(len, a.window) + (int32_t)(cur - rbase);
+        // this span's positions of request r: cost [cur, end) against the
+        // request's positions at [rbase + kSegCost, rbase + kSegCost + n)
+        const int64_t p0 = cur - rbase - kSegCost > 0 ? cur - rbase - kSegCost : 0;
+        const int64_t p1 = end - rbase - kSegCost < n ? end - rbase - kSegCost : n;
+        if (p1 <= p0) {  // only the request's start-up share falls in this span
+            cur = rbase + n + kSegCost;
+            rbase = cur;
+            ++r;
+            continue;
+        }
+        const int64_t seg = p1 - p0;
+        const int32_t pbeg = first_position(len, a.window) + (int32_t)p0;
         const int32_t pend = pbeg + (int32_t)seg;
         const int32_t tiles = (pend - pbeg + kTile - 1) / kTile;
         const int64_t slot = (int64_t)w + r;
@@ -439,14 +459,14 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
                 a.part_ml[(head0 + lane) * 2 + 1] = l_run;
             }
         }
-        cur += seg;
-        rbase += n;
+        cur = rbase + n + kSegCost;
+        rbase = cur;
         ++r;
     }
 }
 
 // Merge the slots of (request, head): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
-// over the slots w + r of the waves w whose spans meet the request.  A bad
+// over the slots w + r of the spans w that hold its positions.  A bad
 // slot, a request past max_seq_len (UKV_FLAG_LAYOUT) or an empty one gives
 // zeros.  One wave per (request, head); lane l sums dims l + 64 k.
 __global__ __launch_bounds__(kWave) void mla_attn_combine_kernel(MlaArgs a) {

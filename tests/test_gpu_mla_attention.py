@@ -23,26 +23,31 @@ from test_gpu_attention import GaussPair, requests
 pytestmark = pytest.mark.gpu
 
 LAT, VD = 576, 512
-TARGET_GROUPS, MIN_SPAN = 1024, 256  # the kernel's split: workgroups over all head groups, positions per span
+# the kernel's split: workgroups over all head groups, minimum span, and the
+# start-up cost of a request in positions (spans are cut by cost)
+TARGET_GROUPS, MIN_SPAN, SEG_COST = 1024, 256, 128
 
 
 def span_of(lens, hq, max_len, window):
-    """Positions per span (one workgroup's share) of the kernel's balanced split for this batch."""
+    """Cost per span (one workgroup's share) of the kernel's balanced split for this batch:
+    an upper bound on the positions one workgroup takes."""
     lens = np.asarray(lens, dtype=np.int64)
     n_max = window if 0 < window < max_len else max_len
     spans = min(TARGET_GROUPS // (hq // 16), -(-len(lens) * n_max // MIN_SPAN))
     spans = -(-max(spans, 1) // 8) * 8
     ok = (lens > 0) & (lens <= max_len)
     att = np.where(ok, np.minimum(lens, window) if window > 0 else lens, 0)
-    return max(-(-int(att.sum()) // spans), MIN_SPAN), int(att.max(initial=0))
+    cost = int(att.sum()) + SEG_COST * int((att > 0).sum())
+    return max(-(-cost // spans), MIN_SPAN), int(att.max(initial=0))
 
 
 def bound_terms(lens, hq, max_len, window=0):
     """The kernel's longest fp32 sum chain: a wave's products over its span (two bf16
     parts per weight), two lane reductions of the row sums, the merge of the slots of
-    the longest request, and the division."""
+    the longest request (its positions can start inside a span: one more), and the
+    division."""
     span, longest = span_of(lens, hq, max_len, window)
-    return 2 * span + 2 + (longest + span - 1) // span + 2 + 2
+    return 2 * span + 2 + (longest + span - 1) // span + 1 + 2 + 2
 
 
 @pytest.fixture(autouse=True)
