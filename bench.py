@@ -48,7 +48,7 @@ ATTN_SRC = os.path.join(ROOT, "store_gather_amd", "csrc", "ukv_attention.hip")
 MLA_ATTN_SRC = os.path.join(ROOT, "store_gather_amd", "csrc", "ukv_mla_attention.hip")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 WORKLOADS = ("decode_8b", "prefill_8b", "hybrid", "move_70b", "tiny", "decode_8b_fused", "prefill_8b_fused",
-             "compact_8b", "swa_decode", "decode_attn_8b", "decode_attn_mla")
+             "compact_8b", "swa_decode", "swa_decode_fused", "decode_attn_8b", "decode_attn_mla")
 
 
 def log(msg):
@@ -165,6 +165,9 @@ DESCRIPTIONS = {
                        "launch (ukv_store_kv_layers), then the per-layer gathers",
     "prefill_8b_fused": "prefill_8b_fused: the prefill_8b batch with all 32 layers stored in one launch and gathered "
                         "back in one launch (ukv_store_kv_layers / ukv_gather_kv_layers), then the move",
+    "swa_decode_fused": "swa_decode_fused: the swa_decode batch with each sub-pool's 12 layers stored in one launch "
+                        "and gathered in one launch (the full layers in full, the window layers their last 128 "
+                        "positions; ukv_store_kv_layers / ukv_gather_kv_layers), then the eviction",
     "swa_decode": "swa_decode: a 24-layer hybrid model (8 KV heads x 64, bf16, page 64) whose 12 full-attention "
                   "layers use a full sub-pool (16,540 pages) and whose 12 sliding-window-128 layers use their own "
                   "sub-pool (638 pages) reached through a full-to-SWA page mapping; 128 requests of U[256, 16384] "
@@ -203,7 +206,7 @@ def build_script(name: str, W, reduced: bool = False) -> Script:
         return attention_mla_script(W, reduced)
     if name.endswith("_fused"):
         return fuse_layers(build_script(name[: -len("_fused")], W, reduced), name,
-                           gathers=name.startswith("prefill"))
+                           gathers=name.startswith(("prefill", "swa")))
     if name == "decode_8b":
         w = W.decode_8b()
     elif name == "prefill_8b":

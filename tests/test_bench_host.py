@@ -46,7 +46,7 @@ def test_decode_8b_step_bytes_by_hand():
 
 
 def test_fused_workloads_keep_the_step_bytes():
-    for base in ("decode_8b", "prefill_8b"):
+    for base in ("decode_8b", "prefill_8b", "swa_decode"):
         a = bench.build_script(base, W, reduced=True)
         b = bench.build_script(base + "_fused", W, reduced=True)
         assert sum(op.nbytes for op in a.ops) == sum(op.nbytes for op in b.ops)
