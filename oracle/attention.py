@@ -115,25 +115,67 @@ def fp32_error_bound(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, 
     return bound
 
 
+def chain_terms_any_split(n: int, parts_per_weight: int = 1) -> int:
+    """Longest fp32 sum chain any split of n positions can form, from n alone.
+
+    Whatever way an evaluation cuts a request into pieces, one chain sums at
+    most ``parts_per_weight * n`` products (the whole request in one piece,
+    each weight entering as that many parts), then at most n partial results
+    (a piece holds at least one position), plus a few reduction and division
+    steps.  The bound of :func:`fp32_error_bound` computed with this many
+    terms holds for every split, so it does not depend on how a kernel
+    distributes positions.
+    """
+    return (parts_per_weight + 1) * n + 8
+
+
+# With every score equal (a zero query), every weight of an evaluation that
+# takes exp2(score - reference) is exactly 1; with integer values (|v| <= 8,
+# at most 2^21 positions) every float32 partial sum of weights and of
+# weighted values is then exact, whatever the split and the merge order, and
+# the output is the exact mean S/n up to the final division: one rounding, or
+# two for a reciprocal and a product.  This bound allows four.
+EXACT_MEAN_REL = 4 * 2.0 ** -24
+
+
+def exact_mean_tolerance(expected: np.ndarray) -> np.ndarray:
+    """Allowed |fp32 output - exact mean| per element for zero-query, integer-valued inputs."""
+    return EXACT_MEAN_REL * np.abs(expected)
+
+
 def decode_attention(pool, sub: int, layer: int, q_bits: np.ndarray, block_table, seq_lens, window: int,
                      scale: float, max_seq_len: int | None = None, read=None, requests=None,
-                     bound_terms: int | None = None, v_dim: int | None = None, weight_rel: float = 0.0):
+                     bound_terms=None, v_dim: int | None = None, weight_rel: float = 0.0, uniform: bool = False,
+                     read_words=None):
     """Decode attention of every request over its positions in the pool's dense views.
 
     q_bits: [R, Hq, D] bf16 bits (uint16); block_table: [R, width] int32
     kernel-facing page indices; seq_lens: [R].  ``read(offset, nbytes)``
     returns the uint16 words at a byte offset of the pool (default: the
     pool's own buffer), so that an addresses-only pool can be served from
-    values generated on demand.  ``requests`` limits the work to some
+    values generated on demand; ``read_words(indices)`` does the same for an
+    array of 2-byte word indices at once.  ``requests`` limits the work to some
     requests (the others stay zero).  An MLA sub-pool needs ``v_dim``, the
     value width taken from the front of each latent row.  Returns (out
     float64 [R, Hq, Dv], set of condition names raised), and with
     ``bound_terms`` also the fp32_error_bound [R, Hq] of every request (0
-    where nothing is read; ``weight_rel`` as there).
+    where nothing is read; ``weight_rel`` as there).  ``bound_terms`` is the
+    longest sum chain: an int for every request, or a function of the
+    request's attended position count (e.g. :func:`chain_terms_any_split`).
+    ``uniform`` takes the closed form of equal scores (a zero query or a zero
+    scale), where softmax weights every position 1/n: the output is the mean
+    of the attended value rows, summed in float64 before one division, so
+    that for integer values it is the exact mean correctly rounded.
     """
-    if read is None:
-        def read(off, nbytes):
-            return pool.raw[off: off + nbytes].view(np.uint16)
+    def read_rows(base, rows, row_bytes):
+        """uint16 words of the view rows ``rows`` (row r at byte base + r * row_bytes)."""
+        offs = base + rows * row_bytes
+        idx = (offs // 2)[:, None] + np.arange(row_bytes // 2)
+        if read_words is not None:
+            return read_words(idx)
+        if read is None:
+            return pool.raw[: pool.raw.size // 2 * 2].view(np.uint16)[idx]
+        return np.stack([read(int(off), row_bytes) for off in offs])
     spec = pool.specs[sub]
     mla = spec.kind == 1
     if mla:
@@ -163,25 +205,30 @@ def decode_attention(pool, sub: int, layer: int, q_bits: np.ndarray, block_table
             flags.add("layout")
             continue
         j0 = n - window if (window > 0 and n > window) else 0
-        positions = range(j0, n)
-        rows = []
-        for j in positions:
-            col = j // ps
-            entry = int(bt[r, col]) if col < width else -1
-            if entry < 0 or entry % bpp != 0 or entry // bpp >= spec.num_pages:
-                rows = None
-                break
-            rows.append(entry * ps + j % ps)
-        if rows is None:
+        j = np.arange(j0, n, dtype=np.int64)  # attended positions
+        col = j // ps
+        if (col >= width).any():
             flags.add("bad_block")
             continue
-        k = np.stack([read(k_base + row * k_row_bytes, k_row_bytes) for row in rows])
-        v = k[:, :dv] if mla else np.stack([read(v_base + row * v_row_bytes, v_row_bytes) for row in rows])
-        qf, kf, vf = (bf16_bits_to_f64(q_bits[r]), bf16_bits_to_f64(k).reshape(-1, hkv, d),
-                      bf16_bits_to_f64(v).reshape(-1, hkv, dv))
+        entry = bt[r, col]
+        if ((entry < 0) | (entry % bpp != 0) | (entry // bpp >= spec.num_pages)).any():
+            flags.add("bad_block")
+            continue
+        rows = entry * ps + j % ps
+        qf = bf16_bits_to_f64(q_bits[r])
+        if uniform:  # the values alone decide the output
+            assert scale == 0.0 or not qf.any(), "the uniform closed form needs equal scores"
+            v = read_rows(k_base, rows, k_row_bytes)[:, :dv] if mla else read_rows(v_base, rows, v_row_bytes)
+            vf = bf16_bits_to_f64(v).reshape(-1, hkv, dv)
+            out[r] = vf.sum(axis=0)[np.arange(hq) // (hq // hkv)] / len(rows)
+            continue
+        k = read_rows(k_base, rows, k_row_bytes)
+        v = k[:, :dv] if mla else read_rows(v_base, rows, v_row_bytes)
+        kf, vf = bf16_bits_to_f64(k).reshape(-1, hkv, d), bf16_bits_to_f64(v).reshape(-1, hkv, dv)
         out[r] = attend(qf, kf, vf, scale)
         if bound_terms is not None:
-            bound[r] = fp32_error_bound(qf, kf, vf, scale, bound_terms, weight_rel)
+            terms = bound_terms(len(rows)) if callable(bound_terms) else bound_terms
+            bound[r] = fp32_error_bound(qf, kf, vf, scale, terms, weight_rel)
     if bound_terms is not None:
         return out, frozenset(flags), bound
     return out, frozenset(flags)

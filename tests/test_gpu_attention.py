@@ -19,13 +19,12 @@ from parity_util import log, ospecs, round8, to_dev
 
 pytestmark = pytest.mark.gpu
 
-MAX_CHUNK, MIN_CHUNK = 1024, 128  # positions per split-K unit of the kernel, by batch size
-
-
-def bound_terms(max_len):
-    """The kernel's longest fp32 sum chain: a unit's positions / 4 per lane, two lane
-    reductions, the merge over units and the division (largest units, most units)."""
-    return MAX_CHUNK // 4 + 2 + (max_len + MIN_CHUNK - 1) // MIN_CHUNK + 2
+# The fp32 bound takes the longest sum chain that any split of a request's positions
+# can form, from the request's length alone: it holds however the kernel divides the
+# work, and retuning that split changes no test.  Where a long request's bound is too
+# loose to see a lost or doubled piece of the split, the exact zero-query tests below
+# (every fp32 partial sum exact) see it.
+BOUND_TERMS = A.chain_terms_any_split
 
 
 @pytest.fixture(autouse=True)
@@ -37,22 +36,37 @@ def _name(request):
 
 
 class GaussPair:
-    """A GPU pool and an oracle pool over identical Irwin-Hall bf16 bytes."""
+    """A GPU pool and an oracle pool over identical bf16 bytes: Irwin-Hall values, or
+    small integers (``ints=True``: float32 sums of them are exact)."""
 
-    def __init__(self, shapes, ps, seed=21, host=True):
+    def __init__(self, shapes, ps, seed=21, host=True, ints=False):
         self.shapes = list(shapes)
         self.ps = ps
         self.seed = seed
         plan = U.ukv_pool_plan(self.shapes, ps)
         n = round8(int(plan.required_bytes))
         self.gpu = U.allocate_pool(self.shapes, ps, device="cuda", extra_bytes=n - int(plan.required_bytes))
-        W.irwin_hall_fill_device(self.gpu.raw, seed)
-        if host:
-            self.orc = oracle.OraclePool(ospecs(self.shapes), ps, W.irwin_hall_bf16_host(seed, 0, n).view(np.uint8).copy())
+        self.host = host
+        self.set_values(ints)
+
+    def set_values(self, ints):
+        """(Re)fill both sides from one stream: the device pool on the device, the
+        oracle's in host memory (or, for an addresses-only oracle, on demand)."""
+        seed, n = self.seed, self.gpu.raw.numel()
+        if ints:
+            W.small_int_fill_device(self.gpu.raw, seed)
+            gen = W.small_int_bf16_host
+            self.read_words = lambda idx: W.small_int_bf16_words(seed, idx)
+        else:
+            W.irwin_hall_fill_device(self.gpu.raw, seed)
+            gen = W.irwin_hall_bf16_host
+            self.read_words = None
+        if self.host:
+            self.orc = oracle.OraclePool(ospecs(self.shapes), self.ps, gen(seed, 0, n).view(np.uint8).copy())
             self.read = None
         else:
-            self.orc = oracle.OraclePool(ospecs(self.shapes), ps, addresses_only=True)
-            self.read = lambda off, nbytes: W.irwin_hall_bf16_host(seed, off, nbytes)
+            self.orc = oracle.OraclePool(ospecs(self.shapes), self.ps, addresses_only=True)
+            self.read = lambda off, nbytes: gen(seed, off, nbytes)
 
 
 def requests(seed, P, ps, lens, share=False):
@@ -146,7 +160,7 @@ def test_decode_attention_parity(hkv, group, d, ps, window):
     for layer in (0, 2):
         got, gf = run_attention(pair, layer, q, bt, lens, window, scale, max_len)
         exp, ef, bound = A.decode_attention(pair.orc, 0, layer, q, bt, lens, window, scale, max_len,
-                                            bound_terms=bound_terms(max_len))
+                                            bound_terms=BOUND_TERMS)
         assert gf == ef == frozenset()
         check_close(got, exp, bound, f"layer {layer}")
         assert np.array_equal(got[lens == 0], np.zeros_like(got[lens == 0]))
@@ -168,9 +182,43 @@ def test_decode_attention_parity_unit_sizes(num_reqs, len_hi, window):
     scale = A.default_scale(d)
     got, gf = run_attention(pair, 0, q, bt, lens, window, scale, len_hi)
     exp, ef, bound = A.decode_attention(pair.orc, 0, 0, q, bt, lens, window, scale, len_hi,
-                                        bound_terms=bound_terms(len_hi))
+                                        bound_terms=BOUND_TERMS)
     assert gf == ef == frozenset()
     check_close(got, exp, bound, f"{num_reqs} requests up to {len_hi}")
+
+
+def check_exact_mean(got, exp, what):
+    """Zero-query outputs against the exact mean of the attended values (oracle/attention.py:
+    exact_mean_tolerance): every weight is 1 and every float32 partial sum of small
+    integers is exact, so only the final division rounds."""
+    tol = A.exact_mean_tolerance(exp)
+    off = np.abs(got - exp) > tol
+    log(f"  {what}: max |err| {float(np.abs(got - exp).max()):.3e}, elements off the exact mean: {int(off.sum())}")
+    assert not off.any(), f"{what}: {int(off.sum())} elements off the exact mean, first at {np.argwhere(off)[0]}"
+
+
+@pytest.mark.parametrize("num_reqs,len_hi,window", [(128, 3000, 0), (64, 3000, 0), (256, 2100, 0), (256, 4000, 700),
+                                                    (32, 9000, 0), (256, 8192, 0), (1, 60000, 0), (3, 60000, 5000)])
+def test_decode_attention_unit_merge_exact(num_reqs, len_hi, window):
+    """Zero queries over small-integer values: the output is the mean of the attended V
+    rows up to one division, whatever the kernel's split into units, so a unit lost,
+    counted twice or merged into the wrong request shows at any length (on the CPU the
+    same tolerance rejects a dropped 16-position tile of an 8,192-position request).
+    Every request is checked: the batch shapes that pick each unit size, the decode
+    batch's shape, and 60,000-position requests."""
+    ps, hkv, group, d = 16, 8, 4, 128
+    g = np.random.default_rng(num_reqs + len_hi + 1)
+    lens = g.integers(1, len_hi, size=num_reqs, endpoint=True).astype(np.int32)
+    lens[0] = len_hi
+    P = 2500
+    pair = GaussPair([W.mha(1, hkv, d, P)], ps, seed=num_reqs + 7, ints=True)
+    pages = requests(4, P, ps, lens, share=True)
+    bt, _ = pair.orc.translate_pages(0, W.padded_table(pages))
+    q = np.zeros((num_reqs, hkv * group, d), np.uint16)
+    got, gf = run_attention(pair, 0, q, bt, lens, window, 0.5, len_hi)
+    exp, ef = A.decode_attention(pair.orc, 0, 0, q, bt, lens, window, 0.5, len_hi, uniform=True)
+    assert gf == ef == frozenset()
+    check_exact_mean(got, exp, f"{num_reqs} requests up to {len_hi}")
 
 
 @pytest.mark.parametrize("hkv,group,d", [(2, 4, 128), (1, 2, 64), (2, 8, 256)])
@@ -276,8 +324,18 @@ def test_decode_attention_full_decode_8b_sampled():
         if layer in (0, 31):
             got = out.cpu().numpy().astype(np.float64)
             exp, ef, bound = A.decode_attention(pair.orc, 0, layer, q, bt, lens, 0, scale, max_len, read=pair.read,
-                                                requests=sample, bound_terms=bound_terms(max_len))
+                                                requests=sample, bound_terms=BOUND_TERMS)
             assert ef == frozenset()
             check_close(got[sample], exp[sample], bound[sample], f"layer {layer}")
             assert np.isfinite(got).all()
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    # the same batch on small-integer values with zero queries: every request exact
+    pair.set_values(ints=True)
+    q0 = np.zeros_like(q)
+    out = U.ukv_decode_attention(pair.gpu, 0, 5, torch.zeros_like(qd), bt_dev, to_dev(lens), max_len, 0, scale,
+                                 workspace=ws)
+    exp, ef = A.decode_attention(pair.orc, 0, 5, q0, bt, lens, 0, scale, max_len, read_words=pair.read_words,
+                                 uniform=True)
+    assert ef == frozenset()
+    check_exact_mean(out.cpu().numpy().astype(np.float64), exp, "layer 5, every request")
     assert U.ukv_pool_error_flags(pair.gpu) == frozenset()

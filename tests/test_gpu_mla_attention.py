@@ -4,8 +4,12 @@ oracle derives per request and head for the kernel's arithmetic (exact bf16
 products, fp32 sums, weights split into two bf16 parts: relative error
 2^-16), and bit-exact where the arithmetic is exact (one position per
 request).  Queries that are zero but for a few dims make the bound tight
-enough to catch a weight kept at bf16 precision; dense queries check the
-scores over the whole 576-wide row.
+enough to catch a weight kept at bf16 precision on short requests; dense
+queries check the scores over the whole 576-wide row.  The bound takes the
+longest sum chain any split of a request can form, from its length alone, so
+no test depends on how the kernel cuts the batch into spans; the span
+structure itself is checked exactly with zero queries over small-integer
+latents, where every float32 partial sum is exact.
 
 The pool holds Irwin-Hall bf16 values generated bit-identically on the device
 and on the host, so the oracle reads the same bytes without any copy back.
@@ -18,36 +22,20 @@ import store_gather_amd as U
 import ukv_workloads as W
 from oracle import attention as A
 from parity_util import log, to_dev
-from test_gpu_attention import GaussPair, requests
+from test_gpu_attention import GaussPair, check_exact_mean, requests
 
 pytestmark = pytest.mark.gpu
 
 LAT, VD = 576, 512
-# the kernel's split: workgroups over all head groups, minimum span, and the
-# start-up cost of a request in positions (spans are cut by cost)
-TARGET_GROUPS, MIN_SPAN, SEG_COST = 1024, 256, 128
 
 
-def span_of(lens, hq, max_len, window):
-    """Cost per span (one workgroup's share) of the kernel's balanced split for this batch:
-    an upper bound on the positions one workgroup takes."""
-    lens = np.asarray(lens, dtype=np.int64)
-    n_max = window if 0 < window < max_len else max_len
-    spans = min(TARGET_GROUPS // (hq // 16), -(-len(lens) * n_max // MIN_SPAN))
-    spans = -(-max(spans, 1) // 8) * 8
-    ok = (lens > 0) & (lens <= max_len)
-    att = np.where(ok, np.minimum(lens, window) if window > 0 else lens, 0)
-    cost = int(att.sum()) + SEG_COST * int((att > 0).sum())
-    return max(-(-cost // spans), MIN_SPAN), int(att.max(initial=0))
-
-
-def bound_terms(lens, hq, max_len, window=0):
-    """The kernel's longest fp32 sum chain: a wave's products over its span (two bf16
-    parts per weight), two lane reductions of the row sums, the merge of the slots of
-    the longest request (its positions can start inside a span: one more), and the
-    division."""
-    span, longest = span_of(lens, hq, max_len, window)
-    return 2 * span + 2 + (longest + span - 1) // span + 1 + 2 + 2
+def bound_terms(n):
+    """The longest fp32 sum chain any split of n positions can form when each weight
+    enters the value product as two bf16 parts: from the request's length alone, so the
+    bound holds however the kernel cuts the batch into spans.  (Where that bound is too
+    loose to see a lost or doubled span of a long request, the exact zero-query tests
+    below see it.)"""
+    return A.chain_terms_any_split(n, parts_per_weight=2)
 
 
 @pytest.fixture(autouse=True)
@@ -76,7 +64,7 @@ def run_mla(pair, layer, q_bits, bt, lens, window, scale, max_len, sub=0, worksp
 
 def oracle_mla(pair, layer, q_bits, bt, lens, window, scale, max_len, sub=0, requests=None):
     return A.decode_attention(pair.orc, sub, layer, q_bits, bt, lens, window, scale, max_len, read=pair.read,
-                              requests=requests, bound_terms=bound_terms(lens, q_bits.shape[1], max_len, window),
+                              requests=requests, bound_terms=bound_terms,
                               v_dim=VD, weight_rel=A.BF16_SPLIT_REL)
 
 
@@ -113,24 +101,33 @@ def test_mla_decode_attention_parity(hq, ps, window, sparse):
         assert np.isfinite(got).all()
 
 
-@pytest.mark.parametrize("num_reqs,hq,len_hi,window", [(512, 16, 8192, 0), (1, 16, 60000, 0), (300, 16, 40, 0),
-                                                       (96, 32, 8000, 0), (8, 48, 2000, 700), (130, 16, 3000, 0)])
-def test_mla_decode_attention_span_shapes(num_reqs, hq, len_hi, window):
-    """Batches that cut the balanced split differently: ~2,000-position spans over 512
-    requests, one request merged from 235 spans, spans that cross a dozen tiny
-    requests, two and three head groups (one with a window), and empty requests among
-    the rest; sampled requests checked (shared pages keep the pool small)."""
-    ps = 64
+SPAN_SHAPES = [(512, 16, 8192, 0), (1, 16, 60000, 0), (300, 16, 40, 0), (96, 32, 8000, 0), (8, 48, 2000, 700),
+               (130, 16, 3000, 0)]
+
+
+def span_batch(num_reqs, len_hi):
     g = np.random.default_rng(num_reqs + len_hi)
     lens = g.integers(1, len_hi, size=num_reqs, endpoint=True).astype(np.int32)
     lens[0] = len_hi
     if num_reqs == 130:
         lens[g.choice(num_reqs - 1, 30, replace=False) + 1] = 0
+    return lens
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+@pytest.mark.parametrize("num_reqs,hq,len_hi,window", SPAN_SHAPES)
+def test_mla_decode_attention_span_shapes(num_reqs, hq, len_hi, window, sparse):
+    """Batches that cut the balanced split differently: ~2,000-position spans over 512
+    requests, one request merged from 235 spans, spans that cross a dozen tiny
+    requests, two and three head groups (one with a window), and empty requests among
+    the rest; sampled requests checked (shared pages keep the pool small)."""
+    ps = 64
+    lens = span_batch(num_reqs, len_hi)
     P = 700
     pair = GaussPair([W.mla(1, P)], ps, seed=num_reqs)
     pages = requests(4, P, ps, lens, share=True)
     bt, _ = pair.orc.translate_pages(0, W.padded_table(pages))
-    q = queries(num_reqs, num_reqs, hq)
+    q = queries(num_reqs, num_reqs, hq, sparse)
     scale = A.default_scale(192)
     got, gf = run_mla(pair, 0, q, bt, lens, window, scale, len_hi)
     sample = sorted({0, min(1, num_reqs - 1), num_reqs // 2, num_reqs - 1, int(np.argmin(lens))})
@@ -139,6 +136,27 @@ def test_mla_decode_attention_span_shapes(num_reqs, hq, len_hi, window):
     assert gf == ef == frozenset()
     check_close(got[sample], exp[sample], bound[sample], f"{num_reqs} requests up to {len_hi}")
     assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("num_reqs,hq,len_hi,window", SPAN_SHAPES + [(1, 16, 60000, 9000), (4096, 16, 64, 0)])
+def test_mla_decode_attention_span_merge_exact(num_reqs, hq, len_hi, window):
+    """Zero queries over small-integer latents: every weight is 1 (both of its bf16
+    parts exact) and every float32 partial sum exact, so each output is the mean of the
+    request's value fronts up to one division, whatever the balanced split.  A span lost,
+    counted twice or merged into the wrong request shows at any length (on the CPU the
+    same tolerance rejects a dropped 16-position tile or 256-position span of a
+    60,000-position request).  Every request of every span shape is checked."""
+    ps = 64
+    lens = span_batch(num_reqs, len_hi)
+    P = 700
+    pair = GaussPair([W.mla(1, P)], ps, seed=num_reqs + 3, ints=True)
+    pages = requests(4, P, ps, lens, share=True)
+    bt, _ = pair.orc.translate_pages(0, W.padded_table(pages))
+    q = np.zeros((num_reqs, hq, LAT), np.uint16)
+    got, gf = run_mla(pair, 0, q, bt, lens, window, 0.3, len_hi)
+    exp, ef = A.decode_attention(pair.orc, 0, 0, q, bt, lens, window, 0.3, len_hi, v_dim=VD, uniform=True)
+    assert gf == ef == frozenset()
+    check_exact_mean(got, exp, f"{num_reqs} requests up to {len_hi}")
 
 
 def test_mla_decode_attention_single_position_is_exact():
@@ -222,10 +240,12 @@ def test_mla_decode_attention_host_errors():
     assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
 
 
-def test_mla_decode_attention_full_hybrid_sampled():
+@pytest.mark.parametrize("sparse", [False, True])
+def test_mla_decode_attention_full_hybrid_sampled(sparse):
     """The hybrid workload's MLA sub-pool at full size (24 layers, 576-wide latents,
     page 64, 128 requests of 256-16,384 positions, ~28 GiB) with 16 query heads: all
-    layers run, six sampled requests checked on two layers."""
+    layers run, six sampled requests checked on two layers; then zero queries over
+    small-integer latents, every request checked against its exact mean."""
     w = W.hybrid()
     ps = w.page_size
     shape = w.shapes[1]
@@ -236,7 +256,7 @@ def test_mla_decode_attention_full_hybrid_sampled():
     bt, ef = pair.orc.build_page_table(0, req, lens)
     assert np.array_equal(bt_dev.cpu().numpy(), bt) and ef == frozenset()
     R, hq = lens.size, 16
-    q = queries(78, R, hq)
+    q = queries(78, R, hq, sparse)
     qd = torch.from_numpy(q.view(np.int16)).to("cuda").view(torch.bfloat16)
     scale = A.default_scale(192)
     max_len = int(lens.max())
@@ -252,6 +272,17 @@ def test_mla_decode_attention_full_hybrid_sampled():
             assert ef == frozenset()
             check_close(got[sample], exp[sample], bound[sample], f"layer {layer}")
             assert np.isfinite(got).all()
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    if sparse:
+        return
+    pair.set_values(ints=True)
+    q0 = np.zeros_like(q)
+    out = U.ukv_mla_decode_attention(pair.gpu, 0, 11, torch.zeros_like(qd), bt_dev, to_dev(lens), max_len, 0, scale,
+                                     workspace=ws)
+    exp, ef = A.decode_attention(pair.orc, 0, 11, q0, bt, lens, 0, scale, max_len, v_dim=VD,
+                                 read_words=pair.read_words, uniform=True)
+    assert ef == frozenset()
+    check_exact_mean(out.cpu().numpy().astype(np.float64), exp, "layer 11, every request")
     assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
 
 

@@ -884,7 +884,8 @@ def test_mla_decode_attention_closed_forms_and_conditions():
 def test_split_weight_bound_covers_a_matrix_core_style_evaluation(n, hq, sparse):
     """An fp32 evaluation that splits each weight into bf16 high and low parts
     (scores from exact bf16 products, fp32 sums) stays inside the bound with
-    weight_rel = 2^-16, on 576-wide latents with 512-wide values.  With a
+    weight_rel = 2^-16 and the chain length any split of n positions can form
+    (from n alone), on 576-wide latents with 512-wide values.  With a
     query that is zero but for a few dims (some in the value part, some past
     it) the score term of the bound all but vanishes, and the bound is tight
     enough to reject the same evaluation with the low parts dropped (on
@@ -900,7 +901,7 @@ def test_split_weight_bound_covers_a_matrix_core_style_evaluation(n, hq, sparse)
     c = A.bf16_bits_to_f64(bits(n * lat)).reshape(n, 1, lat)
     scale = A.default_scale(192)
     exact = A.attend(q, c, c[:, :, :v_dim], scale)
-    bound = A.fp32_error_bound(q, c, c[:, :, :v_dim], scale, n + 2, A.BF16_SPLIT_REL)
+    bound = A.fp32_error_bound(q, c, c[:, :, :v_dim], scale, A.chain_terms_any_split(n, 2), A.BF16_SPLIT_REL)
     import torch
 
     def bf16(x):
@@ -919,7 +920,90 @@ def test_split_weight_bound_covers_a_matrix_core_style_evaluation(n, hq, sparse)
         assert (np.abs(hi + lo - p) <= A.BF16_SPLIT_REL * p).all()
     err = np.abs(out - exact).max(axis=1)
     assert (err <= bound).all(), (err, bound)
-    assert (bound < (2e-3 if sparse else 0.05)).all()
+    assert (bound < (6e-3 if sparse else 0.05)).all()
     if sparse and n <= 100:  # a dropped low part (bf16 weights) is caught on short requests, where
         # the sums' term 2 gamma(n) max|v| stays small
         assert (np.abs(hi_only - exact).max(axis=1) > bound).any()
+
+
+def _int_pool(shapes, ps, seed=13):
+    """A pool whose every byte pair is a small integer in bf16 (exact float32 sums)."""
+    specs = [Spec(s.kind, s.layer_num, s.head_num, s.head_dim, s.v_head_dim, s.elem_bytes, s.num_pages) for s in shapes]
+    req = oracle.plan(specs, ps).required_bytes
+    raw = W.small_int_bf16_host(seed, 0, (req + 7) // 8 * 8).view(np.uint8).copy()
+    return oracle.OraclePool(specs, ps, raw)
+
+
+def _float32_pieces(vals, cuts, reciprocal):
+    """A float32 evaluation of the mean of ``vals`` [n, dv] with every weight 1: the
+    positions cut into pieces at ``cuts``, each piece summed on its own, the pieces'
+    sums merged, then one division (or a reciprocal and a product)."""
+    edges = np.concatenate([[0], np.sort(cuts), [vals.shape[0]]]).astype(np.int64)
+    num = np.zeros(vals.shape[1], np.float32)
+    den = np.float32(0)
+    for a, b in zip(edges[:-1], edges[1:]):
+        num = num + vals[a:b].astype(np.float32).sum(axis=0, dtype=np.float32)
+        den = den + np.float32(b - a)
+    if reciprocal:
+        return (num * (np.float32(1) / den)).astype(np.float64)
+    return (num / den).astype(np.float64)
+
+
+@pytest.mark.parametrize("mla", [True, False])
+def test_exact_mean_tolerance_rejects_dropped_or_doubled_positions(mla):
+    """With a zero query every weight is 1, and with small-integer values every float32
+    partial sum is exact, so a split evaluation returns the mean up to its final
+    division.  The tolerance the GPU tests use for that case accepts a float32
+    evaluation cut into arbitrary pieces (both division forms), and rejects the mean
+    taken with one 16-position tile dropped, one 256-position span dropped, one
+    256-position span counted twice, or one position dropped, on a 60,000-position MLA
+    request (576-wide latents, 512-wide values, 16 query heads) and an 8,192-position
+    MHA request (8 KV heads x 128, 4 query heads per KV head)."""
+    if mla:
+        n, ps, hq = 60000, 64, 16
+        shape = W.mla(1, (n + ps - 1) // ps + 3)
+    else:
+        n, ps, hq = 8192, 16, 32
+        shape = W.mha(1, 8, 128, n // ps + 3)
+    pool = _int_pool([shape], ps)
+    pages = _requests(6, shape.num_pages, ps, [n])
+    bt, fl = pool.translate_pages(0, W.padded_table(pages))
+    assert fl == frozenset()
+    lat = shape.head_dim if mla else 128
+    q = np.zeros((1, hq, lat), np.uint16)
+    kw = {"v_dim": 512} if mla else {}
+    exp, fl = A.decode_attention(pool, 0, 0, q, bt, [n], 0, 1.0, uniform=True, **kw)
+    assert fl == frozenset()
+    # the closed form agrees with the softmax formula on the same rows
+    ref, _ = A.decode_attention(pool, 0, 0, q, bt, [n], 0, 1.0, **kw)
+    assert np.abs(ref - exp).max() < 1e-9
+    tol = A.exact_mean_tolerance(exp[0])
+    # the attended value rows, fetched by the independent strided builder
+    if mla:
+        c, _ = _strided(pool, 0).gather_pages(0, [pages[0]], [n], 0)
+        vals = A.bf16_bits_to_f64(c.view(np.uint16)).reshape(n, lat)[:, :512]
+        heads = [vals] * hq
+    else:
+        _, v = _strided(pool, 0).gather_pages(0, [pages[0]], [n], 0)
+        v = A.bf16_bits_to_f64(v.view(np.uint16)).reshape(n, 8, 128)
+        heads = [v[:, g // 4] for g in range(hq)]
+    assert all(float(np.abs(h).max()) <= 8 for h in heads)
+    g = np.random.default_rng(n)
+    for recip in (False, True):
+        cuts = g.choice(np.arange(1, n), size=37, replace=False)
+        got = np.stack([_float32_pieces(h, cuts, recip) for h in heads])
+        assert (np.abs(got - exp[0]) <= tol).all()
+    mutants = {
+        "tile dropped": np.delete(np.arange(n), np.arange(4096, 4112)),
+        "span dropped": np.delete(np.arange(n), np.arange(n // 2, n // 2 + 256)),
+        "span doubled": np.concatenate([np.arange(n), np.arange(1024, 1280)]),
+        "position dropped": np.arange(1, n),
+    }
+    for what, keep in mutants.items():
+        bad = np.stack([h[keep].sum(axis=0) / keep.size for h in heads])
+        assert (np.abs(bad - exp[0]) > tol).any(), what
+        # the fp32 bound derived from the length alone cannot see a dropped tile this long
+        # (why the tests add the exact case)
+    bound = A.fp32_error_bound(np.zeros((hq, lat)), np.zeros((n, 1, lat)), heads[0][:, None, :], 1.0,
+                               A.chain_terms_any_split(n, 2 if mla else 1))
+    assert (bound > 1e-3).all()

@@ -19,6 +19,8 @@ Generators (both published, both re-implemented here from their definitions):
 * Irwin-Hall (1927): the sum of n independent uniforms; with n = 4 it stands
   in for N(0, 1) where the values must be generated bit-identically on the
   device and on the host (pools of many GiB that attention reads).
+* Small integers: the top four bits of a SplitMix64 output, minus 8: values
+  whose float32 sums are exact, for checks whose result is known exactly.
 * Box-Muller (1958): z0 = sqrt(-2 ln u1) cos(2 pi u2), z1 = sqrt(-2 ln u1) sin(2 pi u2),
   with u1, u2 in (0, 1] from 53-bit SplitMix64 draws; z is rounded to float32
   and then to bfloat16 with round-to-nearest-even on the bit pattern.
@@ -197,6 +199,60 @@ def irwin_hall_fill_device(t, seed: int, byte_start: int = 0, chunk_elems: int =
 
 
 # ----------------------------------------------------------------------------
+# Small-integer bf16 values
+# ----------------------------------------------------------------------------
+
+def small_int_bf16_host(seed: int, byte_start: int, nbytes: int) -> np.ndarray:
+    """bf16 bit patterns of integers in [-8, 7] for bytes [byte_start, byte_start+nbytes) of a buffer.
+
+    The element at byte 2e is the top four bits of SplitMix64 element e of the
+    stream seeded with ``seed``, minus 8.  Every such integer is exact in bf16,
+    and sums of up to 2^21 of them are exact in float32.
+    """
+    assert byte_start % 2 == 0 and nbytes % 2 == 0
+    z = splitmix64(seed, byte_start // 2, nbytes // 2)
+    v = (z >> np.uint64(60)).astype(np.int64) - 8
+    return (v.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def small_int_bf16_words(seed: int, words: np.ndarray) -> np.ndarray:
+    """:func:`small_int_bf16_host`'s values at arbitrary 2-byte word indices (any shape)."""
+    w = np.asarray(words, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed & MASK64) + (w + np.uint64(1)) * np.uint64(GAMMA)
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(M1)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(M2)
+        z = z ^ (z >> np.uint64(31))
+    v = (z >> np.uint64(60)).astype(np.int64) - 8
+    return (v.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def small_int_fill_device(t, seed: int, byte_start: int = 0, chunk_elems: int = 1 << 27):
+    """Write :func:`small_int_bf16_host`'s values for bytes [byte_start, ...) into device uint8 ``t``."""
+    import torch
+
+    assert t.dtype == torch.uint8 and t.is_contiguous()
+    assert byte_start % 2 == 0 and t.numel() % 2 == 0
+    out = t.view(torch.int16)
+    n = out.numel()
+    e0 = byte_start // 2
+    for a in range(0, n, chunk_elems):
+        b = min(n, a + chunk_elems)
+        z = torch.arange(e0 + a + 1, e0 + b + 1, dtype=torch.int64, device=t.device)
+        z.mul_(_i64(GAMMA)).add_(_i64(seed & MASK64))
+        z ^= (z >> 30) & ((1 << 34) - 1)
+        z.mul_(_i64(M1))
+        z ^= (z >> 27) & ((1 << 37) - 1)
+        z.mul_(_i64(M2))
+        z ^= (z >> 31) & ((1 << 33) - 1)
+        v = ((z >> 60) & 15) - 8
+        del z
+        bits = (v.to(torch.float32).view(torch.int32) >> 16) & 0xFFFF
+        out[a:b].copy_(bits.to(torch.int16))
+        del v, bits
+
+
+# ----------------------------------------------------------------------------
 # Shapes of the workloads
 # ----------------------------------------------------------------------------
 
@@ -337,7 +393,7 @@ def tiny_mha(seed: int = 0) -> Workload:
 
 
 def decode_8b(num_pages: int = 4096, num_reqs: int = 256, len_lo: int = 1024, len_hi: int = 8192,
-              new_tokens: int = 256, layer_num: int = 32, seed: int = 0) -> Workload:
+              new_tokens: int = 256, layer_num: int = 32, seed: int = 0, share_pages: bool = True) -> Workload:
     """Llama-3-8B-shape decode step: 32 layers, 8 KV heads of dim 128, bf16, page size 16.
 
     ``num_reqs`` requests with lengths uniform in [len_lo, len_hi].  The pool
@@ -346,13 +402,19 @@ def decode_8b(num_pages: int = 4096, num_reqs: int = 256, len_lo: int = 1024, le
     pages, continuing where the previous request stopped: pages are shared
     between requests (read-only, as prefix sharing would).  The decode store
     writes ``new_tokens`` distinct live slots per layer.
+
+    ``share_pages=False`` keeps the same requests and lengths but sizes the pool
+    to hold every context apart (1 + the pages they need, ~74 K pages, ~144 GiB):
+    no page is read twice in a layer.
     """
     ps = 16
-    w = Workload("decode_8b", ps, [mha(layer_num, 8, 128, num_pages)], seed)
     g = rng(seed, SUB_LENS)
     lens = g.integers(len_lo, len_hi, endpoint=True, size=num_reqs).astype(np.int32)
-    perm = page_permutation(seed, num_pages)
     npages = (lens.astype(np.int64) + ps - 1) // ps
+    if not share_pages:
+        num_pages = int(1 + npages.sum())
+    w = Workload("decode_8b", ps, [mha(layer_num, 8, 128, num_pages)], seed)
+    perm = page_permutation(seed, num_pages)
     start = np.concatenate([[0], np.cumsum(npages)])
     w.req_pages[0] = [perm[(start[r] + np.arange(npages[r])) % perm.size] for r in range(num_reqs)]
     w.req_lens[0] = lens
@@ -498,5 +560,5 @@ __all__ = [
     "normal_bf16_device", "SubPoolShape", "mha", "mla", "rng", "live_slots", "page_permutation",
     "slots_of_requests", "padded_table", "out_offsets", "Workload", "tiny_mha", "decode_8b",
     "dirichlet_lengths", "prefill_8b", "hybrid", "move_70b", "compaction_plan", "swa_decode", "MHA", "MLA",
-    "irwin_hall_bf16_host", "irwin_hall_fill_device",
+    "irwin_hall_bf16_host", "irwin_hall_fill_device", "small_int_bf16_host", "small_int_bf16_words", "small_int_fill_device",
 ]
