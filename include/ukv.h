@@ -53,6 +53,7 @@ extern "C" {
 #define UKV_ERR_ALIGNMENT -5       /* misaligned anchor or buffer */
 #define UKV_ERR_TAIL_PAD -6        /* raw buffer smaller than envelopes + tail pad */
 #define UKV_ERR_HIP -7             /* a HIP runtime call failed */
+#define UKV_ERR_RACE -8            /* debug validation: ids whose rows would race (nothing launched) */
 
 /* ---- sticky device flags (ukv_pool_error_flags) --------------------------- */
 #define UKV_FLAG_SLOT_RANGE 1u /* translate: slot / page past the pool or the v2p table; wrote 0 */
@@ -174,10 +175,13 @@ int ukv_plan_view(const ukv_plan *plan, const ukv_subpool_spec *specs, int32_t s
  *   t < 0 (tombstone) -> 0, the page-0 sink; phys < 0 (unmapped) -> 0;
  *   page >= v2p_len, or phys >= num_pages -> 0 and UKV_FLAG_SLOT_RANGE.
  * slots_dev: int64[n]; v2p_dev: int32[v2p_len] or NULL; out_dev: int32[n].
- * out_dev must not overlap slots_dev (UKV_ERR_INVALID_ARG): the narrower
- * int32 outputs of later slots would land on int64 inputs other threads may
- * not have read yet.  n in [0, 2^31).  Translate once per batch; every layer
- * reuses the ids.
+ * out_dev may be slots_dev itself (the pages' out= path aliases its input, so
+ * a graph-captured batch can translate into its own slot buffer): the int32
+ * ids then fill the buffer's first 4n bytes, translated by one workgroup that
+ * reads each chunk of slots before writing its ids (a few microseconds per
+ * thousand slots); any other overlap of out_dev with slots_dev or v2p_dev is
+ * UKV_ERR_INVALID_ARG.  n in [0, 2^31).  Translate once per batch; every
+ * layer reuses the ids.
  */
 int ukv_translate_loc_for_kernel(const ukv_pool *pool, int32_t sub, const int64_t *slots_dev, int64_t n,
                                  const int32_t *v2p_dev, int64_t v2p_len, int32_t *out_dev, hipStream_t stream);
@@ -200,7 +204,8 @@ int ukv_translate_pages_for_kernel(const ukv_pool *pool, int32_t sub, const int3
  * kernels see kernel-facing ids): phys * ps + t % ps with phys = v2p[t / ps]
  * (identity when v2p_dev is NULL).  Tombstones (t < 0) and unmapped pages
  * give -1; a page past the table or the pool gives -1 and raises
- * UKV_FLAG_SLOT_RANGE.  slots_dev int64[n] -> out_dev int32[n] (no overlap).
+ * UKV_FLAG_SLOT_RANGE.  slots_dev int64[n] -> out_dev int32[n], which may be
+ * slots_dev itself (as in ukv_translate_loc_for_kernel).
  */
 int ukv_translate_loc(const ukv_pool *pool, int32_t sub, const int64_t *slots_dev, int64_t n, const int32_t *v2p_dev,
                       int64_t v2p_len, int32_t *out_dev, hipStream_t stream);
@@ -423,6 +428,27 @@ int ukv_mla_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, c
 uint64_t ukv_mla_decode_attention_workspace_bytes(const ukv_pool *pool, int32_t sub, int32_t num_reqs,
                                                   int32_t q_heads, int32_t v_dim, int32_t max_seq_len,
                                                   int32_t window);
+
+/*
+ * Debug validation (for tests and bring-up; not for the data path).  The
+ * pages' fused-store review (DKV 评论区精华, 风险与影响) shows what goes wrong
+ * when ids are not what a kernel expects; rows that collide are the quieter
+ * failure: two live store entries on one row, or a move whose destinations
+ * repeat or meet its sources, race on the device with no error.
+ * ukv_check_store_ids: UKV_ERR_RACE when two entries of ids (host array) name
+ * the same row, row 0 excepted (the sink row that tombstones share).
+ * ukv_check_move_ids: UKV_ERR_RACE when dst (host array) repeats an id or an
+ * id of src is also in dst.  Both are host-only (no device), O(n log n), and
+ * name the first offending pair in ukv_last_error().
+ * ukv_pool_set_debug(pool, 1): from then on ukv_store_kv[_layers],
+ * ukv_move_kv and ukv_move_pages first copy their id arrays to the host on
+ * their stream (the call then synchronises that stream and allocates host
+ * memory) and run these checks; on UKV_ERR_RACE nothing is launched.  0
+ * turns it off (the default).
+ */
+int ukv_check_store_ids(const int32_t *ids, int64_t n);
+int ukv_check_move_ids(const int32_t *dst, const int32_t *src, int64_t n);
+int ukv_pool_set_debug(ukv_pool *pool, int32_t on);
 
 /*
  * Reads and clears the pool's sticky flags (UKV_FLAG_*): enqueued on

@@ -34,6 +34,7 @@ STATUS = {
     -5: "UKV_ERR_ALIGNMENT",
     -6: "UKV_ERR_TAIL_PAD",
     -7: "UKV_ERR_HIP",
+    -8: "UKV_ERR_RACE",
 }
 FLAGS = {1: "slot_range", 2: "bad_id", 4: "bad_block", 8: "layout"}
 
@@ -44,6 +45,7 @@ EXPORTS = (
     "ukv_status_name", "ukv_translate_loc", "ukv_move_pages", "ukv_remap_pages", "ukv_evict_window",
     "ukv_build_page_table", "ukv_decode_attention", "ukv_decode_attention_workspace_bytes",
     "ukv_mla_decode_attention", "ukv_mla_decode_attention_workspace_bytes",
+    "ukv_check_store_ids", "ukv_check_move_ids", "ukv_pool_set_debug",
 )
 
 
@@ -115,6 +117,9 @@ def _load() -> ctypes.CDLL:
         "ukv_evict_window": [vp, vp, i64, vp, i64, vp, i32, i32, vp],
         "ukv_build_page_table": [vp, i32, vp, i64, vp, i32, vp, i64, vp, vp],
         "ukv_decode_attention": [vp, i32, i32, vp, i32, vp, i64, vp, i32, i32, i32, ctypes.c_float, vp, vp, u64, vp],
+        "ukv_check_store_ids": [vp, i64],
+        "ukv_check_move_ids": [vp, vp, i64],
+        "ukv_pool_set_debug": [vp, i32],
         "ukv_mla_decode_attention": [vp, i32, i32, vp, i32, i32, vp, i64, vp, i32, i32, i32, ctypes.c_float, vp, vp,
                                      u64, vp],
     }
@@ -155,6 +160,26 @@ def _specs_array(specs: Sequence) -> "ctypes.Array":
         arr[i] = SubpoolSpec(int(s.kind), int(s.layer_num), int(s.head_num), int(s.head_dim), int(s.v_head_dim),
                              int(s.elem_bytes), int(s.num_pages))
     return arr
+
+
+def ukv_check_store_ids(ids) -> None:
+    """Host-side race check of a store's kernel-facing ids (numpy int32): raises
+    UkvError(UKV_ERR_RACE) when two entries other than the sink row 0 name one row."""
+    import numpy as np
+
+    a = np.ascontiguousarray(ids, dtype=np.int32)
+    _check(_lib.ukv_check_store_ids(a.ctypes.data if a.size else None, a.size))
+
+
+def ukv_check_move_ids(dst, src) -> None:
+    """Host-side race check of a move's ids: dst distinct, src and dst disjoint."""
+    import numpy as np
+
+    d = np.ascontiguousarray(dst, dtype=np.int32)
+    s_ = np.ascontiguousarray(src, dtype=np.int32)
+    if d.size != s_.size:
+        raise ValueError("dst and src differ in length")
+    _check(_lib.ukv_check_move_ids(d.ctypes.data if d.size else None, s_.ctypes.data if s_.size else None, d.size))
 
 
 def ukv_pool_plan(specs: Sequence, page_size: int) -> Plan:
@@ -552,6 +577,12 @@ def ukv_decode_attention(pool: Pool, sub: int, layer: int, q: torch.Tensor, bloc
                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                      _stream_handle(stream)))
     return out
+
+
+def ukv_pool_set_debug(pool: "Pool", on: bool) -> None:
+    """Debug validation on the pool's stores and moves (host copies of their ids, checked
+    for races before each launch; the calls then synchronise their stream)."""
+    _check(_lib.ukv_pool_set_debug(pool.handle, 1 if on else 0))
 
 
 def ukv_mla_decode_attention_workspace_bytes(pool: Pool, sub: int, num_reqs: int, q_heads: int, v_dim: int,

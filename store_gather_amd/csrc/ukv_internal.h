@@ -21,6 +21,9 @@ int check_launch(const char *who);                                       // hipG
 bool ranges_overlap(const void *a, uint64_t na, const void *b, uint64_t nb);
 
 int plan_pool(const ukv_subpool_spec *specs, int32_t n_specs, int64_t page_size, ukv_plan *out);
+// Race checks of the debug validation (host arrays): UKV_ERR_RACE with the first offending pair.
+int check_store_ids(const int32_t *ids, int64_t n, const char *who);
+int check_move_ids(const int32_t *dst, const int32_t *src, int64_t n, const char *who);
 int view_of(const ukv_plan &p, const ukv_subpool_spec &s, int32_t sub, int32_t layer, int32_t kv, ukv_view *out);
 
 }  // namespace ukv
@@ -32,4 +35,5 @@ struct ukv_pool {
     uint64_t raw_bytes;
     int device;
     uint32_t *flags_dev;  // [0] sticky flags, [1] read-back slot; owned
+    int32_t debug;        // ukv_pool_set_debug: store / move ids checked for races before each launch
 };

@@ -79,7 +79,6 @@ constexpr int kWave = 64;
 constexpr int64_t kMaxGrid = 0x7fffffff;
 constexpr int kTile = 16;                // positions per tile
 constexpr int kHeads = 16;               // query heads per wave (the MFMA width)
-constexpr int kWavesPerCu = 8;          // the span kernel's occupancy: two waves per SIMD
 constexpr int64_t kTargetGroups = 1024;  // two-wave workgroups: 4 per CU x 256 CUs, one round
 constexpr int64_t kMinSpan = 256;        // positions per wave, at least (a partial is 32 KiB)
 constexpr int64_t kSegCost = 128;        // a span's cost of starting a request, in positions' worth of time

@@ -9,10 +9,34 @@
 // step below.
 #include "ukv_internal.h"
 
+#include <algorithm>
+#include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 namespace ukv {
+
+namespace {
+thread_local char g_last_error[1024] = "";
+}
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+const char *last_error() { return g_last_error; }
+
+bool ranges_overlap(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na != 0 && nb != 0 && x < y + nb && y < x + na;
+}
 
 namespace {
 
@@ -131,4 +155,86 @@ int view_of(const ukv_plan &p, const ukv_subpool_spec &s, int32_t sub, int32_t l
     return UKV_OK;
 }
 
+// Positions of entries sorted by value, ties by position: the first equal
+// neighbours are the first repeated value.
+static std::vector<int64_t> order_by_value(const int32_t *v, int64_t n) {
+    std::vector<int64_t> idx((size_t)n);
+    for (int64_t i = 0; i < n; ++i) idx[(size_t)i] = i;
+    std::sort(idx.begin(), idx.end(), [v](int64_t a, int64_t b) { return v[a] != v[b] ? v[a] < v[b] : a < b; });
+    return idx;
+}
+
+int check_store_ids(const int32_t *ids, int64_t n, const char *who) {
+    if (n < 0 || (n > 0 && ids == nullptr)) return fail(UKV_ERR_INVALID_ARG, "%s: null ids or n < 0", who);
+    const std::vector<int64_t> idx = order_by_value(ids, n);
+    for (size_t k = 1; k < idx.size(); ++k) {
+        const int32_t id = ids[idx[k]];
+        if (id != 0 && id == ids[idx[k - 1]])
+            return fail(UKV_ERR_RACE,
+                        "%s: ids[%lld] and ids[%lld] are both row %d: their rows would race (only the sink row 0, "
+                        "which tombstones share, may repeat)",
+                        who, (long long)idx[k - 1], (long long)idx[k], id);
+    }
+    return UKV_OK;
+}
+
+int check_move_ids(const int32_t *dst, const int32_t *src, int64_t n, const char *who) {
+    if (n < 0 || (n > 0 && (dst == nullptr || src == nullptr)))
+        return fail(UKV_ERR_INVALID_ARG, "%s: null dst / src or n < 0", who);
+    const std::vector<int64_t> idx = order_by_value(dst, n);
+    for (size_t k = 1; k < idx.size(); ++k)
+        if (dst[idx[k]] == dst[idx[k - 1]])
+            return fail(UKV_ERR_RACE, "%s: dst[%lld] and dst[%lld] are both %d: their writes would race", who,
+                        (long long)idx[k - 1], (long long)idx[k], dst[idx[k]]);
+    for (int64_t i = 0; i < n; ++i) {  // a source that is also a destination: read and write race
+        const int32_t x = src[i];
+        auto it = std::lower_bound(idx.begin(), idx.end(), x, [dst](int64_t a, int32_t val) { return dst[a] < val; });
+        if (it != idx.end() && dst[*it] == x)
+            return fail(UKV_ERR_RACE, "%s: src[%lld] = %d is also dst[%lld]: the sets must be disjoint", who,
+                        (long long)i, x, (long long)*it);
+    }
+    return UKV_OK;
+}
+
 }  // namespace ukv
+
+// Host-only entry points (no device, no HIP call).
+extern "C" {
+
+int ukv_pool_plan(const ukv_subpool_spec *specs, int32_t n_specs, int64_t page_size, ukv_plan *out) {
+    return ukv::plan_pool(specs, n_specs, page_size, out);
+}
+
+int ukv_plan_view(const ukv_plan *plan, const ukv_subpool_spec *specs, int32_t sub, int32_t layer, int32_t kv,
+                  ukv_view *out) {
+    if (plan == nullptr || specs == nullptr || out == nullptr)
+        return ukv::fail(UKV_ERR_INVALID_ARG, "ukv_plan_view: null argument");
+    if (sub < 0 || sub >= plan->n_sub || plan->n_sub > UKV_MAX_SUB)
+        return ukv::fail(UKV_ERR_INVALID_ARG, "ukv_plan_view: sub-pool %d outside [0, %d)", sub, plan->n_sub);
+    return ukv::view_of(*plan, specs[sub], sub, layer, kv, out);
+}
+
+int ukv_check_store_ids(const int32_t *ids, int64_t n) { return ukv::check_store_ids(ids, n, "ukv_check_store_ids"); }
+
+int ukv_check_move_ids(const int32_t *dst, const int32_t *src, int64_t n) {
+    return ukv::check_move_ids(dst, src, n, "ukv_check_move_ids");
+}
+
+const char *ukv_last_error(void) { return ukv::last_error(); }
+
+const char *ukv_status_name(int status) {
+    switch (status) {
+        case UKV_OK: return "UKV_OK";
+        case UKV_ERR_INVALID_ARG: return "UKV_ERR_INVALID_ARG";
+        case UKV_ERR_ASYMMETRIC_KV: return "UKV_ERR_ASYMMETRIC_KV";
+        case UKV_ERR_KERNEL_ID_BOUND: return "UKV_ERR_KERNEL_ID_BOUND";
+        case UKV_ERR_OVERFLOW: return "UKV_ERR_OVERFLOW";
+        case UKV_ERR_ALIGNMENT: return "UKV_ERR_ALIGNMENT";
+        case UKV_ERR_TAIL_PAD: return "UKV_ERR_TAIL_PAD";
+        case UKV_ERR_HIP: return "UKV_ERR_HIP";
+        case UKV_ERR_RACE: return "UKV_ERR_RACE";
+        default: return "UKV_ERR_UNKNOWN";
+    }
+}
+
+}  // extern "C"

@@ -33,6 +33,7 @@
 #include <initializer_list>
 #include <new>
 #include <type_traits>
+#include <vector>
 
 #include "ukv_internal.h"
 
@@ -40,22 +41,6 @@
 // errors
 // ----------------------------------------------------------------------------
 namespace ukv {
-
-namespace {
-thread_local char g_last_error[1024] = "";
-}
-
-int fail(int code, const char *fmt, ...) {
-    va_list ap;
-    va_start(ap, fmt);
-    std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
-    va_end(ap);
-    return code;
-}
-
-void clear_error() { g_last_error[0] = '\0'; }
-
-const char *last_error() { return g_last_error; }
 
 int check_pool_call(const ukv_pool *pool, int32_t sub, const char *who) {
     if (pool == nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: null pool", who);
@@ -71,11 +56,6 @@ int check_launch(const char *who) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(UKV_ERR_HIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
     return UKV_OK;
-}
-
-bool ranges_overlap(const void *a, uint64_t na, const void *b, uint64_t nb) {
-    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-    return na != 0 && nb != 0 && x < y + nb && y < x + na;
 }
 
 }  // namespace ukv
@@ -143,12 +123,9 @@ struct TranslateArgs {
 // phys = v2p[page] (identity without a table); unmapped (phys < 0) -> 0;
 // past the table or the pool -> 0 plus UKV_FLAG_SLOT_RANGE;
 // else phys * ps * blocks_per_page + offset.
-__global__ __launch_bounds__(kBlock) void translate_slots_kernel(TranslateArgs a) {
-    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (i >= a.n) return;
-    const int64_t t = a.slots[i];
+__device__ __forceinline__ int32_t translate_one(const TranslateArgs &a, int64_t t, bool &out_of_range) {
     int32_t id = a.internal ? -1 : 0;
-    bool out_of_range = false;
+    out_of_range = false;
     if (t >= 0) {
         const int64_t page = t / a.ps;
         const int64_t offset = t - page * a.ps;
@@ -167,8 +144,38 @@ __global__ __launch_bounds__(kBlock) void translate_slots_kernel(TranslateArgs a
             id = (int32_t)(phys * (a.internal ? a.ps : a.page_stride) + offset);
         }
     }
-    a.out[i] = id;
+    return id;
+}
+
+__global__ __launch_bounds__(kBlock) void translate_slots_kernel(TranslateArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= a.n) return;
+    bool out_of_range;
+    a.out[i] = translate_one(a, a.slots[i], out_of_range);
     if (out_of_range) atomicOr(a.flags, UKV_FLAG_SLOT_RANGE);
+}
+
+// The same with the int32 ids written over the int64 slots they come from (the
+// pages' out= path, which may alias its input).  Id i occupies bytes [4i, 4i+4),
+// inside slot i/2, so one workgroup walks the array in chunks: every thread reads
+// its slot, the workgroup waits, then writes.  A chunk's writes land on slots of
+// that chunk or earlier ones, all read before its barrier; later chunks' slots
+// lie past every byte written so far.
+constexpr int kInPlaceBlock = 1024;
+
+__global__ __launch_bounds__(kInPlaceBlock) void translate_inplace_kernel(TranslateArgs a) {
+    bool any_out = false;
+    for (int64_t c = 0; c < a.n; c += kInPlaceBlock) {
+        const int64_t i = c + threadIdx.x;
+        bool out_of_range = false;
+        int32_t id = 0;
+        if (i < a.n) id = translate_one(a, a.slots[i], out_of_range);
+        any_out |= out_of_range;
+        __syncthreads();
+        if (i < a.n) a.out[i] = id;
+        __syncthreads();
+    }
+    if (any_out) atomicOr(a.flags, UKV_FLAG_SLOT_RANGE);
 }
 
 // page q -> the dense views' page index of its first slot, phys * blocks_per_page.
@@ -508,6 +515,183 @@ __global__ __launch_bounds__(kBlock) void move_kernel(MoveArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// row-piece kernels: store, gather and move of rows that are whole 1 KiB pieces
+// ----------------------------------------------------------------------------
+// For rows of 2^k KiB (k >= 0) moved as 16-byte vectors, a wave copies one
+// 1 KiB piece of one view's row (gather: two consecutive pieces): one
+// non-temporal load and one non-temporal store per lane, so the memory system
+// sees short, fully coalesced accesses issued in address order from many
+// waves.  Measured on MI355X against the tile kernels above, same pools and
+// inputs, bit-identical results (% of 8 TB/s, medians of interleaved runs):
+// prefill-shape store of 2 KiB rows, 32 layers in one launch, 71 -> 75%; its
+// gather-back 74 -> 80.5%; the 65,536-row move 71 -> 79%; the 70B-shape move
+// 75 -> 79%; the 1 KiB-row hybrid gather 73 -> 77%; a decode-size store launch
+// (256 rows) 14 -> 7.6 us.  One case goes the other way: the decode gather whose
+// requests share pages (most reads hit the Infinity Cache) ran at 81% with the
+// tile kernel's 8 KiB per wave and runs at 78% here.  Plain loads instead of
+// non-temporal ones lost 4-5 points on the gather-back; 2 and 4 KiB per wave
+// (K and V of a piece together, whole rows, pairs of rows) and a wave-wide
+// request search instead of the binary search were no faster.  1 KiB rows
+// keep the tile store (75 vs 74%).  A piece index w = (row, view, piece) with
+// the piece count a power of two splits into shifts.
+constexpr int kPieceVecs = kWave;  // 16-byte vectors per piece: 1 KiB
+
+// Waves MI355X-class GPUs hold at once for these kernels: CUs x 32.  The CU count is
+// read once per device.
+int64_t resident_waves() {
+    static int64_t cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * 32;
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cache[dev] = (int64_t)cus * 32;
+    }
+    return cache[dev];
+}
+
+// Pieces per wave for a launch of `pieces` 1 KiB pieces: `base` for launches of
+// more than eight rounds of resident waves (there one piece, or one row, per wave
+// measured fastest); a small launch gets enough per wave (at most 8) to finish in
+// one round, so it costs one chain of load latencies instead of several.
+// Measured on the 32-layer decode store (256 rows x 32 layers, 67 MB): 23.3 us
+// with one piece per wave.
+int pieces_per_wave(int64_t pieces, int base) {
+    const int64_t round = resident_waves();
+    if (pieces > 8 * round) return base;
+    int k = base;
+    while (k < 8 && pieces > round * k) k *= 2;
+    return k;
+}
+
+// log2 of the 1 KiB pieces per row, or -1 when rows are not 2^k whole pieces of
+// 16-byte vectors (then the tile kernels run).
+int piece_shift(int vec_bytes, uint64_t row_bytes) {
+    if (vec_bytes != 16 || row_bytes % 1024 != 0) return -1;
+    const uint64_t pcs = row_bytes / 1024;
+    int lp = 0;
+    while ((1ull << lp) < pcs) ++lp;
+    return (1ull << lp) == pcs ? lp : -1;
+}
+
+// K_view[l][ids[i]] = k[l][i], V_view[l][ids[i]] = v[l][i]: piece u = (entry, view,
+// piece of the row) = u >> (lp + log2 NKV), (u >> lp) & (NKV - 1), u & (2^lp - 1),
+// for the layer of grid row blockIdx.y.  Wave w copies pieces K*w .. K*w + K-1,
+// their loads issued together (K > 1 only for launches small enough to finish in
+// one round of resident waves: see pieces_per_wave).
+template <int NKV, int K>
+__global__ __launch_bounds__(kBlock) void store_piece_kernel(StoreArgs a, int lp) {
+    const int lane = lane_id();
+    const int64_t u0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave_in_block()) * K;
+    constexpr int hb = NKV == 2 ? 1 : 0;
+    if ((u0 >> (lp + hb)) >= a.n) return;
+    const int64_t src0 = (int64_t)blockIdx.y * a.src_layer_stride;
+    const uint64_t view0 = (uint64_t)blockIdx.y * a.layer_base_step;
+    u32x4 buf[K];
+    u32x4 *dst[K];
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t u = u0 + k;
+        const int64_t i = u >> (lp + hb);
+        dst[k] = nullptr;
+        if (i >= a.n) continue;
+        const int h = (int)((u >> lp) & (NKV - 1));
+        const int64_t p = u & ((1ll << lp) - 1);
+        const int32_t id = a.ids[i];
+        if (!kernel_facing(id, a.n_rows, a.page_stride, a.ps)) {
+            bad = true;
+            continue;
+        }
+        const int64_t c = p * kPieceVecs + lane;
+        buf[k] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(a.src[h] + src0 + i * a.src_stride) + c);
+        dst[k] = reinterpret_cast<u32x4 *>(a.pool + a.base[h] + view0 + (uint64_t)(uint32_t)id * a.row_bytes) + c;
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        if (dst[k] != nullptr) __builtin_nontemporal_store(buf[k], dst[k]);
+    if (bad && lane == 0 && blockIdx.y == 0) atomicOr(a.flags, UKV_FLAG_BAD_ID);
+}
+
+// Each wave copies K (2 or more) consecutive pieces u = K*w, ... of the (output
+// row, view, piece) sequence: with K = 2, a whole 2 KiB row of one view, or, for
+// 1 KiB rows, the K and the V row of one output row.  The request of the first
+// row is found by binary search over cu_out (scalar); the others advance from it.
+template <int NKV, int K>
+__global__ __launch_bounds__(kBlock) void gather_piece_kernel(GatherArgs a, int lp) {
+    const int lane = lane_id();
+    constexpr int hb = NKV == 2 ? 1 : 0;
+    const int64_t u0 = ((int64_t)blockIdx.x * kWavesPerBlock + wave_in_block()) * K;
+    const int64_t o0 = u0 >> (lp + hb);
+    if (o0 >= a.out_rows) return;
+    const uint64_t view0 = (uint64_t)blockIdx.y * a.layer_base_step;
+    const int64_t out0 = (int64_t)blockIdx.y * a.out_layer_stride;
+    int32_t lo = 0, hi = a.num_reqs;  // r = number of requests r' >= 1 with cu_out[r'] <= o0
+    while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (a.cu_out[mid + 1] <= o0)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    int32_t r = lo;
+    uint32_t bad = 0;
+    u32x4 buf[K];
+    u32x4 *dst[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int64_t u = u0 + k;
+        const int64_t o = u >> (lp + hb);
+        dst[k] = nullptr;
+        if (o >= a.out_rows) continue;
+        while (r < a.num_reqs && a.cu_out[r + 1] <= o) ++r;
+        const int32_t row = gather_source_row(a, o, r, bad);
+        if (row < 0) continue;
+        const int h = (int)((u >> lp) & (NKV - 1));
+        const int64_t c = (u & ((1ll << lp) - 1)) * kPieceVecs + lane;
+        buf[k] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(a.pool + a.base[h] + view0 + (uint64_t)(uint32_t)row * a.row_bytes) + c);
+        dst[k] = reinterpret_cast<u32x4 *>(a.out[h] + out0 + o * (int64_t)a.row_bytes) + c;
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        if (dst[k] != nullptr) __builtin_nontemporal_store(buf[k], dst[k]);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 &&
+        (a.cu_out[0] != 0 || a.cu_out[a.num_reqs] != a.out_rows))
+        bad |= UKV_FLAG_LAYOUT;  // the launch's one check of the ragged layout as a whole
+    if (bad != 0 && lane == 0 && blockIdx.y == 0) atomicOr(a.flags, bad);
+}
+
+// view[l][dst[i]] = view[l][src[i]]: wave w copies piece w & (2^lp - 1) of view
+// (w >> lp) & (NKV - 1) of unit u = w >> (lp + log2 NKV) = pair * nl + layer
+// (layers of one pair are neighbours: their rows share the pair's two pages).
+template <int NKV>
+__global__ __launch_bounds__(kBlock) void move_piece_kernel(MoveArgs a, int lp) {
+    const int lane = lane_id();
+    const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
+    constexpr int hb = NKV == 2 ? 1 : 0;
+    const int64_t u = w >> (lp + hb);
+    if (u >= a.n * a.nl) return;
+    const int h = (int)((w >> lp) & (NKV - 1));
+    const int64_t p = w & ((1ll << lp) - 1);
+    const int64_t i = u / a.nl;
+    const int32_t l = (int32_t)(u - i * a.nl);
+    const int32_t d = a.dst[i];
+    const int32_t s = a.src[i];
+    if (!kernel_facing(d, a.n_rows, a.page_stride, a.ps) || !kernel_facing(s, a.n_rows, a.page_stride, a.ps)) {
+        if (lane == 0 && l == 0 && h == 0 && p == 0) atomicOr(a.flags, UKV_FLAG_BAD_ID);  // one report per pair
+        return;
+    }
+    const uint64_t view = a.base0 + (uint64_t)l * a.layer_step + (uint64_t)h * a.kv_step;
+    const int64_t c = p * kPieceVecs + lane;
+    const u32x4 *from = reinterpret_cast<const u32x4 *>(a.pool + view + (uint64_t)(uint32_t)s * a.row_bytes) + c;
+    u32x4 *to = reinterpret_cast<u32x4 *>(a.pool + view + (uint64_t)(uint32_t)d * a.row_bytes) + c;
+    __builtin_nontemporal_store(__builtin_nontemporal_load(from), to);
+}
+
+// ----------------------------------------------------------------------------
 // page relocation and table rewrite (compaction: DKV alloc excerpt and 关键文件)
 // ----------------------------------------------------------------------------
 struct PageMoveArgs {
@@ -547,7 +731,7 @@ __global__ __launch_bounds__(kBlock) void move_pages_kernel(PageMoveArgs a) {
 #pragma unroll
     for (int j = 0; j < TPL; ++j) {
         const int64_t c = c0 + (int64_t)j * kWave;
-        if (c < a.vecs) buf[j] = src[c];
+        if (c < a.vecs) buf[j] = __builtin_nontemporal_load(&src[c]);
     }
 #pragma unroll
     for (int j = 0; j < TPL; ++j) {
@@ -600,6 +784,20 @@ __global__ void flags_fetch_clear_kernel(uint32_t *f) {
 // ----------------------------------------------------------------------------
 // host helpers
 // ----------------------------------------------------------------------------
+
+// Debug validation: the id arrays of a store (b == nullptr) or a move, copied to
+// the host on the call's stream, checked for rows that would race.
+int debug_check(const ukv_pool *pool, const int32_t *a_dev, const int32_t *b_dev, int64_t n, hipStream_t stream,
+                const char *who) {
+    if (!pool->debug || n == 0) return UKV_OK;
+    std::vector<int32_t> a((size_t)n), b(b_dev != nullptr ? (size_t)n : 0);
+    hipError_t e = hipMemcpyAsync(a.data(), a_dev, (size_t)n * 4, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess && b_dev != nullptr)
+        e = hipMemcpyAsync(b.data(), b_dev, (size_t)n * 4, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(UKV_ERR_HIP, "%s: debug validation copy: %s", who, hipGetErrorString(e));
+    return b_dev == nullptr ? ukv::check_store_ids(a.data(), n, who) : ukv::check_move_ids(a.data(), b.data(), n, who);
+}
 
 // Largest power of two <= 16 dividing every value: the widest integer vector
 // every row access of a call can use.
@@ -656,10 +854,6 @@ Tiling tiling_for(int32_t vecs, int32_t nkv, int64_t rows, bool gather) {
 // C ABI
 // ----------------------------------------------------------------------------
 extern "C" {
-
-int ukv_pool_plan(const ukv_subpool_spec *specs, int32_t n_specs, int64_t page_size, ukv_plan *out) {
-    return ukv::plan_pool(specs, n_specs, page_size, out);
-}
 
 int ukv_pool_create(const ukv_subpool_spec *specs, int32_t n_specs, int64_t page_size, void *raw_dev,
                     uint64_t raw_bytes, ukv_pool **out) {
@@ -736,15 +930,6 @@ int ukv_pool_view(const ukv_pool *pool, int32_t sub, int32_t layer, int32_t kv, 
     return ukv::view_of(pool->plan, pool->spec[sub], sub, layer, kv, out);
 }
 
-int ukv_plan_view(const ukv_plan *plan, const ukv_subpool_spec *specs, int32_t sub, int32_t layer, int32_t kv,
-                  ukv_view *out) {
-    if (plan == nullptr || specs == nullptr || out == nullptr)
-        return fail(UKV_ERR_INVALID_ARG, "ukv_plan_view: null argument");
-    if (sub < 0 || sub >= plan->n_sub || plan->n_sub > UKV_MAX_SUB)
-        return fail(UKV_ERR_INVALID_ARG, "ukv_plan_view: sub-pool %d outside [0, %d)", sub, plan->n_sub);
-    return ukv::view_of(*plan, specs[sub], sub, layer, kv, out);
-}
-
 static int translate_common(const ukv_pool *pool, int32_t sub, const void *in, uint64_t in_elem, int64_t n,
                             const int32_t *v2p, int64_t v2p_len, int32_t *out, hipStream_t stream, bool pages,
                             const char *who, bool internal = false) {
@@ -754,9 +939,13 @@ static int translate_common(const ukv_pool *pool, int32_t sub, const void *in, u
     if (n == 0) return UKV_OK;
     if (in == nullptr || out == nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: null input or output", who);
     if (v2p != nullptr && v2p_len < 0) return fail(UKV_ERR_INVALID_ARG, "%s: v2p_len < 0", who);
-    const bool same = (const void *)out == in && in_elem == sizeof(int32_t);
+    // out may be the input buffer itself (same start): int32 ids over int64 slots take the
+    // one-workgroup in-place kernel; any other overlap is refused
+    const bool same = (const void *)out == in;
     if (!same && ranges_overlap(in, (uint64_t)n * in_elem, out, (uint64_t)n * sizeof(int32_t)))
-        return fail(UKV_ERR_INVALID_ARG, "%s: output overlaps the input", who);
+        return fail(UKV_ERR_INVALID_ARG, "%s: output overlaps the input without starting where it starts", who);
+    if (v2p != nullptr && ranges_overlap(v2p, (uint64_t)v2p_len * 4, out, (uint64_t)n * sizeof(int32_t)))
+        return fail(UKV_ERR_INVALID_ARG, "%s: output overlaps the v2p table", who);
     const ukv_subpool_spec &s = pool->spec[sub];
     const ukv_subpool_plan &q = pool->plan.sub[sub];
     TranslateArgs a;
@@ -776,6 +965,8 @@ static int translate_common(const ukv_pool *pool, int32_t sub, const void *in, u
     const unsigned grid = (unsigned)((n + kBlock - 1) / kBlock);
     if (pages)
         hipLaunchKernelGGL(translate_pages_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
+    else if (same)
+        hipLaunchKernelGGL(translate_inplace_kernel, dim3(1), dim3(kInPlaceBlock), 0, stream, a);
     else
         hipLaunchKernelGGL(translate_slots_kernel, dim3(grid), dim3(kBlock), 0, stream, a);
     return check_launch(who);
@@ -836,6 +1027,8 @@ int ukv_store_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin, 
     if (src_row_stride_bytes < (int64_t)q.row_bytes)
         return fail(UKV_ERR_INVALID_ARG, "%s: src_row_stride_bytes=%lld < row bytes %llu", who,
                     (long long)src_row_stride_bytes, (unsigned long long)q.row_bytes);
+    rc = debug_check(pool, ids_dev, nullptr, n, stream, who);
+    if (rc != UKV_OK) return rc;
     StoreArgs a;
     std::memset(&a, 0, sizeof(a));
     ukv_view vk, vv;
@@ -861,6 +1054,28 @@ int ukv_store_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin, 
                                   (uint64_t)(uintptr_t)k_dev, (uint64_t)(uintptr_t)a.src[1],
                                   (uint64_t)src_row_stride_bytes, magnitude(a.src_layer_stride)});
     a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
+    const int lp = piece_shift(vb, q.row_bytes);
+    if (lp >= 1) {  // rows of 2 KiB and more: a wave per 1 KiB piece (1 KiB rows measured faster in tiles)
+        const int64_t pieces = (n * nkv) << lp;
+        const int k = pieces_per_wave(pieces * layer_count, 1);
+        const int64_t grid = ((pieces + k - 1) / k + kWavesPerBlock - 1) / kWavesPerBlock;
+        if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n too large for one launch", who);
+        const dim3 g((unsigned)grid, (unsigned)layer_count), b(kBlock);
+        auto go = [&](auto kv, auto kk) {
+            hipLaunchKernelGGL((store_piece_kernel<decltype(kv)::value, decltype(kk)::value>), g, b, 0, stream, a,
+                               lp);
+        };
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I4 = std::integral_constant<int, 4>;
+        using I8 = std::integral_constant<int, 8>;
+        if (nkv == 2) {
+            if (k == 1) go(I2(), I1()); else if (k == 2) go(I2(), I2()); else if (k == 4) go(I2(), I4()); else go(I2(), I8());
+        } else {
+            if (k == 1) go(I1(), I1()); else if (k == 2) go(I1(), I2()); else if (k == 4) go(I1(), I4()); else go(I1(), I8());
+        }
+        return check_launch(who);
+    }
     const Tiling tl = tiling_for(a.vecs, nkv, n, false);
     a.tile_rows = tl.tile_rows;
     a.tiles_per_wave = tl.tiles_per_wave;
@@ -942,6 +1157,28 @@ int ukv_gather_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin,
                                   (uint64_t)(uintptr_t)k_out_dev, (uint64_t)(uintptr_t)a.out[1],
                                   magnitude(a.out_layer_stride)});
     a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
+    const int lp = piece_shift(vb, q.row_bytes);
+    if (lp >= 0) {  // rows of whole 1 KiB pieces: a wave per two pieces (more in a small launch)
+        const int64_t pieces = (out_rows * nkv) << lp;
+        const int k = pieces_per_wave(pieces * layer_count, 2);
+        const int64_t grid = ((pieces + k - 1) / k + kWavesPerBlock - 1) / kWavesPerBlock;
+        if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: out_rows too large for one launch", who);
+        const dim3 g((unsigned)grid, (unsigned)layer_count), b(kBlock);
+        auto go = [&](auto kv, auto kk) {
+            hipLaunchKernelGGL((gather_piece_kernel<decltype(kv)::value, decltype(kk)::value>), g, b, 0, stream, a,
+                               lp);
+        };
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I4 = std::integral_constant<int, 4>;
+        using I8 = std::integral_constant<int, 8>;
+        if (nkv == 2) {
+            if (k == 2) go(I2(), I2()); else if (k == 4) go(I2(), I4()); else go(I2(), I8());
+        } else {
+            if (k == 2) go(I1(), I2()); else if (k == 4) go(I1(), I4()); else go(I1(), I8());
+        }
+        return check_launch(who);
+    }
     const Tiling tl = tiling_for(a.vecs, nkv, out_rows, true);
     a.tile_rows = tl.tile_rows;
     a.tiles_per_wave = tl.tiles_per_wave;
@@ -984,6 +1221,8 @@ int ukv_move_kv(const ukv_pool *pool, int32_t sub, const int32_t *dst_dev, const
     const int32_t nl = layer_end - layer_begin;
     if (n == 0 || nl == 0) return UKV_OK;
     if (dst_dev == nullptr || src_dev == nullptr) return fail(UKV_ERR_INVALID_ARG, "%s: null dst or src", who);
+    rc = debug_check(pool, dst_dev, src_dev, n, stream, who);
+    if (rc != UKV_OK) return rc;
     const int64_t units = n * (int64_t)nl;
     const int nkv = s.kind == UKV_MHA ? 2 : 1;
     ukv_view v0;
@@ -1005,6 +1244,16 @@ int ukv_move_kv(const ukv_pool *pool, int32_t sub, const int32_t *dst_dev, const
     a.flags = pool->flags_dev;
     const int vb = vec_bytes_for({q.row_bytes, v0.byte_offset, a.kv_step, (uint64_t)(uintptr_t)pool->raw});
     a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
+    const int lp = piece_shift(vb, q.row_bytes);
+    if (lp >= 0) {  // rows of whole 1 KiB pieces: a wave per piece
+        const int64_t grid = (((units * nkv) << lp) + kWavesPerBlock - 1) / kWavesPerBlock;
+        if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n * layers too large for one launch", who);
+        if (nkv == 2)
+            hipLaunchKernelGGL(move_piece_kernel<2>, dim3((unsigned)grid), dim3(kBlock), 0, stream, a, lp);
+        else
+            hipLaunchKernelGGL(move_piece_kernel<1>, dim3((unsigned)grid), dim3(kBlock), 0, stream, a, lp);
+        return check_launch(who);
+    }
     // units per tile: about 512 chunks of one view per tile, two rounds of 4 per lane
     // (4 rows of 2 KiB; measured on MI355X against 1 and 2 units and 2 or 8 per lane)
     const int64_t tu = (int64_t)2 * kWave * kTasksPerLane / a.vecs;
@@ -1032,6 +1281,8 @@ int ukv_move_pages(const ukv_pool *pool, int32_t sub, const int32_t *dst_pages_d
     if (n == 0) return UKV_OK;
     if (dst_pages_dev == nullptr || src_pages_dev == nullptr)
         return fail(UKV_ERR_INVALID_ARG, "%s: null dst or src", who);
+    rc = debug_check(pool, dst_pages_dev, src_pages_dev, n, stream, who);
+    if (rc != UKV_OK) return rc;
     const ukv_subpool_plan &q = pool->plan.sub[sub];
     PageMoveArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -1103,6 +1354,12 @@ int ukv_evict_window(const ukv_pool *pool, int32_t *mapping_dev, int64_t map_len
     return check_launch(who);
 }
 
+int ukv_pool_set_debug(ukv_pool *pool, int32_t on) {
+    if (pool == nullptr) return fail(UKV_ERR_INVALID_ARG, "ukv_pool_set_debug: null pool");
+    pool->debug = on != 0;
+    return UKV_OK;
+}
+
 int ukv_pool_error_flags(ukv_pool *pool, hipStream_t stream, uint32_t *out_and_clear) {
     if (pool == nullptr || out_and_clear == nullptr)
         return fail(UKV_ERR_INVALID_ARG, "ukv_pool_error_flags: null argument");
@@ -1119,22 +1376,6 @@ int ukv_pool_error_flags(ukv_pool *pool, hipStream_t stream, uint32_t *out_and_c
     if (e != hipSuccess) return fail(UKV_ERR_HIP, "ukv_pool_error_flags: %s", hipGetErrorString(e));
     *out_and_clear = host;
     return UKV_OK;
-}
-
-const char *ukv_last_error(void) { return ukv::last_error(); }
-
-const char *ukv_status_name(int status) {
-    switch (status) {
-        case UKV_OK: return "UKV_OK";
-        case UKV_ERR_INVALID_ARG: return "UKV_ERR_INVALID_ARG";
-        case UKV_ERR_ASYMMETRIC_KV: return "UKV_ERR_ASYMMETRIC_KV";
-        case UKV_ERR_KERNEL_ID_BOUND: return "UKV_ERR_KERNEL_ID_BOUND";
-        case UKV_ERR_OVERFLOW: return "UKV_ERR_OVERFLOW";
-        case UKV_ERR_ALIGNMENT: return "UKV_ERR_ALIGNMENT";
-        case UKV_ERR_TAIL_PAD: return "UKV_ERR_TAIL_PAD";
-        case UKV_ERR_HIP: return "UKV_ERR_HIP";
-        default: return "UKV_ERR_UNKNOWN";
-    }
 }
 
 }  // extern "C"

@@ -84,13 +84,42 @@ def test_translate_pages_parity_and_in_place():
     assert U.ukv_pool_error_flags(pair.gpu) == ef
 
 
-def test_translate_rejects_overlapping_output():
+@pytest.mark.parametrize("n", [1, 2, 1023, 1024, 1025, 5000, 70001])
+def test_translate_in_place_over_its_slots(n):
+    """The int32 ids written over the int64 slots they come from (out = the slots' own
+    buffer): bit-exact against the oracle for the kernel-facing and the internal ids, with
+    and without a v2p table, across the one-workgroup kernel's chunk boundaries, with
+    tombstones, unmapped pages and out-of-range slots (flagged)."""
+    P, ps = 300, 16
+    pair = Pair([W.mha(3, 2, 8, P)], ps)
+    g = np.random.default_rng(n)
+    slots = g.integers(-3, P * ps + 40, size=n).astype(np.int64)
+    v2p = g.permutation(P + 20).astype(np.int32)[:P + 5]
+    v2p[g.choice(P + 5, 30, replace=False)] = -1
+    v2p[v2p >= P + 3] = P + 1  # some mapped past the pool
+    for table in (None, v2p):
+        for internal in (False, True):
+            buf = to_dev(slots)
+            out = buf.view(torch.int32)[:n]
+            fn = U.ukv_translate_loc if internal else U.ukv_translate_loc_for_kernel
+            fn(pair.gpu, 0, buf, v2p=None if table is None else to_dev(table), out=out)
+            ofn = pair.orc.translate_loc if internal else pair.orc.translate
+            exp, ef = ofn(0, slots, table)
+            assert np.array_equal(out.cpu().numpy(), exp), (internal, table is None)
+            assert U.ukv_pool_error_flags(pair.gpu) == ef
+
+
+def test_translate_rejects_other_overlaps():
     pair = Pair([W.mha(2, 2, 8, 16)], 4)
     buf = torch.zeros(64, dtype=torch.int64, device="cuda")
-    out = buf.view(torch.int32)[:64]
-    with pytest.raises(U.UkvError) as e:
-        U.ukv_translate_loc_for_kernel(pair.gpu, 0, buf, out=out)
-    assert e.value.status == "UKV_ERR_INVALID_ARG"
+    for out in (buf.view(torch.int32)[1:65], buf.view(torch.int32)[64:128]):
+        with pytest.raises(U.UkvError) as e:
+            U.ukv_translate_loc_for_kernel(pair.gpu, 0, buf, out=out)
+        assert e.value.status == "UKV_ERR_INVALID_ARG"
+    table = torch.zeros(80, dtype=torch.int32, device="cuda")
+    with pytest.raises(U.UkvError, match="v2p"):
+        U.ukv_translate_loc_for_kernel(pair.gpu, 0, buf, v2p=table, out=table[8:72])
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
 
 
 # ---------------------------------------------------------------------------
@@ -605,3 +634,49 @@ def test_swa_subpool_store_gather_and_eviction():
     assert np.array_equal(map_d.cpu().numpy(), mapping)
     assert (mapping != w.swa_mapping).sum() > 0
     assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+
+
+def test_debug_validation_refuses_racing_ids_before_launch():
+    """With the pool's debug validation on, stores and moves whose ids would race are
+    refused (UKV_ERR_RACE) before anything is launched, so the pool keeps every byte;
+    ids that do not race (tombstones sharing the sink row included) run exactly as
+    without it.  Only the non-racing calls reach the device."""
+    w = W.tiny_mha(seed=0)
+    pair = Pair(w.shapes, w.page_size)
+    rb = pair.rb(0)
+    U.ukv_pool_set_debug(pair.gpu, True)
+    slots = w.store_slots[0]  # 34 live slots and 3 tombstones
+    ids_d = U.ukv_translate_loc_for_kernel(pair.gpu, 0, to_dev(slots))
+    ids, _ = pair.orc.translate(0, slots)
+    k = bf16_rows(300, slots.size, rb)
+    v = bf16_rows(301, slots.size, rb)
+    U.ukv_store_kv(pair.gpu, 0, 1, ids_d, rows_dev(k), rows_dev(v))
+    assert pair.orc.store(0, 1, ids, k, v) == frozenset()
+    pair.record_store(0, 1, ids, k, v)
+    pair.assert_pools_equal()
+    before = pair.gpu.raw.clone()
+    live = np.nonzero(ids != 0)[0]
+    dup = ids.copy()
+    dup[live[5]] = dup[live[20]]
+    with pytest.raises(U.UkvError, match="UKV_ERR_RACE.*would race"):
+        U.ukv_store_kv(pair.gpu, 0, 0, to_dev(dup), rows_dev(k), rows_dev(v))
+    with pytest.raises(U.UkvError, match="UKV_ERR_RACE"):
+        U.ukv_store_kv_layers(pair.gpu, 0, 0, 2, to_dev(dup), rows_dev(np.concatenate([k, k])).view(2, slots.size, -1),
+                              rows_dev(np.concatenate([v, v])).view(2, slots.size, -1))
+    src, _ = pair.orc.translate(0, w.move_src[0])
+    dst, _ = pair.orc.translate(0, w.move_dst[0])
+    overlap = dst.copy()
+    overlap[3] = src[6]
+    with pytest.raises(U.UkvError, match="UKV_ERR_RACE.*disjoint"):
+        U.ukv_move_kv(pair.gpu, 0, to_dev(overlap), to_dev(src))
+    with pytest.raises(U.UkvError, match="UKV_ERR_RACE"):
+        U.ukv_move_pages(pair.gpu, 0, to_dev(np.array([3, 4, 3], np.int32)), to_dev(np.array([7, 8, 9], np.int32)))
+    torch.cuda.synchronize()
+    assert torch.equal(pair.gpu.raw, before), "a refused call wrote to the pool"
+    U.ukv_move_kv(pair.gpu, 0, to_dev(dst), to_dev(src))  # disjoint: runs
+    assert pair.orc.move(0, dst, src, 0, 2) == frozenset()
+    U.ukv_pool_set_debug(pair.gpu, False)
+    U.ukv_move_kv(pair.gpu, 0, to_dev(src), to_dev(dst))  # off again: no host copy, same result as the oracle
+    assert pair.orc.move(0, src, dst, 0, 2) == frozenset()
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    pair.assert_pools_equal()
