@@ -390,6 +390,28 @@ uint64_t ukv_decode_attention_workspace_bytes(const ukv_pool *pool, int32_t sub,
                                               int32_t max_seq_len, int32_t window);
 
 /*
+ * ukv_decode_attention without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, arithmetic, conditions and results
+ * as ukv_decode_attention (the same kernels run); the partial results live in
+ * a fixed 64 MiB device array of the library, one per GPU it runs on, held
+ * until the process ends.  The call itself allocates nothing: the array's
+ * device address is looked up once per device, on the first call there.
+ * Errors: as ukv_decode_attention, plus UKV_ERR_INVALID_ARG when
+ * ukv_decode_attention_workspace_bytes(...) for these sizes exceeds 64 MiB
+ * (256 requests of up to 8,192 positions with 32 query heads of dim 128 need
+ * 34 MB), and UKV_ERR_HIP when the address lookup fails.  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, or other threads) race on it and must be ordered by the caller.
+ * Nothing in the array needs clearing: each call writes every partial it
+ * reads.
+ */
+int ukv_decode_attention_noalloc(const ukv_pool *pool, int32_t sub, int32_t layer, const void *q_dev, int32_t q_heads,
+                                 const int32_t *block_table_dev, int64_t bt_stride, const int32_t *seq_lens_dev,
+                                 int32_t num_reqs, int32_t max_seq_len, int32_t window, float scale, float *out_dev,
+                                 hipStream_t stream);
+
+/*
  * Decode attention over an MLA sub-pool's dense latent view (DKV 功能与动机:
  * the MLA sub-pool already exposes dense per-layer views, read through one
  * dense tensor plus the shared block table).  The pages print no MLA

@@ -44,7 +44,7 @@ EXPORTS = (
     "ukv_gather_kv", "ukv_gather_kv_layers", "ukv_move_kv", "ukv_pool_error_flags", "ukv_last_error",
     "ukv_status_name", "ukv_translate_loc", "ukv_move_pages", "ukv_remap_pages", "ukv_evict_window",
     "ukv_build_page_table", "ukv_decode_attention", "ukv_decode_attention_workspace_bytes",
-    "ukv_mla_decode_attention", "ukv_mla_decode_attention_workspace_bytes",
+    "ukv_mla_decode_attention", "ukv_mla_decode_attention_workspace_bytes", "ukv_decode_attention_noalloc",
     "ukv_check_store_ids", "ukv_check_move_ids", "ukv_pool_set_debug",
 )
 
@@ -117,6 +117,7 @@ def _load() -> ctypes.CDLL:
         "ukv_evict_window": [vp, vp, i64, vp, i64, vp, i32, i32, vp],
         "ukv_build_page_table": [vp, i32, vp, i64, vp, i32, vp, i64, vp, vp],
         "ukv_decode_attention": [vp, i32, i32, vp, i32, vp, i64, vp, i32, i32, i32, ctypes.c_float, vp, vp, u64, vp],
+        "ukv_decode_attention_noalloc": [vp, i32, i32, vp, i32, vp, i64, vp, i32, i32, i32, ctypes.c_float, vp, vp],
         "ukv_check_store_ids": [vp, i64],
         "ukv_check_move_ids": [vp, vp, i64],
         "ukv_pool_set_debug": [vp, i32],
@@ -583,6 +584,33 @@ def ukv_pool_set_debug(pool: "Pool", on: bool) -> None:
     """Debug validation on the pool's stores and moves (host copies of their ids, checked
     for races before each launch; the calls then synchronise their stream)."""
     _check(_lib.ukv_pool_set_debug(pool.handle, 1 if on else 0))
+
+
+def ukv_decode_attention_noalloc(pool: Pool, sub: int, layer: int, q: torch.Tensor, block_table: torch.Tensor,
+                                 seq_lens: torch.Tensor, max_seq_len: int, window: int, scale: float,
+                                 out: torch.Tensor, stream=None) -> torch.Tensor:
+    """ukv_decode_attention with the partial results in the library's fixed device array
+    (nothing allocated: the caller passes the output too)."""
+    d = pool.device
+    _dev_ptr(q, "q", d, torch.bfloat16)
+    _dev_ptr(block_table, "block_table", d, torch.int32)
+    _dev_ptr(seq_lens, "seq_lens", d, torch.int32)
+    _dev_ptr(out, "out", d, torch.float32)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [num_reqs, q_heads, head_dim] tensor")
+    num_reqs, q_heads, head_dim = q.shape
+    if seq_lens.numel() != num_reqs or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous with one length per request")
+    if block_table.dim() != 2 or block_table.shape[0] != num_reqs or (
+            block_table.numel() > 0 and block_table.stride(1) != 1):
+        raise ValueError("block_table must be [num_reqs, width] with unit inner stride")
+    if tuple(out.shape) != (num_reqs, q_heads, head_dim) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor shaped like q")
+    _check(_lib.ukv_decode_attention_noalloc(pool.handle, sub, layer, q.data_ptr(), q_heads, block_table.data_ptr(),
+                                             block_table.stride(0) if block_table.numel() else 0,
+                                             seq_lens.data_ptr(), num_reqs, int(max_seq_len), int(window),
+                                             float(scale), out.data_ptr(), _stream_handle(stream)))
+    return out
 
 
 def ukv_mla_decode_attention_workspace_bytes(pool: Pool, sub: int, num_reqs: int, q_heads: int, v_dim: int,

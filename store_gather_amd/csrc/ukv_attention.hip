@@ -41,6 +41,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "ukv_internal.h"
 
@@ -506,6 +507,40 @@ int64_t max_chunks_for(int32_t max_seq_len, int32_t window, int32_t chunk) {
     return n > 0 ? (n + chunk - 1) / chunk : 0;
 }
 
+// ukv_decode_attention_noalloc's partials: a fixed device array, one per GPU the
+// library runs on, held until the process ends (64 MiB: the decode batch of 256
+// requests of up to 8,192 positions with 32 query heads of 128 needs 34 MB).  In
+// host code `scratch` only names the symbol; its device address, looked up once
+// per device, is what kernels and copies take.
+constexpr uint64_t kNoAllocScratchBytes = 64ull << 20;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_lock;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, found with hipGetSymbolAddress on the
+// first call on that device (the device is current: check_pool_call checked it).
+int device_scratch(void **out, const char *who) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(UKV_ERR_HIP, "%s: current device %d unusable for the fixed scratch", who, dev);
+    std::lock_guard<std::mutex> hold(g_scratch_lock);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(UKV_ERR_HIP, "%s: device address of the fixed scratch: %s", who, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return UKV_OK;
+}
+
+int decode_attention_with(const ukv_pool *pool, int32_t sub, int32_t layer, const void *q_dev, int32_t q_heads,
+                          const int32_t *block_table_dev, int64_t bt_stride, const int32_t *seq_lens_dev,
+                          int32_t num_reqs, int32_t max_seq_len, int32_t window, float scale, float *out_dev,
+                          void *workspace_dev, uint64_t workspace_bytes, hipStream_t stream, const char *who);
+
 }  // namespace
 
 extern "C" {
@@ -562,7 +597,42 @@ int ukv_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const
                          const int32_t *block_table_dev, int64_t bt_stride, const int32_t *seq_lens_dev,
                          int32_t num_reqs, int32_t max_seq_len, int32_t window, float scale, float *out_dev,
                          void *workspace_dev, uint64_t workspace_bytes, hipStream_t stream) {
-    const char *who = "ukv_decode_attention";
+    return decode_attention_with(pool, sub, layer, q_dev, q_heads, block_table_dev, bt_stride, seq_lens_dev, num_reqs,
+                                 max_seq_len, window, scale, out_dev, workspace_dev, workspace_bytes, stream,
+                                 "ukv_decode_attention");
+}
+
+int ukv_decode_attention_noalloc(const ukv_pool *pool, int32_t sub, int32_t layer, const void *q_dev, int32_t q_heads,
+                                 const int32_t *block_table_dev, int64_t bt_stride, const int32_t *seq_lens_dev,
+                                 int32_t num_reqs, int32_t max_seq_len, int32_t window, float scale, float *out_dev,
+                                 hipStream_t stream) {
+    const char *who = "ukv_decode_attention_noalloc";
+    int rc = check_pool_call(pool, sub, who);
+    if (rc != UKV_OK) return rc;
+    const uint64_t need = ukv_decode_attention_workspace_bytes(pool, sub, num_reqs, q_heads, max_seq_len, window);
+    if (need > kNoAllocScratchBytes)
+        return fail(UKV_ERR_INVALID_ARG,
+                    "%s: this batch needs %llu bytes of partial results; the fixed scratch holds %llu "
+                    "(pass a workspace to ukv_decode_attention instead)",
+                    who, (unsigned long long)need, (unsigned long long)kNoAllocScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        rc = device_scratch(&ws, who);
+        if (rc != UKV_OK) return rc;
+    }
+    return decode_attention_with(pool, sub, layer, q_dev, q_heads, block_table_dev, bt_stride, seq_lens_dev, num_reqs,
+                                 max_seq_len, window, scale, out_dev, ws, need > 0 ? kNoAllocScratchBytes : 0, stream,
+                                 who);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_attention_with(const ukv_pool *pool, int32_t sub, int32_t layer, const void *q_dev, int32_t q_heads,
+                          const int32_t *block_table_dev, int64_t bt_stride, const int32_t *seq_lens_dev,
+                          int32_t num_reqs, int32_t max_seq_len, int32_t window, float scale, float *out_dev,
+                          void *workspace_dev, uint64_t workspace_bytes, hipStream_t stream, const char *who) {
     int rc = check_pool_call(pool, sub, who);
     if (rc != UKV_OK) return rc;
     const ukv_subpool_spec &s = pool->spec[sub];
@@ -660,4 +730,4 @@ int ukv_decode_attention(const ukv_pool *pool, int32_t sub, int32_t layer, const
     }
 }
 
-}  // extern "C"
+}  // namespace
