@@ -203,11 +203,13 @@ def rocprof_summary(directory: str, workload: str, out_dir: str = PROFILE_DIR) -
             if r["Counter_Name"] == name:
                 out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
                 grids.setdefault(r["Kernel_Name"], []).append(int(r["Grid_Size"]))
-        if script.roofline_largest_grid:
-            for k in out:
+        if script.roofline_largest_grid:  # the largest grid over all the roofline kind's kernels
+            g = max(max(v) for k, v in grids.items() if is_roof(k))
+            for k in list(out):
                 if is_roof(k):
-                    g = max(grids[k])
                     out[k] = [v for v, gg in zip(out[k], grids[k]) if gg == g]
+                    if not out[k]:
+                        del out[k]
         return out
 
     fetch, write = counters("FETCH_SIZE"), counters("WRITE_SIZE")
