@@ -551,12 +551,12 @@ int64_t resident_waves() {
     return cache[dev];
 }
 
-// Pieces per wave for a launch of `pieces` 1 KiB pieces: `base` for launches of
-// more than eight rounds of resident waves (there one piece, or one row, per wave
-// measured fastest); a small launch gets enough per wave (at most 8) to finish in
-// one round, so it costs one chain of load latencies instead of several.
-// Measured on the 32-layer decode store (256 rows x 32 layers, 67 MB): 23.3 us
-// with one piece per wave.
+// Pieces per store wave for a launch of `pieces` 1 KiB pieces: `base` for
+// launches of more than eight rounds of resident waves (there one piece per
+// wave measured fastest); a small launch gets enough per wave (at most 8) to
+// finish in one round, so it pays one chain of load latencies instead of
+// several.  Measured on the 32-layer decode store (256 rows x 32 layers, 67 MB,
+// four pieces per wave): 13.1-13.6 against 13.6-14.2 us.
 int pieces_per_wave(int64_t pieces, int base) {
     const int64_t round = resident_waves();
     if (pieces > 8 * round) return base;
@@ -615,9 +615,9 @@ __global__ __launch_bounds__(kBlock) void store_piece_kernel(StoreArgs a, int lp
     if (bad && lane == 0 && blockIdx.y == 0) atomicOr(a.flags, UKV_FLAG_BAD_ID);
 }
 
-// Each wave copies K (2 or more) consecutive pieces u = K*w, ... of the (output
-// row, view, piece) sequence: with K = 2, a whole 2 KiB row of one view, or, for
-// 1 KiB rows, the K and the V row of one output row.  The request of the first
+// Each wave copies K consecutive pieces u = K*w, ... of the (output row, view,
+// piece) sequence (K = 2: a whole 2 KiB row of one view, or, for 1 KiB rows, the
+// K and the V row of one output row).  The request of the first
 // row is found by binary search over cu_out (scalar); the others advance from it.
 template <int NKV, int K>
 __global__ __launch_bounds__(kBlock) void gather_piece_kernel(GatherArgs a, int lp) {
@@ -1158,25 +1158,17 @@ int ukv_gather_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin,
                                   magnitude(a.out_layer_stride)});
     a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
     const int lp = piece_shift(vb, q.row_bytes);
-    if (lp >= 0) {  // rows of whole 1 KiB pieces: a wave per two pieces (more in a small launch)
+    if (lp >= 0) {  // rows of whole 1 KiB pieces: a wave per two pieces
+        // (four per wave in a small launch was slower: a window gather of 16,384
+        // rows took 17.9 against 15.6 us)
         const int64_t pieces = (out_rows * nkv) << lp;
-        const int k = pieces_per_wave(pieces * layer_count, 2);
-        const int64_t grid = ((pieces + k - 1) / k + kWavesPerBlock - 1) / kWavesPerBlock;
+        const int64_t grid = ((pieces + 1) / 2 + kWavesPerBlock - 1) / kWavesPerBlock;
         if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: out_rows too large for one launch", who);
         const dim3 g((unsigned)grid, (unsigned)layer_count), b(kBlock);
-        auto go = [&](auto kv, auto kk) {
-            hipLaunchKernelGGL((gather_piece_kernel<decltype(kv)::value, decltype(kk)::value>), g, b, 0, stream, a,
-                               lp);
-        };
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
-        using I4 = std::integral_constant<int, 4>;
-        using I8 = std::integral_constant<int, 8>;
-        if (nkv == 2) {
-            if (k == 2) go(I2(), I2()); else if (k == 4) go(I2(), I4()); else go(I2(), I8());
-        } else {
-            if (k == 2) go(I1(), I2()); else if (k == 4) go(I1(), I4()); else go(I1(), I8());
-        }
+        if (nkv == 2)
+            hipLaunchKernelGGL((gather_piece_kernel<2, 2>), g, b, 0, stream, a, lp);
+        else
+            hipLaunchKernelGGL((gather_piece_kernel<1, 2>), g, b, 0, stream, a, lp);
         return check_launch(who);
     }
     const Tiling tl = tiling_for(a.vecs, nkv, out_rows, true);

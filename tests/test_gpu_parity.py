@@ -288,6 +288,63 @@ def test_odd_row_sizes(shape, ps):
     pair.assert_pools_equal()
 
 
+@pytest.mark.parametrize("shape,ps", [
+    (W.mla(3, 24, latent_dim=512), 8),        # 1 KiB latents: one-view pieces, one per row
+    (W.mla(2, 24, latent_dim=1024), 4),       # 2 KiB latents: one-view pieces, two per row
+    (W.mha(2, 8, 256, 24), 4),                # 4 KiB rows: four pieces per row and view
+    (W.mha(3, 4, 128, 24), 16),               # 1 KiB rows: gather pieces K and V of one row, tiled store
+])
+def test_row_piece_shapes(shape, ps):
+    """The row-piece kernels on the row shapes the workloads do not cover: latents of
+    whole KiB (one view), 4 KiB rows, 1 KiB MHA rows; stores, gathers (full and
+    windowed, ragged) and a move, against the oracle byte for byte."""
+    pair = Pair([shape], ps)
+    P = shape.num_pages
+    slots = W.live_slots(5, P, ps, min(70, (P - 1) * ps))
+    _store_all_layers(pair, 0, slots, 4500)
+    pair.assert_pools_equal()
+    g = np.random.default_rng(2)
+    lens = np.array([1, ps, 2 * ps + 1, 0, 5 * ps - 1, 3], dtype=np.int32)
+    pages = [g.integers(1, P, size=max(1, -(-int(n) // ps))).astype(np.int32) for n in lens]
+    _gather_all_layers(pair, 0, pages, lens, [0, ps + 1, 0][: shape.layer_num])
+    mv = W.live_slots(9, P, ps, 24, sub=9)
+    src, _ = pair.orc.translate(0, mv[:12])
+    dst, _ = pair.orc.translate(0, mv[12:])
+    U.ukv_move_kv(pair.gpu, 0, to_dev(dst), to_dev(src), 0, shape.layer_num)
+    pair.orc.move(0, dst, src, 0, shape.layer_num)
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    pair.assert_pools_equal()
+
+
+# (entries, layers) -> pieces per wave on 256 CUs: 1 (small), 2, 4, 8 (a ragged last wave
+# in each layer), 1 (more than eight rounds of resident waves)
+@pytest.mark.parametrize("n,layers", [(256, 1), (101, 32), (256, 32), (401, 32), (1500, 32), (40, 32)])
+def test_store_pieces_per_wave(n, layers):
+    """Fused stores whose size gives each wave 1, 2, 4 or 8 pieces (a small launch is
+    packed into one round of resident waves), with tombstones and a bad id among the
+    entries: byte for byte against the oracle, flags too."""
+    P, ps = 160, 16
+    shape = W.mha(32, 8, 128, P)
+    pair = Pair([shape], ps)
+    rb = pair.rb(0)
+    slots = W.live_slots(n, P, ps, n).copy()
+    slots[::37] = -1  # tombstones
+    ids, _ = pair.orc.translate(0, slots)
+    ids = ids.copy()
+    ids[5] = 3  # not on a page's first block: skipped and flagged
+    k = bf16_rows(6000 + n, layers * n, rb)
+    v = bf16_rows(7000 + n, layers * n, rb)
+    U.ukv_store_kv_layers(pair.gpu, 0, 32 - layers, layers, to_dev(ids), rows_dev(k).view(layers, n, -1),
+                          rows_dev(v).view(layers, n, -1))
+    flags = set()
+    for i in range(layers):
+        l = 32 - layers + i
+        flags |= pair.orc.store(0, l, ids, k[i * n:(i + 1) * n], v[i * n:(i + 1) * n])
+        pair.record_store(0, l, ids, k[i * n:(i + 1) * n], v[i * n:(i + 1) * n])
+    assert U.ukv_pool_error_flags(pair.gpu) == flags == {"bad_id"}
+    pair.assert_pools_equal()
+
+
 def test_strided_and_misaligned_sources():
     pair = Pair([W.mha(4, 2, 64, 20)], 8)
     rb = pair.rb(0)
