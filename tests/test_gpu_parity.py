@@ -331,7 +331,7 @@ def test_store_pieces_per_wave(n, layers):
     slots[::37] = -1  # tombstones
     ids, _ = pair.orc.translate(0, slots)
     ids = ids.copy()
-    ids[5] = 3  # not on a page's first block: skipped and flagged
+    ids[5] = 2 * ps + 3  # on page 0's third block, not its first: skipped and flagged
     k = bf16_rows(6000 + n, layers * n, rb)
     v = bf16_rows(7000 + n, layers * n, rb)
     U.ukv_store_kv_layers(pair.gpu, 0, 32 - layers, layers, to_dev(ids), rows_dev(k).view(layers, n, -1),
