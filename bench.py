@@ -95,6 +95,11 @@ LIB_KERNELS = ("store_kernel", "store_piece_kernel", "gather_kernel", "gather_pi
                "validate_mark_kernel", "validate_check_kernel", "translate_inplace_kernel")
 
 
+# The attention entry points: one call is the split kernel, then the kernel that merges its
+# partials; bench.py's HIP events bracket the call, so its roofline time holds both.
+ROOFLINE_MERGE_KERNEL = {"attn_chunk": "attn_combine_kernel", "mla_attn_span": "mla_attn_combine_kernel"}
+
+
 def profile_commands(workload: str, out: str = "$OUT") -> Dict[str, str]:
     """The three profiler runs one summary needs (run from /tmp with TMPDIR=/tmp; $R is the
     repository root, $OUT a directory for rocprofv3's CSV files): a kernel trace, then one
@@ -188,6 +193,15 @@ def rocprof_summary(directory: str, workload: str, out_dir: str = PROFILE_DIR) -
     lines += ["", f"Roofline dispatches: {len(sel)} of {len(trace)} {kernel} dispatches"
               + (f" (the largest grid, {gmax} work-items; the smaller ones are another launch kind)"
                  if script.roofline_largest_grid else "") + f", average {roof_avg / 1e3:.1f} us"]
+    merge = ROOFLINE_MERGE_KERNEL.get(kernel)
+    if merge:  # the attention entry points launch the split kernel, then a merge kernel
+        md = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+              for r in rows(os.path.join(directory, "trace", "run_kernel_trace.csv"))
+              if re.search(r"(^|::|\s)" + merge + r"\b", r["Kernel_Name"])]
+        if md:
+            m_avg = sum(md) / len(md)
+            lines.append(f"Each call also launches its merge kernel ({merge}): average {m_avg / 1e3:.1f} us; "
+                         f"both kernels {(roof_avg + m_avg) / 1e3:.1f} us per call, the interval bench.py's events bracket")
     if bench_line:
         rl = bench_line["roofline"]
         lines += [f"Same run, bench.py's HIP events around every roofline launch: {rl['ms_per_launch'] * 1e3:.1f} us "

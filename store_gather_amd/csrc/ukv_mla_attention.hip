@@ -32,14 +32,18 @@
 //    same b % 8), so the latent rows they share are read once into that
 //    XCD's L2.
 //  - per 16 positions, S^T = C Q^T on v_mfma_f32_16x16x32_bf16 (18 k-steps
-//    over 576): the latent rows are the A operand straight from HBM (lane l
-//    loads 16 bytes of position l % 16), the 16 heads' queries the B
-//    operand, so lane l ends with the scores of positions 4 (l / 16) + i for
-//    head l % 16 -- the weights of those four positions are then already
+//    over 576): the latent rows are the A operand, the 16 heads' queries the
+//    B operand, so lane l ends with the scores of positions 4 (l / 16) + i
+//    for head l % 16 -- the weights of those four positions are then already
 //    where the P V product wants them, with no exchange between lanes.
-//  - the rows' first 512 elements also go to LDS (row-major), and the value
-//    operand comes out of LDS through the gfx950 transposing read
-//    ds_read_b64_tr_b16: four positions of one dim per lane per read.
+//  - the rows are not loaded in that operand layout (16 rows x 64 bytes per
+//    load, which holds a plain read of the view to about 65% of HBM
+//    bandwidth): each wave loads its half of the rows' first 512 elements two
+//    rows per load (whole 128-byte lines), with the streaming hint, and stages
+//    them in LDS (row-major); the A operand of the score product comes back
+//    from LDS, and the value operand through the gfx950 transposing read
+//    ds_read_b64_tr_b16 (four positions of one dim per lane per read).  Only
+//    the small rotary chunk is loaded in the operand layout.
 //  - each weight p enters the product as two bf16 parts, bf16(p) and
 //    bf16(p - bf16(p)), so the weights keep about 16 significant bits
 //    (relative error <= 2^-16): one K = 32 product per 16 value dims takes
@@ -54,12 +58,14 @@
 //    its 256 value dims and 32 of the rotary dims, computes the partial
 //    scores over them, and the two add each other's partials through LDS
 //    (the same sum, bit for bit, in both), then each multiplies the weights
-//    into its own 256 value dims.  Per wave: 16 x 256 fp32 sums and one
-//    9-chunk row buffer, ~200 registers, so two waves per SIMD; the queries
+//    into its own 256 value dims.  Per wave: 16 x 256 fp32 sums and two
+//    9-chunk row buffers, ~230 registers, so two waves per SIMD; the queries
 //    sit in LDS once for both.
-//  - once a tile has been staged and its scores taken, the next tile's rows
-//    go out into the same registers and stay in flight during the value
-//    product; block-table entries are read a tile ahead of their rows.
+//  - two tiles' rows in flight per wave, in two register buffers: once tile
+//    t has been staged and its scores taken, the rows of tile t + 2 go out
+//    into its buffer; block-table entries are read two tiles ahead of their
+//    rows.  Every load is issued on every path, so the compiler's count of
+//    loads in flight is exact and each wait is for one tile's rows only.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -140,6 +146,10 @@ __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t v, int lane) {
 }
 
 __device__ __forceinline__ u32x4 load16(const uint8_t *p) { return *(const u32x4 *)p; }
+// A latent row's bytes: read once per launch, with the streaming hint.
+__device__ __forceinline__ u32x4 load16_nt(const uint8_t *p) {
+    return __builtin_nontemporal_load((const u32x4 *)p);
+}
 
 // e is a multiple of bpp: floor(e / bpp) by a double reciprocal is off by at
 // most one for e < 2^31, fixed by one correction step.
@@ -163,7 +173,7 @@ constexpr int kQPitch = kLatent * 2 + 16;
 // 288 dims, and the two waves add each other's partials through LDS; both
 // then hold the same scores and take the same softmax decisions, and each
 // multiplies the weights into its own 256 value dims.  Per wave: 16 x 256
-// fp32 sums (64 registers) and one 9-chunk row buffer -- two waves per
+// fp32 sums (64 registers) and two 9-chunk row buffers -- two waves per
 // SIMD.
 template <int KS, int NB>
 __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_attn_span_kernel(MlaArgs a) {
@@ -242,7 +252,7 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     // positions 4 grp .. 4 grp + 3 (nb in this wave's blocks)
     const int tr_off = (4 * grp + col / 4) * kPitch + 8 * (col % 4) + 32 * VH * half;
 
-    u32x4 k0[KH];
+    u32x4 kA[KH], kB[KH];
     int64_t cur = start;
     while (cur < end) {
         r = __builtin_amdgcn_readfirstlane(r);
@@ -296,54 +306,89 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
             }
             return p;
         };
-        // table entry of a position (a load), -1 past the table; nothing past the segment
+        // table entry of a position, raw: read by every lane (at the row's last
+        // column when past it), so that every tile issues the same loads and the
+        // compiler's count of loads in flight is exact on every path; row_of
+        // makes the range checks, where the value is first used (a check here
+        // would wait for this load, the newest, and with it for every row load
+        // before it).
         auto entry = [&](const Pos &p) -> int32_t {
-            return (p.j < pend && (int64_t)p.col < a.bt_stride) ? bt_row[p.col] : -1;
+            return bt_row[(int64_t)p.col < a.bt_stride ? (int64_t)p.col : a.bt_stride - 1];
         };
         bool bad = false;
         auto row_of = [&](const Pos &p, int32_t e) -> int32_t {
             if (p.j >= pend) return -1;
-            if (e < 0 || e >= entry_lim || !multiple_of(e, (int32_t)a.bpp, a.inv_bpp)) {
+            if ((int64_t)p.col >= a.bt_stride || e < 0 || e >= entry_lim ||
+                !multiple_of(e, (int32_t)a.bpp, a.inv_bpp)) {
                 bad = true;
                 return -1;
             }
             return e * (int32_t)ps + (int32_t)p.off;  // < n_rows < 2^31
         };
-        // the wave's chunks of a tile's rows, loaded unconditionally (a position
+        // The wave's share of a tile's rows, loaded unconditionally (a position
         // past the segment reads row 0; its scores are masked and its values
-        // zeroed in LDS)
-        auto load_tile = [&](u32x4 (&k)[KH], int32_t row) {
-            const uint8_t *p = view + (uint64_t)(uint32_t)(row < 0 ? 0 : row) * a.row_bytes + 16 * grp;
-#pragma unroll
-            for (int j = 0; j < KH; ++j) k[j] = load16(p + 64 * chunk(j));
+        // zeroed in LDS).  k[0..7]: its 512-byte value half of all 16 rows, two
+        // rows per load (lane l: row of position 2 i + l / 32, 16 bytes at
+        // 512 half + 16 (l % 32)), so that each load reads whole 128-byte lines
+        // -- reading the rows in the matrix cores' operand layout instead (16
+        // rows x 64 bytes per load) holds a plain read of this layer view to
+        // about 65% of HBM bandwidth, against 75-79% this way.  The rows of the
+        // other positions come from the lanes that computed them.  k[8]: its
+        // half of the rotary chunk, in the operand layout (lane (grp, col):
+        // position col, 16 bytes at 1024 + 64 half + 16 grp).
+        auto row_at = [&](int32_t row, int i) {  // row of position 2 i + lane / 32
+            const int32_t ra = __builtin_amdgcn_readlane(row, 2 * i);
+            const int32_t rb = __builtin_amdgcn_readlane(row, 2 * i + 1);
+            return lane < 32 ? ra : rb;
         };
-        // this wave's partial scores, then the other wave's added (through LDS, by tile parity)
+        auto load_tile = [&](u32x4 (&k)[KH], int32_t row) {
+            const int32_t rr = row < 0 ? 0 : row;
+            const uint8_t *vp = view + 512 * half + 16 * (lane & 31);
+#pragma unroll
+            for (int i = 0; i < KH - 1; ++i) k[i] = load16_nt(vp + (uint64_t)(uint32_t)row_at(rr, i) * a.row_bytes);
+            k[KH - 1] = load16_nt(view + (uint64_t)(uint32_t)rr * a.row_bytes + 16 * grp + 64 * chunk(KH - 1));
+        };
+        // the value half into LDS (row-major, this wave's columns only); rows past
+        // the segment stage zeros
+        auto stage = [&](const u32x4 (&k)[KH], int32_t row, int32_t t) {
+            uint8_t *st = lds + (lane >> 5) * kPitch + 512 * half + 16 * (lane & 31);
+            if (pbeg + (t + 1) * kTile <= pend) {  // every position of the tile is in the segment (uniform)
+#pragma unroll
+                for (int i = 0; i < KH - 1; ++i) *(u32x4 *)(st + 2 * i * kPitch) = k[i];
+            } else {  // the segment's last tile
+#pragma unroll
+                for (int i = 0; i < KH - 1; ++i)
+                    *(u32x4 *)(st + 2 * i * kPitch) = row_at(row, i) >= 0 ? k[i] : u32x4{0, 0, 0, 0};
+            }
+        };
+        // this wave's partial scores, then the other wave's added (through LDS, by
+        // tile parity).  The value chunks' operands come back from the wave's own
+        // LDS columns (LDS runs a wave's operations in order, and the compiler
+        // may not move the reads above the writes of the same array).
         auto scores = [&](const u32x4 (&k)[KH], int32_t t) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            const uint8_t *ap = lds + col * kPitch + 512 * half + 16 * grp;
+            // three accumulators: chains of three dependent products instead of nine
+            f32x4 part[3] = {};
 #pragma unroll
             for (int j = 0; j < KH; ++j)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, k[j]), __builtin_bit_cast(bf16x8, load16(qsrc + 64 * chunk(j))), acc, 0,
-                    0, 0);
+                part[j % 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, j < KH - 1 ? load16(ap + 64 * j) : k[KH - 1]),
+                    __builtin_bit_cast(bf16x8, load16(qsrc + 64 * chunk(j))), part[j % 3], 0, 0, 0);
+            const f32x4 acc = (part[0] + part[1]) + part[2];
             xch[t & 1][half][lane] = acc;
             __syncthreads();
             const f32x4 other = xch[t & 1][1 - half][lane];
             return half == 0 ? acc + other : other + acc;  // the same sum, bit for bit, in both waves
         };
-        auto stage = [&](const u32x4 (&k)[KH], bool valid, int32_t t) {
-            uint8_t *st = lds + col * kPitch + 16 * grp + 512 * half;
-            if (pbeg + (t + 1) * kTile <= pend) {  // every position of the tile is in the segment (uniform)
-#pragma unroll
-                for (int j = 0; j < KH - 1; ++j) *(u32x4 *)(st + 64 * j) = k[j];
-            } else {  // the segment's last tile: positions past its end stage zeros
-#pragma unroll
-                for (int j = 0; j < KH - 1; ++j) *(u32x4 *)(st + 64 * j) = valid ? k[j] : u32x4{0, 0, 0, 0};
-            }
-        };
-        // One pass over the segment, one tile at a time: once tile t has been
-        // staged and its scores taken, the rows of tile t + 1 go out into the
-        // same registers and stay in flight during the value product.  Table
-        // entries are read a tile ahead of their rows' loads.  The weights are 2^(x - ref) for a fixed reference ref,
+        // One pass over the segment, one tile at a time, with two tiles' rows
+        // in flight: the rows of tiles t and t + 1 sit in two register buffers
+        // (kA for even tiles, kB for odd ones); once tile t has been staged and
+        // its scores taken, the rows of tile t + 2 go out into its buffer and
+        // stay in flight through the value product of tile t and the staging,
+        // scores and value product of tile t + 1.  Table entries are read two
+        // tiles ahead of their rows' loads and issued after the previous
+        // tile's rows, so the wait for an entry is never a wait for rows
+        // issued after it (loads complete in order).  The weights are 2^(x - ref) for a fixed reference ref,
         // so the sums are never rescaled (they stay in the matrix cores'
         // accumulators):
         //   MODE 0: ref = the first tile's max score; returns false (sums
@@ -361,32 +406,43 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
             Pos q0 = {pbeg + col, 0u, 0u};
             q0.col = (uint32_t)q0.j / ps;
             q0.off = (uint32_t)q0.j - q0.col * ps;
-            const int32_t e0 = entry(q0);
-            Pos qn = advance(q0);
-            int32_t en = entry(qn);
-            const int32_t row0 = row_of(q0, e0);
+            const Pos q1 = advance(q0);
+            const int32_t e0 = entry(q0), e1 = entry(q1);
+            Pos qa = advance(q1);  // tile 2, then every even tile two ahead of the one in kA
+            Pos qb = advance(qa);  // tile 3, then every odd tile two ahead of the one in kB
+            const int32_t row0 = row_of(q0, e0), row1 = row_of(q1, e1);
             if (__any(bad)) return true;
-            load_tile(k0, row0);
-            bool va = row0 >= 0;
+            // the order of every later tile: rows, then the entry two tiles on
+            load_tile(kA, row0);
+            int32_t ea = entry(qa);
+            load_tile(kB, row1);  // row 0 when the segment has one tile
+            int32_t eb = entry(qb);
+            int32_t va = row0, vb = row1;  // the rows in kA and kB (-1: past the segment)
             // scores of tile t -> weights, row sums and P V; false: the reference was outgrown
             auto tile_math = [&](const f32x4 &sc, int32_t t) -> bool {
                 const int32_t p0 = pbeg + t * kTile + 4 * grp;
                 float x[4];
-                float tmax = -INFINITY;
+                float lmax = -INFINITY;  // over this lane's four positions
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     x[i] = p0 + i < pend ? sc[i] * a.scale_log2 : -INFINITY;
-                    tmax = fmaxf(tmax, x[i]);
+                    lmax = fmaxf(lmax, x[i]);
                 }
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                // The lanes of one head (same col) hold the same reference, so a
+                // score outgrows it exactly when some lane's own max does: only
+                // the first tile needs the tile's max over the four lane groups,
+                // and the max-first pass reduces its per-lane maxima once at its end.
                 if constexpr (MODE == 2) {
-                    m_run = fmaxf(m_run, tmax);
+                    m_run = fmaxf(m_run, lmax);
                     return true;
                 } else {
                     if constexpr (MODE == 0) {
-                        if (t == 0) m_run = tmax;
-                        if (__any(tmax > m_run + kGrowGap)) return false;
+                        if (t == 0) {
+                            float tmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+                            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                            m_run = tmax;
+                        }
+                        if (__any(lmax > m_run + kGrowGap)) return false;
                     }
                     s16x4 whi, wlo;
 #pragma unroll
@@ -416,24 +472,48 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
                     return true;
                 }
             };
-            for (int32_t t = 0; t < tiles; ++t) {
-                if constexpr (MODE != 2) stage(k0, va, t);
-                const f32x4 sa = scores(k0, t);
-                const int32_t rown = row_of(qn, en);
-                if (__any(bad)) return true;
-                qn = advance(qn);
-                en = entry(qn);
-                if (t + 1 < tiles) load_tile(k0, rown);
-                va = rown >= 0;
-                if (!tile_math(sa, t)) return false;
+            // tile t from buffer k (its rows v); then the rows of tile t + 2 from (q, e) into k
+            // and the entry of tile t + 4 into e.  Both loads are issued on every path (row 0
+            // past the segment's last tile or for a bad entry), the check for a bad entry after
+            // them: a path that skipped them would join the others with fewer loads in flight,
+            // and the compiler would then wait for every load at each entry's use.  Every
+            // mode stages the tile: the scores read it back.
+            auto step = [&](u32x4 (&k)[KH], int32_t &v, Pos &q, int32_t &e, int32_t t) -> int {
+                stage(k, v, t);
+                const f32x4 sc = scores(k, t);
+                const int32_t rown = row_of(q, e);
+                q = advance(advance(q));
+                load_tile(k, rown);
+                e = entry(q);
+                v = rown;
+                if (__any(bad)) return 1;
+                return tile_math(sc, t) ? 0 : 2;
+            };
+            // Tiles in pairs, with no way out of the loop but its end: the compiler
+            // makes every loop single-exit, so an exit between the two steps would
+            // join the way back to the loop's head with fewer loads in flight.  Both
+            // steps always run (after a bad entry or an outgrown reference the
+            // second one's sums are discarded with the first's), so the loads in
+            // flight at the head are always [rows t, entry t + 2, rows t + 1,
+            // entry t + 3].  An odd last tile follows from kA.
+            int st = 0;
+            int32_t t = 0;
+            for (; t + 1 < tiles; t += 2) {
+                const int sa = step(kA, va, qa, ea, t);
+                const int sb = step(kB, vb, qb, eb, t + 1);
+                st = sa != 0 ? sa : sb;
+                if (st != 0) break;
             }
-            return true;
+            if (st == 0 && t < tiles) st = step(kA, va, qa, ea, t);
+            return st != 2;
         };
         if (!pass(std::integral_constant<int, 0>())) {
             // a score outgrew the first tile's by more than 2^kGrowGap: the
             // segment's max first, then the sums against it
             m_run = -INFINITY;
             pass(std::integral_constant<int, 2>());
+            m_run = fmaxf(m_run, __shfl_xor(m_run, 16));  // the head's max over the four lane groups
+            m_run = fmaxf(m_run, __shfl_xor(m_run, 32));
             if (!__any(bad)) pass(std::integral_constant<int, 1>());
         }
         const bool seg_bad = __any(bad);
