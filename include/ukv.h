@@ -221,8 +221,12 @@ int ukv_translate_loc(const ukv_pool *pool, int32_t sub, const int64_t *slots_de
  * k_dev, v_dev: rows of row_bytes at k_dev + i * src_row_stride_bytes
  *   (src_row_stride_bytes >= row_bytes).  MLA: k_dev is the latent, v_dev
  *   must be NULL.
- * Id 0 is the sink row: tombstoned entries all write it and race (any of
- * them may win, per 4-byte word).  Repeated live ids race the same way.
+ * Id 0 is the sink row: tombstoned entries all write it and race.  Each
+ * chunk of the copy's vector width comes whole from one of them: the width
+ * is the largest of 16, 8, 4, 2 and 1 bytes that divides row_bytes, the K and
+ * V views' byte offsets, the pool's, k_dev's and v_dev's addresses and the
+ * source strides (16 bytes for 16-byte aligned rows).  Repeated live ids
+ * race the same way.
  */
 int ukv_store_kv(const ukv_pool *pool, int32_t sub, int32_t layer, const int32_t *ids_dev, int64_t n,
                  const void *k_dev, const void *v_dev, int64_t src_row_stride_bytes, hipStream_t stream);

@@ -2,7 +2,6 @@
 identical pre-filled bytes, and the byte comparison with the sink-row rule."""
 from __future__ import annotations
 
-import math
 import sys
 from typing import Dict, List, Optional, Sequence
 
@@ -50,34 +49,55 @@ class Pair:
     def kvs(self, sub: int) -> int:
         return 2 if self.shapes[sub].kind == W.MHA else 1
 
-    def record_store(self, sub: int, layer: int, ids: np.ndarray, k: np.ndarray, v: Optional[np.ndarray]) -> None:
-        """Remember the rows a store sends to the sink row (id 0) of each view."""
+    def record_store(self, sub: int, layer: int, ids: np.ndarray, k: np.ndarray, v: Optional[np.ndarray],
+                     unit: Optional[int] = None) -> None:
+        """Remember the rows a store sends to the sink row (id 0) of each view, and the unit
+        each of them writes whole: the store's vector width, by the rule include/ukv.h states
+        for ukv_store_kv.  The default takes 16-byte aligned sources with rows back to back
+        (what rows_dev gives); a test with other sources passes the width its call gets."""
         at = np.nonzero(np.asarray(ids) == 0)[0]
+        rb = self.rb(sub)
+        bases = [self.orc.view_base(sub, layer, kv) for kv in range(self.kvs(sub))]
+        if unit is None:
+            unit = copy_unit(rb, *bases)
         for kv, rows in enumerate((k, v)[: self.kvs(sub)]):
             key = (sub, layer, kv)
             if at.size:
-                self.sink[key] = [rows[i] for i in at]
+                self.sink[key] = (unit, [rows[i] for i in at])
 
     def assert_pools_equal(self) -> None:
         got = self.gpu.raw.cpu().numpy()
         assert_bytes_equal_with_sinks(got, self.orc, self.sink)
 
 
-def assert_bytes_equal_with_sinks(got: np.ndarray, orc: oracle.OraclePool, sink: Dict[tuple, List[np.ndarray]]):
+def copy_unit(*values: int) -> int:
+    """The largest of 16, 8, 4, 2, 1 bytes dividing every value: the vector width a store
+    copies in for these row bytes, view offsets, addresses and strides."""
+    u = 16
+    for v in values:
+        while u > 1 and int(v) % u:
+            u //= 2
+    return u
+
+
+def assert_bytes_equal_with_sinks(got: np.ndarray, orc: oracle.OraclePool, sink: Dict[tuple, tuple]):
+    """Every byte equal to the oracle's, except on the sink rows of `sink` ((sub, layer, kv) ->
+    (unit, tombstoned source rows)): racing stores leave each `unit`-byte chunk of a sink row
+    whole from one of its tombstoned rows (the one rule the library promises there)."""
     exp = orc.raw
     assert got.shape == exp.shape
     diff = got != exp
     if not diff.any():
         return
-    for (sub, layer, kv), cands in sink.items():
+    for (sub, layer, kv), (unit, cands) in sink.items():
         rb = orc.row_bytes(sub)
+        assert rb % unit == 0
         off = orc.view_base(sub, layer, kv)  # row 0 of the view: the sink row
-        g = math.gcd(rb, 4)
-        dt = {1: np.uint8, 2: np.uint16, 4: np.uint32}[g]
-        seg = got[off: off + rb].view(dt)
-        c = np.stack([np.asarray(x, dtype=np.uint8).view(dt) for x in cands])
-        ok = (c == seg[None, :]).any(axis=0)
-        assert ok.all(), f"sink row of {(sub, layer, kv)}: word {np.nonzero(~ok)[0][:8]} from no tombstoned row"
+        seg = got[off: off + rb].reshape(-1, unit)
+        c = np.stack([np.asarray(x, dtype=np.uint8).reshape(-1, unit) for x in cands])
+        ok = (c == seg[None]).all(axis=2).any(axis=0)
+        assert ok.all(), (f"sink row of {(sub, layer, kv)}: {unit}-byte chunks {np.nonzero(~ok)[0][:8]} "
+                          "whole from no tombstoned row")
         diff[off: off + rb] = False
     bad = np.nonzero(diff)[0]
     assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]} (of {got.size})"

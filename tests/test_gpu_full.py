@@ -9,8 +9,8 @@ device the test then checks
   * every gathered row against the envelope row at the oracle's address,
   * every byte nothing may write against the pre-fill pattern, regenerated
     from its definition (SplitMix64 over 8-byte words) chunk by chunk,
-  * the sink rows with the tombstone rule (each 4-byte word from one of the
-    tombstoned entries of that call).
+  * the sink rows with the tombstone rule (each chunk of the store's vector
+    width, 16 bytes here, whole from one of the tombstoned entries of that call).
 Every output row of every layer is compared; nothing is sampled.
 """
 import numpy as np
@@ -20,8 +20,8 @@ import torch
 import oracle
 import store_gather_amd as U
 import ukv_workloads as W
-from parity_util import (assert_bytes_are_pattern, assert_rows_subset, equal_rows_chunked, log, offsets_to_rows,
-                         ospecs, pattern_mismatch_rows, round8, rows_view)
+from parity_util import (assert_bytes_are_pattern, assert_rows_subset, copy_unit, equal_rows_chunked, log,
+                         offsets_to_rows, ospecs, pattern_mismatch_rows, round8, rows_view)
 
 pytestmark = pytest.mark.gpu
 SEED = 21
@@ -92,9 +92,13 @@ def _store_layers(pool, orc, sub, ids_d, ids, slots, masks, value_seed):
             masks[sub][r] = True
             assert equal_rows_chunked(rows, r[live], src[h], live), f"layer {layer} kv {h}: stored rows"
             if tomb.numel():
-                sink = rows[int(r[tomb[0]])].view(torch.int32)
-                cand = src[h].index_select(0, tomb).view(tomb.numel(), -1, 4).view(torch.int32).squeeze(-1)
-                assert bool((cand == sink.unsqueeze(0)).any(dim=0).all()), f"layer {layer} kv {h}: sink row"
+                # each chunk of the store's vector width whole from one tombstoned row
+                unit = copy_unit(rb, *[orc.view_base(sub, layer, x) for x in range(nkv)],
+                                 *[t.data_ptr() for t in src])
+                sink = rows[int(r[tomb[0]])].view(-1, unit)
+                cand = src[h].index_select(0, tomb).view(tomb.numel(), -1, unit)
+                ok = (cand == sink.unsqueeze(0)).all(dim=2).any(dim=0)
+                assert bool(ok.all()), f"layer {layer} kv {h}: sink row ({unit}-byte chunks)"
     torch.cuda.synchronize()
 
 

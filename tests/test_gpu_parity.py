@@ -2,8 +2,9 @@
 
 Integer / byte work, so the bar is bit-exact on every byte of the pool and of
 every output, with one documented exception: the sink row (id 0 of each view)
-that tombstoned store entries all write, where each 4-byte word must come from
-one of those entries' source rows.  Sizes here span several waves and blocks
+that tombstoned store entries all write, where each chunk of the store's vector
+width (16 bytes for aligned rows) must come whole from one of those entries'
+source rows.  Sizes here span several waves and blocks
 with ragged tails; the workload-sized cases are in test_gpu_full.py.
 """
 import numpy as np
