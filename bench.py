@@ -972,13 +972,18 @@ BAR = (
 
 def _launch_times(g, torch, ops, launches: int):
     """Per-launch milliseconds of ``ops`` run in order, cycled to at least ``launches``
-    launches (after two untimed ones), each between two HIP events on the current stream."""
+    launches, each between two HIP events on the current stream, right after an untimed
+    warm pass of the same launches (_warm_pass)."""
     seq = (ops * (-(-launches // len(ops))))[:max(launches, len(ops))]
     for op in seq[:2]:
         g.launch(op)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in seq]
+    warm = _warm_pass(seq)
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(spin_cycles_per_ms(torch) * (2.0 + 0.1 * len(seq))))  # queue ahead of the GPU
+    # a spin kernel holds the GPU while the host queues the warm and the timed launches
+    torch.cuda._sleep(int(spin_cycles_per_ms(torch) * (2.0 + 0.1 * (len(warm) + 2 * len(seq)))))
+    for op in warm:
+        g.launch(op)
     for op, (e0, e1) in zip(seq, evs):
         e0.record()
         g.launch(op)
@@ -1044,6 +1049,22 @@ def run_bar(torch, U, W, device, launches: int = 12) -> dict:
 
 
 _SPIN = {}
+
+
+WARM_MS = 15.0  # GPU time the untimed warm pass runs for, at least (see _warm_pass)
+
+
+def _warm_pass(seq) -> list:
+    """The untimed launches queued just ahead of a timed pass: ``seq`` repeated until it
+    moves about WARM_MS of work at 6.5 TB/s (1 to 100 times).  Started from an idle GPU, a
+    sequence of bandwidth-bound launches slows down for its first ~10 ms and then recovers
+    (the swa_decode full-layer gather, back to back: 725, 735, 752, 810, 846, 838, 827,
+    811, 803, 779, 761, 750 us per launch; the same launches after such a pass: 698-712
+    us), which looks like the GPU's power management reacting to the load; without the
+    pass, short sequences measured that transient, not the kernels."""
+    total = sum(op.nbytes for op in seq)
+    reps = int(min(100, max(1, -(-WARM_MS * 6.5e9 // max(total, 1)))))
+    return list(seq) * reps
 
 
 def spin_cycles_per_ms(torch) -> float:
@@ -1129,10 +1150,13 @@ def run_workload(name, args, torch, U, W, device) -> dict:
             g.launch(op)
         e0, e1 = mk(), mk()
         torch.cuda.synchronize()
-        # a spin kernel holds the GPU while the host queues the whole sequence, so the
-        # events bracket back-to-back kernels, not the host's launch rate (short
-        # kernels finish faster than Python issues them)
-        torch.cuda._sleep(int(spin * (2.0 + 0.1 * len(seq))))
+        # a spin kernel holds the GPU while the host queues the warm pass and the
+        # timed sequence, so the events bracket back-to-back kernels, not the host's
+        # launch rate (short kernels finish faster than Python issues them)
+        warm = _warm_pass(seq)
+        torch.cuda._sleep(int(spin * (2.0 + 0.1 * (len(warm) + len(seq)))))
+        for op in warm:
+            g.launch(op)
         e0.record()
         for op in seq:
             g.launch(op)
