@@ -88,7 +88,7 @@ def traffic_from_profile(workload: str, kernel: str, profile_dir: str = None):
 # ----------------------------------------------------------------------------
 
 # The library's kernels, as they appear in rocprofv3's kernel names.
-LIB_KERNELS = ("store_kernel", "store_piece_kernel", "gather_kernel", "gather_piece_kernel", "move_kernel",
+LIB_KERNELS = ("store_kernel", "store_piece_kernel", "store_group_kernel", "gather_kernel", "gather_piece_kernel", "move_kernel",
                "move_piece_kernel", "translate_slots_kernel", "translate_pages_kernel", "move_pages_kernel",
                "remap_pages_kernel", "evict_window_kernel", "build_page_table_kernel", "attn_chunk_kernel",
                "attn_combine_kernel", "mla_attn_span_kernel", "mla_attn_combine_kernel", "flags_fetch_clear_kernel",
@@ -122,8 +122,9 @@ def _is_lib_kernel(name: str) -> bool:
 
 def _matches(name: str, kernel: str) -> bool:
     """Kernel names of one launch kind: `kernel` is the short name (store, gather, move,
-    move_pages, attn_chunk, mla_attn_span); both the row-piece and the tile kernels count."""
-    return re.search(r"(^|::|\s)" + kernel + r"(_piece)?_kernel\b", name) is not None
+    move_pages, attn_chunk, mla_attn_span); the row-piece, row-group and tile kernels all
+    count."""
+    return re.search(r"(^|::|\s)" + kernel + r"(_piece|_group)?_kernel\b", name) is not None
 
 
 def _grid(row: dict, keys) -> int:

@@ -317,6 +317,50 @@ def test_row_piece_shapes(shape, ps):
     pair.assert_pools_equal()
 
 
+@pytest.mark.parametrize("shape,n", [
+    (W.mla(4, 40, latent_dim=576), 203),      # 1,152-byte latents: 9 loads per lane, one view
+    (W.mla(3, 40, latent_dim=640), 64),       # 1,280 bytes: 10 loads
+    (W.mha(3, 9, 64, 40), 77),                # 1,152-byte MHA rows: K and V groups
+    (W.mha(2, 12, 64, 40), 8),                # 1,536 bytes: 12 loads, one whole group
+    (W.mha(2, 15, 64, 40), 131),              # 1,920 bytes: 15 loads
+])
+def test_store_group_shapes(shape, n):
+    """The row-group store (rows of 1,152 to 1,920 bytes, eight entries of one view per
+    wave) on ragged entry counts, with tombstones and a bad id among the entries, one
+    layer at a time and fused over the layers: byte for byte against the oracle, flags
+    too."""
+    ps = 16
+    pair = Pair([shape], ps)
+    rb = pair.rb(0)
+    assert 1024 < rb < 2048 and rb % 128 == 0
+    L = shape.layer_num
+    nkv = pair.kvs(0)
+    slots = W.live_slots(n + 3, shape.num_pages, ps, n).copy()
+    slots[::11] = -1  # tombstones
+    ids, _ = pair.orc.translate(0, slots)
+    ids = ids.copy()
+    ids[min(6, n - 1)] = ps + 1  # on page 0's second block: skipped and flagged
+    for layer in range(L):  # one layer per launch
+        k = bf16_rows(8100 + layer, n, rb)
+        v = bf16_rows(8200 + layer, n, rb) if nkv == 2 else None
+        U.ukv_store_kv(pair.gpu, 0, layer, to_dev(ids), rows_dev(k), None if v is None else rows_dev(v))
+        assert pair.orc.store(0, layer, ids, k, v) == {"bad_id"}
+        pair.record_store(0, layer, ids, k, v)
+    assert U.ukv_pool_error_flags(pair.gpu) == {"bad_id"}
+    pair.assert_pools_equal()
+    k = bf16_rows(8300, L * n, rb)  # all layers in one launch, new values
+    v = bf16_rows(8400, L * n, rb) if nkv == 2 else None
+    U.ukv_store_kv_layers(pair.gpu, 0, 0, L, to_dev(ids), rows_dev(k).view(L, n, -1),
+                          None if v is None else rows_dev(v).view(L, n, -1))
+    for layer in range(L):
+        kl = k[layer * n:(layer + 1) * n]
+        vl = None if v is None else v[layer * n:(layer + 1) * n]
+        assert pair.orc.store(0, layer, ids, kl, vl) == {"bad_id"}
+        pair.record_store(0, layer, ids, kl, vl)
+    assert U.ukv_pool_error_flags(pair.gpu) == {"bad_id"}
+    pair.assert_pools_equal()
+
+
 # (entries, layers) -> pieces per wave on 256 CUs: 1 (small), 2, 4, 8 (a ragged last wave
 # in each layer), 1 (more than eight rounds of resident waves)
 @pytest.mark.parametrize("n,layers", [(256, 1), (101, 32), (256, 32), (401, 32), (1500, 32), (40, 32)])
