@@ -58,14 +58,17 @@
 //    its 256 value dims and 32 of the rotary dims, computes the partial
 //    scores over them, and the two add each other's partials through LDS
 //    (the same sum, bit for bit, in both), then each multiplies the weights
-//    into its own 256 value dims.  Per wave: 16 x 256 fp32 sums and two
-//    9-chunk row buffers, ~230 registers, so two waves per SIMD; the queries
-//    sit in LDS once for both.
-//  - two tiles' rows in flight per wave, in two register buffers: once tile
-//    t has been staged and its scores taken, the rows of tile t + 2 go out
-//    into its buffer; block-table entries are read two tiles ahead of their
-//    rows.  Every load is issued on every path, so the compiler's count of
-//    loads in flight is exact and each wait is for one tile's rows only.
+//    into its own 256 value dims.  Per wave: 16 x 256 fp32 sums, one 9-chunk
+//    row buffer and its 9 chunks of the 16 queries (the score product's B
+//    operand, loaded once per request), ~226 registers, so two waves per
+//    SIMD.  (Queries in LDS cost 9 KB of LDS reads per wave and tile: 229
+//    against 217 us per layer on the decode batch.)
+//  - once a tile has been staged and its scores taken, the next tile's rows
+//    go out into the same registers and stay in flight during the value
+//    product; block-table entries are read a tile ahead of their rows.  Every
+//    load is issued on every path, so the compiler's count of loads in
+//    flight is exact.  (A second row buffer, for two tiles in flight, took
+//    the registers the queries now hold, and was no faster.)
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -162,10 +165,8 @@ __device__ __forceinline__ bool multiple_of(int32_t e, int32_t bpp, double inv_b
 }
 
 // Row pitch of the LDS value tile: 512 bf16 plus 32 bytes, so that the
-// sixteen rows one transposing read touches spread over the banks; the
-// queries' rows (576 bf16) get 16 bytes for the same reason.
+// sixteen rows one transposing read touches spread over the banks.
 constexpr int kPitch = kValue * 2 + 32;
-constexpr int kQPitch = kLatent * 2 + 16;
 
 // A workgroup of two waves owns (span, head group).  Wave `half` loads the
 // row chunks s = 8 half .. 8 half + 7 (its 256 value dims) and s = 16 + half
@@ -173,8 +174,8 @@ constexpr int kQPitch = kLatent * 2 + 16;
 // 288 dims, and the two waves add each other's partials through LDS; both
 // then hold the same scores and take the same softmax decisions, and each
 // multiplies the weights into its own 256 value dims.  Per wave: 16 x 256
-// fp32 sums (64 registers) and two 9-chunk row buffers -- two waves per
-// SIMD.
+// fp32 sums (64 registers), one 9-chunk row buffer and the queries' 9 chunks
+// -- two waves per SIMD.
 template <int KS, int NB>
 __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_attn_span_kernel(MlaArgs a) {
     static_assert(KS * 32 == kLatent && NB * 16 == kValue && KS == NB / 2 + 2, "latent / value width");
@@ -182,7 +183,6 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     constexpr int VH = NB / 2;      // 16-dim value blocks per wave
     __shared__ __attribute__((aligned(16))) uint8_t lds[kTile * kPitch];
     __shared__ __attribute__((aligned(16))) f32x4 xch[2][2][kWave];  // partial scores by tile parity and wave
-    __shared__ __attribute__((aligned(16))) uint8_t qlds[kHeads * kQPitch];  // the request's 16 queries
     const int half = (int)(threadIdx.x / kWave);
     const int lane = lane_id();
     const int grp = lane >> 4;
@@ -242,7 +242,6 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
 
     // queries as the B operand, from LDS (one copy for both waves): column col
     // is head hg*16 + col, lane group grp reads dims [8 (4 s + grp), +8) at k-step s
-    const uint8_t *qsrc = qlds + col * kQPitch + 16 * grp;
     const uint8_t *view = a.pool + a.base;
     const uint32_t ps = a.ps;
     const uint32_t q16 = (uint32_t)kTile / ps, r16 = (uint32_t)kTile - q16 * ps;
@@ -252,7 +251,7 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
     // positions 4 grp .. 4 grp + 3 (nb in this wave's blocks)
     const int tr_off = (4 * grp + col / 4) * kPitch + 8 * (col % 4) + 32 * VH * half;
 
-    u32x4 kA[KH], kB[KH];
+    u32x4 kA[KH];
     int64_t cur = start;
     while (cur < end) {
         r = __builtin_amdgcn_readfirstlane(r);
@@ -277,14 +276,11 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int32_t pend = pbeg + (int32_t)seg;
         const int32_t tiles = (pend - pbeg + kTile - 1) / kTile;
         const int64_t slot = (int64_t)w + r;
-        {  // this request's 16 queries into LDS: 16 x 72 chunks of 16 bytes over both waves
-            const uint8_t *qg = (const uint8_t *)(a.q + ((int64_t)r * a.q_heads + hg * kHeads) * kLatent);
-            __syncthreads();  // the previous request's queries are no longer read
-            for (int c = (int)threadIdx.x; c < kHeads * (kLatent / 8); c += 2 * kWave) {
-                const int hq = c / (kLatent / 8), off = (c - hq * (kLatent / 8)) * 16;
-                *(u32x4 *)(qlds + hq * kQPitch + off) = load16(qg + (int64_t)hq * kLatent * 2 + off);
-            }
-            __syncthreads();
+        u32x4 qreg[KH];  // the score product's B operand: head col's dims of this wave's chunks
+        {
+            const uint8_t *qg = (const uint8_t *)(a.q + ((int64_t)r * a.q_heads + hg * kHeads + col) * kLatent) + 16 * grp;
+#pragma unroll
+            for (int j = 0; j < KH; ++j) qreg[j] = load16(qg + 64 * chunk(j));
         }
         f32x4 o[VH];
         float m_run = -INFINITY;  // the weights' reference (log2 units) of head col
@@ -373,22 +369,17 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
             for (int j = 0; j < KH; ++j)
                 part[j % 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8, j < KH - 1 ? load16(ap + 64 * j) : k[KH - 1]),
-                    __builtin_bit_cast(bf16x8, load16(qsrc + 64 * chunk(j))), part[j % 3], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, qreg[j]), part[j % 3], 0, 0, 0);
             const f32x4 acc = (part[0] + part[1]) + part[2];
             xch[t & 1][half][lane] = acc;
             __syncthreads();
             const f32x4 other = xch[t & 1][1 - half][lane];
             return half == 0 ? acc + other : other + acc;  // the same sum, bit for bit, in both waves
         };
-        // One pass over the segment, one tile at a time, with two tiles' rows
-        // in flight: the rows of tiles t and t + 1 sit in two register buffers
-        // (kA for even tiles, kB for odd ones); once tile t has been staged and
-        // its scores taken, the rows of tile t + 2 go out into its buffer and
-        // stay in flight through the value product of tile t and the staging,
-        // scores and value product of tile t + 1.  Table entries are read two
-        // tiles ahead of their rows' loads and issued after the previous
-        // tile's rows, so the wait for an entry is never a wait for rows
-        // issued after it (loads complete in order).  The weights are 2^(x - ref) for a fixed reference ref,
+        // One pass over the segment, one tile at a time: once tile t has been
+        // staged and its scores taken, the rows of tile t + 1 go out into the
+        // same registers and stay in flight during the value product.  Table
+        // entries are read a tile ahead of their rows' loads.  The weights are 2^(x - ref) for a fixed reference ref,
         // so the sums are never rescaled (they stay in the matrix cores'
         // accumulators):
         //   MODE 0: ref = the first tile's max score; returns false (sums
@@ -406,18 +397,13 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
             Pos q0 = {pbeg + col, 0u, 0u};
             q0.col = (uint32_t)q0.j / ps;
             q0.off = (uint32_t)q0.j - q0.col * ps;
-            const Pos q1 = advance(q0);
-            const int32_t e0 = entry(q0), e1 = entry(q1);
-            Pos qa = advance(q1);  // tile 2, then every even tile two ahead of the one in kA
-            Pos qb = advance(qa);  // tile 3, then every odd tile two ahead of the one in kB
-            const int32_t row0 = row_of(q0, e0), row1 = row_of(q1, e1);
+            const int32_t e0 = entry(q0);
+            Pos qa = advance(q0);
+            const int32_t row0 = row_of(q0, e0);
             if (__any(bad)) return true;
-            // the order of every later tile: rows, then the entry two tiles on
             load_tile(kA, row0);
             int32_t ea = entry(qa);
-            load_tile(kB, row1);  // row 0 when the segment has one tile
-            int32_t eb = entry(qb);
-            int32_t va = row0, vb = row1;  // the rows in kA and kB (-1: past the segment)
+            int32_t va = row0;
             // scores of tile t -> weights, row sums and P V; false: the reference was outgrown
             auto tile_math = [&](const f32x4 &sc, int32_t t) -> bool {
                 const int32_t p0 = pbeg + t * kTile + 4 * grp;
@@ -472,39 +458,29 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
                     return true;
                 }
             };
-            // tile t from buffer k (its rows v); then the rows of tile t + 2 from (q, e) into k
-            // and the entry of tile t + 4 into e.  Both loads are issued on every path (row 0
+            // tile t from buffer k (its rows v); then the rows of tile t + 1 from (q, e) into k
+            // and the entry of tile t + 2 into e.  Both loads are issued on every path (row 0
             // past the segment's last tile or for a bad entry), the check for a bad entry after
             // them: a path that skipped them would join the others with fewer loads in flight,
-            // and the compiler would then wait for every load at each entry's use.  Every
-            // mode stages the tile: the scores read it back.
+            // and the compiler would then wait for every load at each step.  Every mode
+            // stages the tile: the scores read it back.
             auto step = [&](u32x4 (&k)[KH], int32_t &v, Pos &q, int32_t &e, int32_t t) -> int {
                 stage(k, v, t);
                 const f32x4 sc = scores(k, t);
                 const int32_t rown = row_of(q, e);
-                q = advance(advance(q));
+                q = advance(q);
                 load_tile(k, rown);
                 e = entry(q);
                 v = rown;
                 if (__any(bad)) return 1;
                 return tile_math(sc, t) ? 0 : 2;
             };
-            // Tiles in pairs, with no way out of the loop but its end: the compiler
-            // makes every loop single-exit, so an exit between the two steps would
-            // join the way back to the loop's head with fewer loads in flight.  Both
-            // steps always run (after a bad entry or an outgrown reference the
-            // second one's sums are discarded with the first's), so the loads in
-            // flight at the head are always [rows t, entry t + 2, rows t + 1,
-            // entry t + 3].  An odd last tile follows from kA.
+            // the loads in flight at the loop's head: [rows t, entry t + 1]
             int st = 0;
-            int32_t t = 0;
-            for (; t + 1 < tiles; t += 2) {
-                const int sa = step(kA, va, qa, ea, t);
-                const int sb = step(kB, vb, qb, eb, t + 1);
-                st = sa != 0 ? sa : sb;
+            for (int32_t t = 0; t < tiles; ++t) {
+                st = step(kA, va, qa, ea, t);
                 if (st != 0) break;
             }
-            if (st == 0 && t < tiles) st = step(kA, va, qa, ea, t);
             return st != 2;
         };
         if (!pass(std::integral_constant<int, 0>())) {
