@@ -692,9 +692,12 @@ __global__ __launch_bounds__(kBlock) void gather_piece_kernel(GatherArgs a, int 
 // 8 rows' 8 V vectors (row f / V, vector f % V).  Every load and store moves a
 // whole 1 KiB (the sources are contiguous rows); one instruction spans at most
 // two rows, whose ids are wave-uniform and come through the scalar cache.
-// Measured on the hybrid workload's MLA store (1.05 M latents, 2.43 GB): 380-383
-// us (80% of 8 TB/s) in six runs, against 427-469 us for the tile kernel (one run
-// in eight at 377).  The compiler waits for every memory operation before each
+// Measured on the hybrid workload's MLA store (1.05 M latents, 2.43 GB): 376-383
+// us (80% of 8 TB/s) in 12 of 14 runs (431 and 475 us in the other two), against
+// 427-469 us for the tile kernel in 9 of 12 runs (377-379 us in three).  Groups of
+// whole 1 KiB rows ran 45% slower than the tiles, of 2 KiB rows faster on the small
+// 32-layer decode store but slower on the single-layer prefill store, so only these
+// widths take them.  The compiler waits for every memory operation before each
 // store here; a variant with the loads issued unconditionally, one wait for them
 // and then the stores back to back ran at 431 us, and a gather built the same
 // way stayed behind the tile gather (434-455 against 404-427 us).
