@@ -240,8 +240,8 @@ __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)
         carry += __shfl(incl, kWave - 1);
     }
 
-    // queries as the B operand, from LDS (one copy for both waves): column col
-    // is head hg*16 + col, lane group grp reads dims [8 (4 s + grp), +8) at k-step s
+    // the queries are the B operand, in registers: column col is head hg*16 + col,
+    // lane group grp holds dims [8 (4 s + grp), +8) at k-step s
     const uint8_t *view = a.pool + a.base;
     const uint32_t ps = a.ps;
     const uint32_t q16 = (uint32_t)kTile / ps, r16 = (uint32_t)kTile - q16 * ps;
