@@ -572,10 +572,11 @@ int group_loads(int vec_bytes, uint64_t row_bytes) {
     return (int)(row_bytes / 128);
 }
 
-// Launch kernel template K<NKV, J> for J = loads per lane (9..15) through f(tag).
+// Launch kernel template K<NKV, J> for J = loads per lane (9..16) through f(tag).
 template <typename F>
 void with_group_loads(int j, F &&f) {
     switch (j) {
+        case 16: f(std::integral_constant<int, 16>()); break;
         case 9: f(std::integral_constant<int, 9>()); break;
         case 10: f(std::integral_constant<int, 10>()); break;
         case 11: f(std::integral_constant<int, 11>()); break;
@@ -687,7 +688,8 @@ __global__ __launch_bounds__(kBlock) void gather_piece_kernel(GatherArgs a, int 
 
 // Stores of rows of V = 8 J 16-byte vectors with 64 < V < 128 (1,152 to 1,920
 // bytes; the MLA latent of 576 bf16 among them), which are no whole number of
-// 1 KiB pieces: a wave copies kGroupRows = 8 consecutive entries of one view as J
+// 1 KiB pieces, and small launches of 2 KiB rows (V = 128; each load then stays
+// within one row): a wave copies kGroupRows = 8 consecutive entries of one view as J
 // loads and J stores per lane, lane l of load j taking vector f = 64 j + l of the
 // 8 rows' 8 V vectors (row f / V, vector f % V).  Every load and store moves a
 // whole 1 KiB (the sources are contiguous rows); one instruction spans at most
@@ -1141,7 +1143,13 @@ int ukv_store_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin, 
                                   (uint64_t)src_row_stride_bytes, magnitude(a.src_layer_stride)});
     a.vecs = (int32_t)(q.row_bytes / (uint64_t)vb);
     const int lp = piece_shift(vb, q.row_bytes);
-    if (lp >= 1) {  // rows of 2 KiB and more: a wave per 1 KiB piece (1 KiB rows measured faster in tiles)
+    // A small launch of 2 KiB rows (one that would give a wave more than one piece)
+    // takes the row-group store, 16 loads per lane: the 32-layer decode store (256
+    // rows x 32 layers, 67 MB) ran 11.7-11.8 against 13.2-13.5 us on pieces; a large
+    // one keeps its pieces (groups made the single-layer prefill store 53-54 against
+    // 47.4 us).
+    const bool small_2k = lp == 1 && pieces_per_wave(((n * nkv) << lp) * layer_count, 1) > 1;
+    if (lp >= 1 && !small_2k) {  // rows of 2 KiB and more: a wave per 1 KiB piece (1 KiB rows measured faster in tiles)
         const int64_t pieces = (n * nkv) << lp;
         const int k = pieces_per_wave(pieces * layer_count, 1);
         const int64_t grid = ((pieces + k - 1) / k + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -1162,7 +1170,7 @@ int ukv_store_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin, 
         }
         return check_launch(who);
     }
-    if (const int gj = group_loads(vb, q.row_bytes)) {  // 1,152 to 1,920-byte rows: a wave per 8 rows of a view
+    if (const int gj = small_2k ? 16 : group_loads(vb, q.row_bytes)) {  // a wave per 8 rows of a view
         const int64_t grid = (((n + kGroupRows - 1) / kGroupRows) * nkv + kWavesPerBlock - 1) / kWavesPerBlock;
         if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n too large for one launch", who);
         const dim3 g((unsigned)grid, (unsigned)layer_count), b(kBlock);
