@@ -362,8 +362,10 @@ def test_store_group_shapes(shape, n):
 
 
 # (entries, layers) -> pieces per wave on 256 CUs: 1 (small), 2, 4, 8 (a ragged last wave
-# in each layer), 1 (more than eight rounds of resident waves)
-@pytest.mark.parametrize("n,layers", [(256, 1), (101, 32), (256, 32), (401, 32), (1500, 32), (40, 32)])
+# in each layer), 1 (more than eight rounds of resident waves); multi-layer launches take
+# the XCD order, (101, 3) and (7, 5) with a grid that is no multiple of the 8 XCDs
+@pytest.mark.parametrize("n,layers", [(256, 1), (101, 32), (256, 32), (401, 32), (1500, 32), (40, 32), (101, 3),
+                                      (7, 5)])
 def test_store_pieces_per_wave(n, layers):
     """Fused stores whose size gives each wave 1, 2, 4 or 8 pieces (a small launch is
     packed into one round of resident waves), with tombstones and a bad id among the
