@@ -232,10 +232,10 @@ struct StoreArgs {
     int32_t vecs;          // row_bytes / sizeof(V)
     int32_t tile_rows;     // rows per tile, <= 64
     int32_t tiles_per_wave;
+    uint32_t layers;           // grid y (in the struct's alignment gap: the arguments stay within 128 bytes)
     uint64_t layer_base_step;  // view bytes from one stored layer to the next (grid y)
     int64_t src_layer_stride;  // source bytes from one stored layer to the next
     uint32_t *flags;
-    uint32_t grid_x, grid_y;   // the piece store's grid, for its XCD order (multi-layer launches)
 };
 
 // K_view[l][ids[i]] = k[l][i], V_view[l][ids[i]] = v[l][i] for the layer of
@@ -610,22 +610,25 @@ int piece_shift(int vec_bytes, uint64_t row_bytes) {
 // launch order, and the workgroups of one XCD take consecutive logical blocks, so
 // each XCD stores its own run of layers instead of every XCD working on the same
 // layer.  Measured on the 32-layer prefill store (32,768 rows x 32 layers, 8.6 GB)
-// on four boxes: 1,352-1,406 us (76-79% of 8 TB/s) against 1,404-1,443 us in
-// launch order; the same order for the gather and the move was 1.5-2.5% slower.
-// Single-layer launches keep launch order (no extra argument load before the first
-// piece: the 256-row decode store is latency-bound).
+// on six boxes: 1,328-1,406 us (76-81% of 8 TB/s) against 1,404-1,443 us in launch
+// order; the same order for the gather and the move was 1.5-2.5% slower, and it did
+// not speed up the single-layer prefill store, so those keep launch order.  The
+// kernel recomputes the grid from its arguments, and the layer count sits in the
+// argument block's alignment gap: two more argument words, which took the block past
+// 128 bytes, made the latency-bound 256-row decode store 2.7-2.8 us against 2.5 us.
 template <int NKV, int K, bool XL>
 __global__ __launch_bounds__(kBlock) void store_piece_kernel(StoreArgs a, int lp) {
     const int lane = lane_id();
+    constexpr int hb = NKV == 2 ? 1 : 0;
     uint32_t x = blockIdx.x, y = blockIdx.y;
-    if constexpr (XL) {  // grid_x * grid_y < 2^32 (host)
-        const uint32_t g = a.grid_x * a.grid_y, i = y * a.grid_x + x, xcd = i & 7;
+    if constexpr (XL) {  // the host's grid: gx = ceil(ceil(pieces / K) / waves per block); gx * layers < 2^32
+        const uint32_t gx = (uint32_t)(((((a.n << hb) << lp) + K - 1) / K + kWavesPerBlock - 1) / kWavesPerBlock);
+        const uint32_t g = gx * a.layers, i = y * gx + x, xcd = i & 7;
         const uint32_t l = xcd * (g >> 3) + min(xcd, g & 7) + (i >> 3);
-        y = l / a.grid_x;
-        x = l - y * a.grid_x;
+        y = l / gx;
+        x = l - y * gx;
     }
     const int64_t u0 = ((int64_t)x * kWavesPerBlock + wave_in_block()) * K;
-    constexpr int hb = NKV == 2 ? 1 : 0;
     if ((u0 >> (lp + hb)) >= a.n) return;
     const int64_t src0 = (int64_t)y * a.src_layer_stride;
     const uint64_t view0 = (uint64_t)y * a.layer_base_step;
@@ -1174,8 +1177,7 @@ int ukv_store_kv_layers(const ukv_pool *pool, int32_t sub, int32_t layer_begin, 
         const int64_t grid = ((pieces + k - 1) / k + kWavesPerBlock - 1) / kWavesPerBlock;
         if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n too large for one launch", who);
         const dim3 g((unsigned)grid, (unsigned)layer_count), b(kBlock);
-        a.grid_x = (uint32_t)grid;
-        a.grid_y = (uint32_t)layer_count;
+        a.layers = (uint32_t)layer_count;
         const bool xl = layer_count > 1 && (uint64_t)grid * (uint64_t)layer_count < (1ull << 32);
         auto go = [&](auto kv, auto kk) {
             constexpr int NKV = decltype(kv)::value, K = decltype(kk)::value;
