@@ -13,6 +13,8 @@ device the test then checks
     width, 16 bytes here, whole from one of the tombstoned entries of that call).
 Every output row of every layer is compared; nothing is sampled.
 """
+from types import SimpleNamespace
+
 import numpy as np
 import pytest
 import torch
@@ -297,3 +299,67 @@ def test_full_compaction_prefill_8b():
     assert np.array_equal(v2p_d.cpu().numpy(), v2p_exp)
     assert U.ukv_pool_error_flags(pool) == frozenset()
     del snap
+
+
+def _top_pages(ps):
+    """The largest page count the host plan admits for one layer of one 8-element bf16 head
+    (16-byte rows) at page size ps: kernel-facing rows then reach just below 2^31."""
+    lo, hi = 1, 1 << 28
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if U.plan_status([W.mha(1, 1, 8, mid)], ps) == "UKV_OK":
+            lo = mid
+        else:
+            hi = mid - 1
+    return lo
+
+
+def test_full_top_of_the_kernel_id_space():
+    """16-byte rows (one layer, one head of 8 bf16), page size 16, the largest page count the
+    2^31 row bound admits (32 GiB, 2^31 rows): the last two pages, page 1 and a middle one
+    stored (K and V, one tombstone; the last V row is the envelope's last row; page 0 is the
+    sink and holds no live slot), gathered back in full and windowed through a table that
+    lists the last page first, then rows of the top and middle pages moved to page 2 and to
+    one near the top.  Every touched row against the oracle's addresses, every other byte
+    against the pre-fill."""
+    ps = 16
+    P = _top_pages(ps)
+    assert U.plan_status([W.mha(1, 1, 8, P + 1)], ps) == "UKV_ERR_KERNEL_ID_BOUND"
+    assert oracle.plan(ospecs([W.mha(1, 1, 8, P)]), ps).code == "ok"
+    assert oracle.plan(ospecs([W.mha(1, 1, 8, P + 1)]), ps).code != "ok"
+    w = SimpleNamespace(shapes=[W.mha(1, 1, 8, P)], page_size=ps)
+    pool, orc = _make(w)
+    anchor, env, rb = _sub_geom(pool, 0)
+    assert rb == 16 and env // rb > (1 << 31) - 64
+    top, mid = P - 1, P // 2
+    pages = [top, top - 1, 1, mid]
+    slots = np.concatenate([np.arange(p * ps, (p + 1) * ps) for p in pages]).astype(np.int64)
+    slots[5] = -1  # a tombstone
+    ids_d, ids = _translate(pool, orc, 0, slots)
+    assert int(ids.max()) == top * 2 * ps + ps - 1
+    masks = _masks(pool)
+    _store_layers(pool, orc, 0, ids_d, ids, slots, masks, 1700)
+    assert bool(masks[0][env // rb - 1])  # the envelope's last row was written
+    log("  stores checked")
+    req_pages = [np.array([top, top - 1], np.int32), np.array([mid, 1], np.int32)]
+    lens = [2 * ps, ps + 4]
+    bt_d, bt = _block_table(pool, orc, 0, req_pages)
+    _gather_layers(pool, orc, 0, bt_d, bt, lens, [0], [0])
+    _gather_layers(pool, orc, 0, bt_d, bt, lens, [5], [0])
+    log("  gathers checked")
+    src = np.concatenate([np.arange(top * ps, (top + 1) * ps), np.arange(mid * ps, (mid + 1) * ps)]).astype(np.int64)
+    dst = np.concatenate([np.arange(2 * ps, 3 * ps), np.arange((top - 2) * ps, (top - 1) * ps)]).astype(np.int64)
+    src_d, s_ids = _translate(pool, orc, 0, src)
+    dst_d, d_ids = _translate(pool, orc, 0, dst)
+    U.ukv_move_kv(pool, 0, dst_d, src_d)
+    d_off, s_off, fl = orc.move_map(0, d_ids, s_ids, 0, 1)
+    assert fl == frozenset()
+    rows = rows_view(pool.raw, anchor, env, rb)
+    d_rows = torch.from_numpy(offsets_to_rows(d_off, anchor, rb)).cuda()
+    s_rows = torch.from_numpy(offsets_to_rows(s_off, anchor, rb)).cuda()
+    # sources and destinations are disjoint, so the sources still hold what was stored
+    assert equal_rows_chunked(rows, d_rows, rows, s_rows), "moved rows"
+    masks[0][d_rows] = True
+    _check_untouched(pool, masks)
+    log("  move and untouched bytes checked")
+    assert U.ukv_pool_error_flags(pool) == frozenset()
