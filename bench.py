@@ -100,11 +100,16 @@ LIB_KERNELS = ("store_kernel", "store_piece_kernel", "store_group_kernel", "gath
 ROOFLINE_MERGE_KERNEL = {"attn_chunk": "attn_combine_kernel", "mla_attn_span": "mla_attn_combine_kernel"}
 
 
+STALL_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_WRREQ_sum", "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum",
+                  "TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum")
+
+
 def profile_commands(workload: str, out: str = "$OUT") -> Dict[str, str]:
-    """The three profiler runs one summary needs (run from /tmp with TMPDIR=/tmp; $R is the
+    """The four profiler runs one summary needs (run from /tmp with TMPDIR=/tmp; $R is the
     repository root, $OUT a directory for rocprofv3's CSV files): a kernel trace, then one
     counter per run (FETCH_SIZE, WRITE_SIZE), each beside a plain 1 GiB copy that
-    calibrates the counter."""
+    calibrates the counter, then L2's requests to memory and the cycles they waited for
+    DRAM credits (four L2 counters, one run)."""
     bench = f"python3 $R/bench.py --workload {workload} --no-cpu-baseline --no-bar"
     return {
         "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o run -- {bench} "
@@ -113,6 +118,8 @@ def profile_commands(workload: str, out: str = "$OUT") -> Dict[str, str]:
                  f"--steps 1 --warmup 1 --copy-calibration",
         "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/write -o run -- {bench} "
                  f"--steps 1 --warmup 1 --copy-calibration",
+        "stalls": f"rocprofv3 --pmc {' '.join(STALL_COUNTERS)} --output-format csv -d {out}/stalls -o run -- {bench} "
+                  f"--steps 1 --warmup 1",
     }
 
 
@@ -135,8 +142,9 @@ def _grid(row: dict, keys) -> int:
 
 
 def rocprof_summary(directory: str, workload: str, out_dir: str = PROFILE_DIR) -> List[str]:
-    """Write the kernel-trace and counter summaries of one workload from the three
-    rocprofv3 runs of :func:`profile_commands` kept under ``directory``.
+    """Write the kernel-trace and counter summaries of one workload from the
+    rocprofv3 runs of :func:`profile_commands` kept under ``directory`` (the stall run is
+    optional: without it the counters summary ends after the bytes beyond L2).
 
     Kernel trace: the stats rows of this library's kernels, and the roofline kind's
     average duration (only its largest-grid dispatches where the workload's script
@@ -212,9 +220,9 @@ def rocprof_summary(directory: str, workload: str, out_dir: str = PROFILE_DIR) -
     with open(trace_path, "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    def counters(name):
+    def counters(name, run=None):
         out, grids = {}, {}
-        for r in rows(os.path.join(directory, name.split("_")[0].lower(), "run_counter_collection.csv")):
+        for r in rows(os.path.join(directory, run or name.split("_")[0].lower(), "run_counter_collection.csv")):
             if r["Counter_Name"] == name:
                 out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
                 grids.setdefault(r["Kernel_Name"], []).append(int(r["Grid_Size"]))
@@ -263,8 +271,21 @@ def rocprof_summary(directory: str, workload: str, out_dir: str = PROFILE_DIR) -
                                                                 else ""),
               f"beyond_l2_bytes_per_launch: {roof_bytes}",
               f"algorithmic_bytes_per_launch: {alg}",
-              f"traffic / algorithmic: {roof_bytes / alg:.4f}" if (roof_bytes and alg) else "traffic / algorithmic: n/a",
-              f"kernel_source_sha256_16: {h}"]
+              f"traffic / algorithmic: {roof_bytes / alg:.4f}" if (roof_bytes and alg) else "traffic / algorithmic: n/a"]
+    if os.path.exists(os.path.join(directory, "stalls", "run_counter_collection.csv")):
+        # L2's requests to memory and the cycles they waited because the memory side had
+        # no credits left, summed over the L2 channels, per roofline dispatch
+        st = {c: counters(c, "stalls") for c in STALL_COUNTERS}
+        per = {}
+        for c, by_kernel in st.items():
+            vals = [v for k, vs in by_kernel.items() if is_roof(k) for v in vs]
+            per[c] = sum(vals) / len(vals) if vals else None
+        lines += ["", "DRAM credit stalls (one more run):", "  " + cmds["stalls"],
+                  "Per roofline dispatch, summed over the L2 channels: requests from L2 to memory, and the",
+                  "cycles they waited because the memory side had no credits (room) left for them:"]
+        for c in STALL_COUNTERS:
+            lines.append(f"  {c}: {per[c]:.4g}" if per[c] is not None else f"  {c}: n/a")
+    lines.append(f"kernel_source_sha256_16: {h}")
     counters_path = os.path.join(out_dir, f"{kernel}_{workload}_counters.txt")
     with open(counters_path, "w") as f:
         f.write("\n".join(lines) + "\n")

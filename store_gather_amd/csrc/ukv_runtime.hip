@@ -75,6 +75,14 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 // The wave's index inside the block, made uniform so that everything derived
 // from it is computed in scalar registers.
 __device__ __forceinline__ int wave_in_block() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)); }
+
+// XCD order: workgroups go to the 8 XCDs round-robin in launch order (launch index i
+// on XCD i % 8); this gives the workgroups of one XCD consecutive logical blocks, a
+// bijection of [0, g).
+__device__ __forceinline__ uint32_t xcd_logical_block(uint32_t i, uint32_t g) {
+    const uint32_t xcd = i & 7;
+    return xcd * (g >> 3) + min(xcd, g & 7) + (i >> 3);
+}
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
 // A kernel-facing row id lies on block 0 of some page: id = page * (ps *
@@ -627,8 +635,7 @@ __global__ __launch_bounds__(kBlock) void store_piece_kernel(StoreArgs a, int lp
     uint32_t x = blockIdx.x, y = blockIdx.y;
     if constexpr (XL) {  // the host's grid: gx = ceil(ceil(pieces / K) / waves per block); gx * layers < 2^32
         const uint32_t gx = (uint32_t)(((((a.n << hb) << lp) + K - 1) / K + kWavesPerBlock - 1) / kWavesPerBlock);
-        const uint32_t g = gx * a.layers, i = y * gx + x, xcd = i & 7;
-        const uint32_t l = xcd * (g >> 3) + min(xcd, g & 7) + (i >> 3);
+        const uint32_t l = xcd_logical_block(y * gx + x, gx * a.layers);
         y = l / gx;
         x = l - y * gx;
     }
@@ -819,15 +826,20 @@ struct PageMoveArgs {
     int64_t vecs;       // page_bytes / sizeof(V)
     int64_t segs;       // segments per page
     uint32_t *flags;
+    uint32_t grid;      // workgroups in the launch (< 2^32), for the XCD order
 };
 
 // A page's rows on every layer, K and V, are one contiguous envelope, so a
 // page relocation is a straight copy of page_bytes.  One wave per
 // (pair, 64 * TPL-chunk segment); the pair index is wave-uniform, so the
-// page lookups are scalar loads.
+// page lookups are scalar loads.  The workgroups of one XCD take consecutive
+// blocks (XCD order): each XCD copies its own run of pages.  Measured on the
+// compaction of 1,789 pages of 2 MiB (7.5 GB), three A/B pairs in one run:
+// 1,152-1,158 us (81% of 8 TB/s) against 1,231-1,234 us (76%) in launch order,
+// where the eight XCDs copy the same few pages at once.
 template <typename V, int TPL>
 __global__ __launch_bounds__(kBlock) void move_pages_kernel(PageMoveArgs a) {
-    const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block();
+    const int64_t w = (int64_t)xcd_logical_block(blockIdx.x, a.grid) * kWavesPerBlock + wave_in_block();
     const int64_t pair = w / a.segs;
     if (pair >= a.n) return;
     const int64_t seg = w - pair * a.segs;
@@ -1435,6 +1447,7 @@ int ukv_move_pages(const ukv_pool *pool, int32_t sub, const int32_t *dst_pages_d
     const int64_t waves = n * a.segs;
     const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
     if (grid > kMaxGrid) return fail(UKV_ERR_INVALID_ARG, "%s: n pages too large for one launch", who);
+    a.grid = (uint32_t)grid;
     auto launch = [&](auto *tag) {
         using V = std::remove_pointer_t<decltype(tag)>;
         hipLaunchKernelGGL((move_pages_kernel<V, kTpl>), dim3((unsigned)grid), dim3(kBlock), 0, stream, a);

@@ -128,6 +128,11 @@ def test_rocprof_summary_from_fixture_csvs(tmp_path):
     assert "traffic / algorithmic: 1.5000" in counters
     assert f"kernel_source_sha256_16: {bench.kernel_source_hash('gather')}" in counters
     assert "rocprofv3 --pmc FETCH_SIZE" in counters and "--rocprof-summary" in counters
+    # the stall run: means over the two gather dispatches only (the store's rows are ignored)
+    for line in ("TCC_EA0_RDREQ_sum: 20", "TCC_EA0_WRREQ_sum: 30", "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum: 2",
+                 "TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum: 100"):
+        assert "  " + line + "\n" in counters, line
+    assert "rocprofv3 --pmc TCC_EA0_RDREQ_sum" in counters
     assert bench.traffic_from_profile("tiny", "gather", profile_dir=str(tmp_path)) == 6144
 
 
