@@ -623,8 +623,10 @@ int piece_shift(int vec_bytes, uint64_t row_bytes) {
 // each XCD stores its own run of layers instead of every XCD working on the same
 // layer.  Measured on the 32-layer prefill store (32,768 rows x 32 layers, 8.6 GB)
 // on six boxes: 1,328-1,406 us (76-81% of 8 TB/s) against 1,404-1,443 us in launch
-// order; the same order for the gather and the move was 1.5-2.5% slower, and it did
-// not speed up the single-layer prefill store, so those keep launch order.  The
+// order, with a twentieth of the cycles L2's writes waited for DRAM credits (2.8e6
+// against 5.75e7 per launch).  The same order made the gathers 5-9% and the row move
+// 2% slower, and did not speed up the single-layer prefill store: those keep launch
+// order.  The
 // kernel recomputes the grid from its arguments, and the layer count sits in the
 // argument block's alignment gap: two more argument words, which took the block past
 // 128 bytes, made the latency-bound 256-row decode store 2.7-2.8 us against 2.5 us.
