@@ -645,6 +645,22 @@ def test_move_pages_and_remap_parity():
     assert np.array_equal(vd.cpu().numpy(), v2p)
 
 
+@pytest.mark.parametrize("n", [37, 101])
+def test_move_pages_ragged_xcd_grid(n):
+    """Page relocations whose launch grid is no multiple of the 8 XCDs (1 KiB pages: one
+    wave per page, ceil(n / 4) = 10 and 26 workgroups), so both terms of the XCD order
+    run: byte for byte against the oracle."""
+    pair = Pair([W.mha(2, 2, 16, 256)], 4)
+    assert pair.rb(0) * 4 * 4 == 1024  # page bytes: ps x 2L blocks x row bytes
+    g = np.random.default_rng(n)
+    perm = g.permutation(256).astype(np.int32)
+    dst, src = perm[:n], perm[n:2 * n]
+    U.ukv_move_pages(pair.gpu, 0, to_dev(dst), to_dev(src))
+    assert pair.orc.move_pages(0, dst, src) == frozenset()
+    assert U.ukv_pool_error_flags(pair.gpu) == frozenset()
+    pair.assert_pools_equal()
+
+
 def test_compaction_end_to_end():
     """Requests written through a virtual-to-physical table; the pages above the watermark are
     relocated below it and the table rewritten; every request reads the same K/V after."""
