@@ -78,7 +78,8 @@ __device__ __forceinline__ int wave_in_block() { return __builtin_amdgcn_readfir
 
 // XCD order: workgroups go to the 8 XCDs round-robin in launch order (launch index i
 // on XCD i % 8); this gives the workgroups of one XCD consecutive logical blocks, a
-// bijection of [0, g).
+// bijection of [0, g).  Only the speed depends on that dispatch order: any other
+// still covers every block once.
 __device__ __forceinline__ uint32_t xcd_logical_block(uint32_t i, uint32_t g) {
     const uint32_t xcd = i & 7;
     return xcd * (g >> 3) + min(xcd, g & 7) + (i >> 3);
